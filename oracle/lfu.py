@@ -1,0 +1,59 @@
+"""Replay of the per-layer expert-cache policy, for checking the GPU library's
+cache bookkeeping.  TEST INFRASTRUCTURE ONLY.
+
+Policy (Rockchip-NPU MoE streaming plan, §6.2.2 cache entry with a use count
+and a last-used tick, the ExpertCache of §6.2.3, and §9.5 item 1 preferring
+LFU): a lookup that hits increments the entry's use count; a missing expert
+takes an empty slot if one exists (lowest slot index first), otherwise it
+evicts the entry with the smallest use count; a newly inserted entry starts
+with count 1.  Readings where the plan is silent: the last-used tick breaks
+count ties (older first), then the slot index; experts chosen by the current
+step are never evicted by that step; counts are never aged; hits are
+processed before misses, misses in ascending expert order; one access per
+(step, chosen expert), forced-reuse steps included.
+"""
+from __future__ import annotations
+
+
+class LfuReplay:
+    def __init__(self, n_slots: int):
+        self.n_slots = n_slots
+        self.expert = [-1] * n_slots
+        self.count = [0] * n_slots
+        self.tick = [0] * n_slots
+        self.now = 0
+        self.accesses = self.hits = self.misses = self.evictions = 0
+
+    def step(self, chosen):
+        """chosen: iterable of distinct expert ids.  Returns (slot per chosen id
+        in the given order, list of booleans 'was a miss')."""
+        chosen = list(chosen)
+        assert len(set(chosen)) == len(chosen) and len(chosen) <= self.n_slots
+        self.now += 1
+        where = {e: s for s, e in enumerate(self.expert) if e >= 0}
+        pinned = set()
+        slot_of, miss_of = {}, {}
+        for e in chosen:
+            self.accesses += 1
+            if e in where:
+                s = where[e]
+                self.count[s] += 1
+                self.tick[s] = self.now
+                self.hits += 1
+                slot_of[e], miss_of[e] = s, False
+                pinned.add(s)
+        for e in sorted(x for x in chosen if x not in where):
+            empties = [s for s in range(self.n_slots) if self.expert[s] < 0]
+            if empties:
+                s = empties[0]
+            else:
+                cands = [s for s in range(self.n_slots) if s not in pinned]
+                s = min(cands, key=lambda s: (self.count[s], self.tick[s], s))
+                self.evictions += 1
+            self.expert[s] = e
+            self.count[s] = 1
+            self.tick[s] = self.now
+            self.misses += 1
+            pinned.add(s)
+            slot_of[e], miss_of[e] = s, True
+        return [slot_of[e] for e in chosen], [miss_of[e] for e in chosen]
