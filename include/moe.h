@@ -1,0 +1,229 @@
+/*
+ * moe.h -- C ABI of the gfx950 routed-expert MoE FFN library (libmoe.so).
+ *
+ * One MoE FFN layer, per token: an int8 router scores all E experts; a
+ * softmax top-K picks K of them and renormalises their coefficients over the
+ * chosen set; each chosen expert runs a SwiGLU FFN whose weights are affine
+ * 4-bit with one (scale, bias) pair per 64 inputs of a row; an always-on
+ * shared expert is added with unit weight; the result is the weighted sum.
+ *   BigMoeOnEdge (onecrewdev), section "re-routing at every token and layer":
+ *     router scores -> top-K experts with coefficients -> weighted merge
+ *     y = sum_j w_j * Expert_j(x); the shared path is not counted among K.
+ *   Rockchip-NPU MoE streaming plan (cnblogs), §2.1/§2.5: affine 4-bit
+ *     group-64 expert weights, 8-bit router; §2.4: the shared expert is fused
+ *     with the weighted routed outputs; §6.2.2 and §9.5: a per-layer 16-slot
+ *     LFU expert cache; §8.4: 128-token prefill chunks.
+ *
+ * Conventions for every function:
+ *  - Returns moe_status; nothing throws across the ABI.  On a non-OK status
+ *    moe_last_error() returns a message for the calling thread, and any
+ *    output buffers are undefined.
+ *  - "DEVICE" pointers are HIP device memory owned by the caller; "HOST"
+ *    pointers are ordinary host memory owned by the caller.
+ *  - `stream` arguments are hipStream_t values passed as void* (NULL = the
+ *    default stream).  Work is enqueued on that stream; functions return
+ *    without waiting for the GPU unless stated otherwise.
+ *  - One host thread may use a given layer/stack object at a time.  Distinct
+ *    objects may be used concurrently on distinct streams.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1, /* bad argument or descriptor */
+  MOE_ERR_NOMEM = 2,   /* device or pinned host allocation failed */
+  MOE_ERR_HIP = 3,     /* a HIP runtime call failed */
+  MOE_ERR_IO = 4,      /* an expert could not be brought into its cache slot */
+  MOE_ERR_STATE = 5    /* call not valid in the object's current state */
+} moe_status;
+
+enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 };        /* activation dtype of x / out */
+enum { MOE_RESIDENT = 0, MOE_STREAMED = 1 };        /* where routed experts live */
+enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
+
+typedef struct moe_layer moe_layer; /* opaque, owned by the library */
+typedef struct moe_stack moe_stack; /* opaque, owned by the library */
+typedef struct moe_lfu moe_lfu;     /* opaque host-only cache policy object */
+
+/*
+ * Layer descriptor.  All weight pointers are HOST pointers in the canonical
+ * layout below; moe_layer_create copies them, so the caller may free them as
+ * soon as it returns.
+ *
+ * A 4-bit matrix with R rows (outputs) and C columns (inputs), C % 64 == 0:
+ *   q  uint32 [R][C/8]  : nibble k (bits 4k..4k+3) of word j is q[row][8j+k]
+ *   s  uint16 [R][C/64] : fp16 scale of the 64-column group
+ *   b  uint16 [R][C/64] : fp16 bias of the 64-column group
+ *   weight[row][col] = s[row][col/64] * q[row][col] + b[row][col/64]
+ * Routed experts are stacked along a leading expert axis [E]:
+ *   gate, up: R = d_ff, C = d_model;   down: R = d_model, C = d_ff.
+ * The shared expert uses d_ff_shared (0 = no shared expert; pointers NULL).
+ * Router: int8 [E][d_model], fp16 per-row scale [E], optional fp32 per-expert
+ *   logit bias [E]:  logit_e = scale_e * sum_c W[e][c] * x[c] + bias_e.
+ */
+typedef struct {
+  int32_t d_model;     /* multiple of 64, <= 8192 */
+  int32_t n_experts;   /* E, 1..1024 */
+  int32_t top_k;       /* K, 1..min(E, 64) */
+  int32_t d_ff;        /* routed expert hidden size, multiple of 64 */
+  int32_t d_ff_shared; /* shared expert hidden size, multiple of 64, or 0 */
+  int32_t act_dtype;   /* MOE_ACT_F32 or MOE_ACT_BF16 */
+  int32_t max_tokens;  /* largest n_tokens any forward call will pass (>= 1) */
+  int32_t residency;   /* MOE_RESIDENT: all experts in HBM; MOE_STREAMED:
+                          routed experts in pinned host memory, served through
+                          a per-layer HBM slot cache (see moe_cache_attach) */
+  const int8_t* router_w;
+  const uint16_t* router_scale;
+  const float* router_bias; /* may be NULL */
+  const uint32_t* gate_q;
+  const uint16_t* gate_s;
+  const uint16_t* gate_b;
+  const uint32_t* up_q;
+  const uint16_t* up_s;
+  const uint16_t* up_b;
+  const uint32_t* down_q;
+  const uint16_t* down_s;
+  const uint16_t* down_b;
+  const uint32_t* sh_gate_q;
+  const uint16_t* sh_gate_s;
+  const uint16_t* sh_gate_b;
+  const uint32_t* sh_up_q;
+  const uint16_t* sh_up_s;
+  const uint16_t* sh_up_b;
+  const uint32_t* sh_down_q;
+  const uint16_t* sh_down_s;
+  const uint16_t* sh_down_b;
+} moe_layer_desc;
+
+/* Validates the descriptor, repacks the weights into the library's device
+ * layout and allocates the layer's device workspace.  Blocks until the copies
+ * are done.  Errors: MOE_ERR_INVALID (shape limits above, NULL weights),
+ * MOE_ERR_NOMEM, MOE_ERR_HIP. */
+moe_status moe_layer_create(const moe_layer_desc* desc, moe_layer** out);
+
+/* Frees everything the layer owns (waits for the device first). NULL is OK. */
+moe_status moe_layer_destroy(moe_layer* layer);
+
+/* out[t] = MoE(x[t]) for t < n_tokens.
+ * x, out: DEVICE [n_tokens][d_model] of act_dtype, row-major; may not alias.
+ * n_tokens: 0..max_tokens (0 is a no-op).
+ * Resident layers: only enqueues work on `stream`.  Streamed layers: blocks
+ * the calling thread until the routing of this call is known on the host
+ * (one small device->host copy), then enqueues the cache fills and compute. */
+moe_status moe_layer_forward(const void* x, moe_layer* layer, void* out, int32_t n_tokens, void* stream);
+
+/* Optional controls of one forward call.  Every field may be 0/NULL. */
+typedef struct {
+  int32_t* topk_ids;          /* DEVICE [T][K] out: chosen experts, ascending */
+  float* topk_w;              /* DEVICE [T][K] out: their coefficients */
+  const int32_t* forced_ids;  /* DEVICE [T][K] in: use these (ascending, distinct,
+                                 < E) expert sets instead of the top-K; the
+                                 coefficients are renormalised from this call's
+                                 logits over the given set */
+  int32_t reuse_previous;     /* nonzero: use the expert sets of this layer's
+                                 previous forward call (same n_tokens), with
+                                 coefficients from this call's logits */
+  int32_t path;               /* MOE_PATH_*; AUTO picks DECODE for small T or
+                                 fp32 activations, PREFILL otherwise */
+  int32_t residual;           /* nonzero: out = act(x_in + y) where x_in is the
+                                 `residual_src` tensor (stack glue) */
+  const void* residual_src;   /* DEVICE [T][d_model] of act_dtype, or NULL */
+  int32_t* sort_offsets;      /* DEVICE [E+1] out (prefill path only) */
+  int32_t* sort_perm;         /* DEVICE [T*K] out (prefill path only) */
+} moe_fwd_opts;
+
+moe_status moe_layer_forward_ex(const void* x, moe_layer* layer, void* out, int32_t n_tokens,
+                                const moe_fwd_opts* opts, void* stream);
+
+/* Router + softmax top-K only: ids DEVICE int32 [T][K] (ascending per token),
+ * w DEVICE fp32 [T][K]. */
+moe_status moe_layer_route(const void* x, moe_layer* layer, int32_t* ids, float* w, int32_t n_tokens,
+                           void* stream);
+
+/* Token->expert grouping of a [T][K] id array (ascending per row, < E):
+ * counts[E], offsets[E+1] (exclusive scan), perm[T*K] = t*K+k ordered by
+ * (expert, token), inv[T*K] = position of pair t*K+k in perm.  All DEVICE,
+ * T <= max_tokens of the layer.  Rockchip-NPU plan §8.4 (one fetched expert
+ * serves all rows of the chunk that chose it). */
+moe_status moe_layer_sort(const int32_t* ids, moe_layer* layer, int32_t n_tokens, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
+
+/* Bytes the layer keeps in device memory, and the per-expert byte size
+ * (gate + up + down at 4.5 bits per weight, padded to 256 B). */
+moe_status moe_layer_bytes(const moe_layer* layer, uint64_t* device_bytes, uint64_t* expert_bytes);
+
+/* Waits for the device, then returns and clears the layer's sticky kernel
+ * error flags in *flags (HOST): bit 0 = a forced expert id was outside
+ * 0..E-1 (it was replaced by 0), bit 1 = a chosen expert was not resident. */
+moe_status moe_layer_check_errors(moe_layer* layer, int32_t* flags);
+
+/* ---- expert cache (MOE_STREAMED layers) --------------------------------
+ * Rockchip-NPU plan §6.2.2/§6.2.3/§9.5: per-layer slots, LFU eviction; the
+ * cache entry keeps a use count and a last-used tick.  Policy: a hit adds
+ * one to the entry's count; a miss takes the lowest empty slot, else evicts
+ * the entry with the least (count, last-used tick, slot) among entries not
+ * chosen by the current call; a new entry starts at count 1; counts are
+ * never aged.  Fills are hipMemcpyAsync from pinned host memory on a side
+ * stream, ordered before the expert kernels by events. */
+
+/* Allocates n_slots HBM slots (n_slots >= top_k * max_tokens is not required;
+ * n_slots >= the number of distinct experts a single call can choose is:
+ * calls needing more return MOE_ERR_STATE).  side_stream may be NULL, in which
+ * case the library creates one.  Errors: MOE_ERR_STATE if the layer is not
+ * MOE_STREAMED or already has a cache. */
+moe_status moe_cache_attach(moe_layer* layer, int32_t n_slots, void* side_stream);
+
+typedef struct {
+  uint64_t accesses;   /* one per (call, token, chosen expert) that was looked up */
+  uint64_t hits;
+  uint64_t misses;
+  uint64_t evictions;  /* misses that replaced a resident expert */
+  uint64_t h2d_bytes;  /* misses * expert bytes */
+  uint64_t h2d_ns;     /* wall time of the fills, host clock, summed */
+} moe_cache_stats;
+
+moe_status moe_cache_stats_get(const moe_layer* layer, moe_cache_stats* out);
+/* Clears the counters; drop_contents != 0 also empties every slot. */
+moe_status moe_cache_reset(moe_layer* layer, int32_t drop_contents);
+/* HOST outputs [n_slots]: expert held by each slot (-1 = empty), use count. */
+moe_status moe_cache_contents(const moe_layer* layer, int32_t* expert_of_slot, uint32_t* use_count);
+/* Test hook: make expert `expert` unreadable (1) or readable (0); a call that
+ * needs to fill an unreadable expert returns MOE_ERR_IO before enqueuing any
+ * expert compute and leaves the slot table unchanged. */
+moe_status moe_cache_fail_expert(moe_layer* layer, int32_t expert, int32_t fail);
+
+/* ---- stack of layers (decode through many MoE layers) ------------------
+ * h <- act(h + MoE_l(act(rmsnorm(h)))) for each layer l in order, where
+ * rmsnorm(h) = h / sqrt(mean(h^2) + eps) with unit gain. */
+moe_status moe_stack_create(moe_layer* const* layers, int32_t n_layers, float rms_eps, moe_stack** out);
+/* h: DEVICE [n_tokens][d_model], updated in place.  reuse_mask: HOST
+ * [n_layers] or NULL; nonzero entries make that layer reuse its previous
+ * call's expert sets (see moe_fwd_opts.reuse_previous).  ids_out: DEVICE
+ * [n_layers][n_tokens][K] or NULL. */
+moe_status moe_stack_forward(void* h, moe_stack* stack, int32_t n_tokens, const uint8_t* reuse_mask,
+                             int32_t* ids_out, void* stream);
+moe_status moe_stack_destroy(moe_stack* stack);
+
+/* ---- host-only cache policy (no GPU needed) ----------------------------
+ * The same policy object the streamed layers use, exposed for checking. */
+moe_status moe_lfu_create(int32_t n_slots, moe_lfu** out);
+/* chosen: HOST [n] distinct expert ids of one call.  slot_out[n], miss_out[n]
+ * (HOST) receive the slot of each id and 1 where it was a miss. */
+moe_status moe_lfu_step(moe_lfu* lfu, const int32_t* chosen, int32_t n, int32_t* slot_out, int32_t* miss_out);
+moe_status moe_lfu_stats(const moe_lfu* lfu, moe_cache_stats* out);
+moe_status moe_lfu_destroy(moe_lfu* lfu);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,640 @@
+// C ABI of the MoE FFN library: descriptor validation, weight repack and
+// upload, workspace management, kernel launch sequencing, the streamed expert
+// cache and the stack driver.  No PyTorch types cross this boundary.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+#include "layout.hpp"
+#include "lfu.hpp"
+
+namespace moe {
+size_t decode_lds_bytes_x(int d);
+size_t decode_lds_bytes_down(int F, int NI, int K, int act);
+size_t prefill_workspace_bytes(int T, int d, int E, int K, int f, int fs);
+void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, int fs);
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_OK(expr)                                                                                   \
+  do {                                                                                                 \
+    hipError_t e_ = (expr);                                                                            \
+    if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));     \
+  } while (0)
+
+template <class T>
+hipError_t dalloc(T** p, size_t bytes) {
+  return hipMalloc(reinterpret_cast<void**>(p), bytes ? bytes : 16);
+}
+
+}  // namespace
+
+struct moe_layer {
+  int dev = 0;
+  int d = 0, E = 0, K = 0, f = 0, fs = 0, act = 0, max_tokens = 0, residency = 0;
+  BlobLayout rl, sl;
+  BlobOffsets ro{}, so{};
+  // device weights
+  uint8_t* d_experts = nullptr;  // resident: E blobs at stride rl.stride
+  uint8_t* d_shared = nullptr;
+  int8_t* d_router_w = nullptr;
+  uint16_t* d_router_scale = nullptr;
+  float* d_router_bias = nullptr;
+  uint64_t* d_expert_addr = nullptr;  // [E]
+  // decode workspace
+  float* d_logits = nullptr;
+  int32_t* d_ids = nullptr;
+  float* d_wts = nullptr;
+  uint32_t* d_counter = nullptr;
+  void* d_abuf = nullptr;
+  float* d_asum = nullptr;
+  int32_t* d_err = nullptr;
+  // prefill workspace
+  char* d_prefill = nullptr;
+  size_t prefill_bytes = 0;
+  // previous call (for reuse_previous)
+  int prev_T = -1;
+  // streamed experts
+  uint8_t* h_store = nullptr;  // pinned, E blobs
+  uint8_t* d_slots = nullptr;
+  int n_slots = 0;
+  std::unique_ptr<LfuPolicy> lfu;
+  hipStream_t side = nullptr;
+  bool own_side = false;
+  hipEvent_t ev_fill = nullptr, ev_fill_start = nullptr;
+  bool fill_pending = false;
+  uint64_t* h_addr = nullptr;  // pinned mirror of d_expert_addr
+  int32_t* h_ids = nullptr;    // pinned routing copy
+  std::vector<char> fail_expert;
+  moe_cache_stats stats{};
+  uint64_t device_bytes = 0;
+};
+
+moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_opts* o, hipStream_t s);
+
+struct moe_stack {
+  std::vector<moe_layer*> layers;
+  float eps = 1e-6f;
+};
+
+struct moe_lfu {
+  LfuPolicy policy;
+  explicit moe_lfu(int n) : policy(n) {}
+};
+
+namespace {
+
+moe_status validate(const moe_layer_desc* D) {
+  if (!D) return fail(MOE_ERR_INVALID, "descriptor is NULL");
+  if (D->d_model <= 0 || D->d_model % 64 || D->d_model > 8192)
+    return fail(MOE_ERR_INVALID, "d_model=%d must be a positive multiple of 64 and <= 8192", D->d_model);
+  if (D->n_experts < 1 || D->n_experts > 1024) return fail(MOE_ERR_INVALID, "n_experts=%d not in 1..1024", D->n_experts);
+  if (D->top_k < 1 || D->top_k > D->n_experts || D->top_k > 64)
+    return fail(MOE_ERR_INVALID, "top_k=%d must be in 1..min(E,64)", D->top_k);
+  if (D->d_ff <= 0 || D->d_ff % 64) return fail(MOE_ERR_INVALID, "d_ff=%d must be a positive multiple of 64", D->d_ff);
+  if (D->d_ff_shared < 0 || D->d_ff_shared % 64)
+    return fail(MOE_ERR_INVALID, "d_ff_shared=%d must be a multiple of 64 (or 0)", D->d_ff_shared);
+  if (D->act_dtype != MOE_ACT_F32 && D->act_dtype != MOE_ACT_BF16)
+    return fail(MOE_ERR_INVALID, "act_dtype=%d unknown", D->act_dtype);
+  if (D->max_tokens < 1 || D->max_tokens > 65536) return fail(MOE_ERR_INVALID, "max_tokens=%d not in 1..65536", D->max_tokens);
+  if (D->residency != MOE_RESIDENT && D->residency != MOE_STREAMED)
+    return fail(MOE_ERR_INVALID, "residency=%d unknown", D->residency);
+  if (!D->router_w || !D->router_scale || !D->gate_q || !D->gate_s || !D->gate_b || !D->up_q || !D->up_s ||
+      !D->up_b || !D->down_q || !D->down_s || !D->down_b)
+    return fail(MOE_ERR_INVALID, "a routed weight pointer is NULL");
+  if (D->d_ff_shared > 0 && (!D->sh_gate_q || !D->sh_gate_s || !D->sh_gate_b || !D->sh_up_q || !D->sh_up_s ||
+                             !D->sh_up_b || !D->sh_down_q || !D->sh_down_s || !D->sh_down_b))
+    return fail(MOE_ERR_INVALID, "a shared-expert weight pointer is NULL");
+  const int F = D->d_ff_shared + D->top_k * D->d_ff;
+  const int NI = D->d_ff_shared / 64 + D->top_k * (D->d_ff / 64);
+  if (decode_lds_bytes_down(F, NI, D->top_k, D->act_dtype) > 64 * 1024)
+    return fail(MOE_ERR_INVALID, "d_ff_shared + top_k*d_ff = %d too large for the decode combine kernel", F);
+  return MOE_OK;
+}
+
+BlobOffsets offsets_of(const BlobLayout& L) {
+  return BlobOffsets{(uint32_t)L.gate.q_off, (uint32_t)L.gate.sb_off, (uint32_t)L.up.q_off,
+                     (uint32_t)L.up.sb_off,  (uint32_t)L.down.q_off, (uint32_t)L.down.sb_off};
+}
+
+// Repack experts [e0, e1) of the canonical arrays into consecutive blobs.
+void pack_experts(const moe_layer_desc* D, const BlobLayout& L, int e0, int e1, uint8_t* dst) {
+  const size_t gu_w = (size_t)D->d_ff * D->d_model / 8, gu_g = (size_t)D->d_ff * D->d_model / 64;
+  for (int e = e0; e < e1; ++e) {
+    uint8_t* blob = dst + (size_t)(e - e0) * L.stride;
+    std::memset(blob, 0, L.stride);
+    pack_matrix(L.gate, D->gate_q + e * gu_w, D->gate_s + e * gu_g, D->gate_b + e * gu_g, blob);
+    pack_matrix(L.up, D->up_q + e * gu_w, D->up_s + e * gu_g, D->up_b + e * gu_g, blob);
+    pack_matrix(L.down, D->down_q + e * gu_w, D->down_s + e * gu_g, D->down_b + e * gu_g, blob);
+  }
+}
+
+void pack_parallel(const moe_layer_desc* D, const BlobLayout& L, uint8_t* dst) {
+  const int E = D->n_experts;
+  const int nt = std::max(1, std::min<int>(E, (int)std::thread::hardware_concurrency()));
+  std::vector<std::thread> th;
+  for (int i = 0; i < nt; ++i) {
+    const int e0 = E * i / nt, e1 = E * (i + 1) / nt;
+    th.emplace_back([=] { pack_experts(D, L, e0, e1, dst + (size_t)e0 * L.stride); });
+  }
+  for (auto& t : th) t.join();
+}
+
+void free_layer(moe_layer* L) {
+  if (!L) return;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(L->d_experts);
+  (void)hipFree(L->d_shared);
+  (void)hipFree(L->d_router_w);
+  (void)hipFree(L->d_router_scale);
+  (void)hipFree(L->d_router_bias);
+  (void)hipFree(L->d_expert_addr);
+  (void)hipFree(L->d_logits);
+  (void)hipFree(L->d_ids);
+  (void)hipFree(L->d_wts);
+  (void)hipFree(L->d_counter);
+  (void)hipFree(L->d_abuf);
+  (void)hipFree(L->d_asum);
+  (void)hipFree(L->d_err);
+  (void)hipFree(L->d_prefill);
+  (void)hipFree(L->d_slots);
+  if (L->h_store) (void)hipHostFree(L->h_store);
+  if (L->h_addr) (void)hipHostFree(L->h_addr);
+  if (L->h_ids) (void)hipHostFree(L->h_ids);
+  if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
+  if (L->ev_fill_start) (void)hipEventDestroy(L->ev_fill_start);
+  if (L->own_side && L->side) (void)hipStreamDestroy(L->side);
+  delete L;
+}
+
+moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
+  HIP_OK(hipGetDevice(&L->dev));
+  L->d = D->d_model;
+  L->E = D->n_experts;
+  L->K = D->top_k;
+  L->f = D->d_ff;
+  L->fs = D->d_ff_shared;
+  L->act = D->act_dtype;
+  L->max_tokens = D->max_tokens;
+  L->residency = D->residency;
+  L->rl = make_blob_layout(L->d, L->f);
+  L->ro = offsets_of(L->rl);
+  if (L->fs > 0) {
+    L->sl = make_blob_layout(L->d, L->fs);
+    L->so = offsets_of(L->sl);
+  }
+  const size_t E = L->E, stride = L->rl.stride;
+  uint64_t dev_bytes = 0;
+  // routed experts
+  std::vector<uint64_t> addr(E, 0);
+  if (L->residency == MOE_RESIDENT) {
+    if (dalloc(&L->d_experts, E * stride) != hipSuccess)
+      return fail(MOE_ERR_NOMEM, "hipMalloc of %zu bytes of expert weights failed", E * stride);
+    dev_bytes += E * stride;
+    std::vector<uint8_t> host(E * stride);
+    pack_parallel(D, L->rl, host.data());
+    HIP_OK(hipMemcpy(L->d_experts, host.data(), E * stride, hipMemcpyHostToDevice));
+    for (size_t e = 0; e < E; ++e) addr[e] = reinterpret_cast<uint64_t>(L->d_experts + e * stride);
+  } else {
+    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_store), E * stride, hipHostMallocDefault) != hipSuccess)
+      return fail(MOE_ERR_NOMEM, "pinned host store of %zu bytes failed", E * stride);
+    pack_parallel(D, L->rl, L->h_store);
+    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_addr), E * 8, hipHostMallocDefault) != hipSuccess)
+      return fail(MOE_ERR_NOMEM, "pinned expert table failed");
+    std::memset(L->h_addr, 0, E * 8);
+    L->fail_expert.assign(E, 0);
+  }
+  // shared expert
+  if (L->fs > 0) {
+    std::vector<uint8_t> blob(L->sl.stride, 0);
+    pack_matrix(L->sl.gate, D->sh_gate_q, D->sh_gate_s, D->sh_gate_b, blob.data());
+    pack_matrix(L->sl.up, D->sh_up_q, D->sh_up_s, D->sh_up_b, blob.data());
+    pack_matrix(L->sl.down, D->sh_down_q, D->sh_down_s, D->sh_down_b, blob.data());
+    if (dalloc(&L->d_shared, blob.size()) != hipSuccess) return fail(MOE_ERR_NOMEM, "shared expert alloc failed");
+    HIP_OK(hipMemcpy(L->d_shared, blob.data(), blob.size(), hipMemcpyHostToDevice));
+    dev_bytes += blob.size();
+  }
+  // router
+  if (dalloc(&L->d_router_w, E * L->d) != hipSuccess || dalloc(&L->d_router_scale, E * 2) != hipSuccess)
+    return fail(MOE_ERR_NOMEM, "router alloc failed");
+  HIP_OK(hipMemcpy(L->d_router_w, D->router_w, E * L->d, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(L->d_router_scale, D->router_scale, E * 2, hipMemcpyHostToDevice));
+  dev_bytes += E * L->d + E * 2;
+  if (D->router_bias) {
+    if (dalloc(&L->d_router_bias, E * 4) != hipSuccess) return fail(MOE_ERR_NOMEM, "router bias alloc failed");
+    HIP_OK(hipMemcpy(L->d_router_bias, D->router_bias, E * 4, hipMemcpyHostToDevice));
+    dev_bytes += E * 4;
+  }
+  if (dalloc(&L->d_expert_addr, E * 8) != hipSuccess) return fail(MOE_ERR_NOMEM, "expert table alloc failed");
+  HIP_OK(hipMemcpy(L->d_expert_addr, addr.data(), E * 8, hipMemcpyHostToDevice));
+  // decode workspace
+  const size_t T = L->max_tokens, K = L->K;
+  const size_t F = L->fs + K * L->f;
+  if (dalloc(&L->d_logits, T * E * 4) != hipSuccess || dalloc(&L->d_ids, T * K * 4) != hipSuccess ||
+      dalloc(&L->d_wts, T * K * 4) != hipSuccess || dalloc(&L->d_counter, T * 4) != hipSuccess ||
+      dalloc(&L->d_abuf, T * F * 4) != hipSuccess || dalloc(&L->d_asum, T * (F / 8) * 4) != hipSuccess ||
+      dalloc(&L->d_err, 64) != hipSuccess)
+    return fail(MOE_ERR_NOMEM, "decode workspace alloc failed");
+  HIP_OK(hipMemset(L->d_ids, 0, T * K * 4));
+  HIP_OK(hipMemset(L->d_wts, 0, T * K * 4));
+  HIP_OK(hipMemset(L->d_counter, 0, T * 4));
+  HIP_OK(hipMemset(L->d_err, 0, 64));
+  // prefill workspace (bf16 only)
+  if (L->act == MOE_ACT_BF16 && L->max_tokens > 1) {
+    L->prefill_bytes = prefill_workspace_bytes((int)T, L->d, L->E, L->K, L->f, L->fs);
+    if (dalloc(&L->d_prefill, L->prefill_bytes) != hipSuccess) return fail(MOE_ERR_NOMEM, "prefill workspace alloc failed");
+    HIP_OK(hipMemset(L->d_prefill, 0, L->prefill_bytes));
+  }
+  L->device_bytes = dev_bytes;
+  HIP_OK(hipDeviceSynchronize());
+  return MOE_OK;
+}
+
+LayerArgs base_args(moe_layer* L, const void* x, void* out, int T) {
+  LayerArgs a{};
+  a.d = L->d; a.E = L->E; a.K = L->K; a.f = L->f; a.fs = L->fs; a.T = T;
+  a.act = L->act;
+  a.rms = 0;
+  a.eps = 1e-6f;
+  a.x = x;
+  a.router_w = L->d_router_w;
+  a.router_scale = L->d_router_scale;
+  a.router_bias = L->d_router_bias;
+  a.expert_addr = L->d_expert_addr;
+  a.shared_blob = L->d_shared;
+  a.ro = L->ro;
+  a.so = L->so;
+  a.logits = L->d_logits;
+  a.ids = L->d_ids;
+  a.wts = L->d_wts;
+  a.counter = L->d_counter;
+  a.abuf = L->d_abuf;
+  a.asum_part = L->d_asum;
+  a.err = L->d_err;
+  a.out = out;
+  return a;
+}
+
+// Make every expert chosen by the routing in L->d_ids resident in a slot,
+// after the router has run on `stream`.  Blocks on the routing copy.
+moe_status stream_in(moe_layer* L, int T, hipStream_t stream) {
+  if (!L->lfu) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
+  const size_t n = (size_t)T * L->K;
+  HIP_OK(hipMemcpyAsync(L->h_ids, L->d_ids, n * 4, hipMemcpyDeviceToHost, stream));
+  HIP_OK(hipStreamSynchronize(stream));
+  if (L->fill_pending) {  // account the previous call's fills (complete by now)
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, L->ev_fill_start, L->ev_fill) == hipSuccess) L->stats.h2d_ns += (uint64_t)(ms * 1e6);
+    L->fill_pending = false;
+  }
+  std::vector<int32_t> chosen(L->h_ids, L->h_ids + n);
+  std::sort(chosen.begin(), chosen.end());
+  chosen.erase(std::unique(chosen.begin(), chosen.end()), chosen.end());
+  for (int32_t e : chosen) {
+    if (e < 0 || e >= L->E) return fail(MOE_ERR_STATE, "routing produced expert id %d outside 0..%d", e, L->E - 1);
+    if (L->lfu->find(e) < 0 && L->fail_expert[e])
+      return fail(MOE_ERR_IO, "expert %d could not be read into a cache slot", e);
+  }
+  const int m = (int)chosen.size();
+  if (m > L->n_slots)
+    return fail(MOE_ERR_STATE, "call chose %d distinct experts but the cache has %d slots", m, L->n_slots);
+  std::vector<int32_t> slot(m), miss(m), evicted(m);
+  L->lfu->step(chosen.data(), m, slot.data(), miss.data(), evicted.data());
+  const size_t stride = L->rl.stride;
+  bool any = false;
+  for (int i = 0; i < m; ++i) {
+    if (!miss[i]) continue;
+    if (!any) HIP_OK(hipEventRecord(L->ev_fill_start, L->side));
+    any = true;
+    uint8_t* dst = L->d_slots + (size_t)slot[i] * stride;
+    HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice, L->side));
+    if (evicted[i] >= 0) L->h_addr[evicted[i]] = 0;
+    L->h_addr[chosen[i]] = reinterpret_cast<uint64_t>(dst);
+    L->stats.h2d_bytes += stride;
+  }
+  L->stats.accesses = L->lfu->accesses;
+  L->stats.hits = L->lfu->hits;
+  L->stats.misses = L->lfu->misses;
+  L->stats.evictions = L->lfu->evictions;
+  if (any) {
+    HIP_OK(hipEventRecord(L->ev_fill, L->side));
+    HIP_OK(hipStreamWaitEvent(stream, L->ev_fill, 0));
+    L->fill_pending = true;
+  }
+  HIP_OK(hipMemcpyAsync(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice, stream));
+  return MOE_OK;
+}
+
+moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStream_t s) {
+  const int T = a.T;
+  if (T == 0) return MOE_OK;
+  if (T < 0 || T > L->max_tokens) return fail(MOE_ERR_INVALID, "n_tokens=%d not in 0..%d", T, L->max_tokens);
+  HIP_OK(hipSetDevice(L->dev));
+  if (o) {
+    a.ids_out = o->topk_ids;
+    a.w_out = o->topk_w;
+    a.forced = o->forced_ids;
+    if (o->reuse_previous) {
+      if (o->forced_ids) return fail(MOE_ERR_INVALID, "forced_ids and reuse_previous are exclusive");
+      if (L->prev_T != T) return fail(MOE_ERR_STATE, "reuse_previous needs a previous call with the same n_tokens");
+      a.forced = L->d_ids;
+    }
+    if (o->residual) {
+      if (!o->residual_src) return fail(MOE_ERR_INVALID, "residual requested without residual_src");
+      a.resid = o->residual_src;
+    }
+  }
+  int path = o ? o->path : MOE_PATH_AUTO;
+  if (path == MOE_PATH_AUTO) path = (L->act == MOE_ACT_BF16 && T >= 16 && L->d_prefill) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
+  if (path == MOE_PATH_PREFILL) {
+    if (L->act != MOE_ACT_BF16 || !L->d_prefill)
+      return fail(MOE_ERR_INVALID, "the prefill path needs bf16 activations and max_tokens > 1");
+    if (L->residency == MOE_STREAMED) return fail(MOE_ERR_INVALID, "the prefill path needs resident experts");
+    moe_status st = launch_prefill_path(L, a, o, s);
+    if (st == MOE_OK) L->prev_T = T;
+    return st;
+  }
+  if (path != MOE_PATH_DECODE) return fail(MOE_ERR_INVALID, "unknown path %d", path);
+  if (L->residency == MOE_STREAMED) {
+    LayerArgs a1 = a;
+    a1.stages = kStageRouter | kStageShared;
+    HIP_OK(launch_decode(a1, s));
+    moe_status st = stream_in(L, T, s);
+    if (st != MOE_OK) return st;
+    LayerArgs a2 = a;
+    a2.stages = kStageRouted | kStageDown;
+    HIP_OK(launch_decode(a2, s));
+  } else {
+    HIP_OK(launch_decode(a, s));
+  }
+  L->prev_T = T;
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_opts* o, hipStream_t s) {
+  PrefillArgs p{};
+  p.L = a;
+  prefill_carve(p, L->d_prefill, a.T, L->d, L->E, L->K, L->f, L->fs);
+  p.sort_offsets_out = o ? o->sort_offsets : nullptr;
+  p.sort_perm_out = o ? o->sort_perm : nullptr;
+  HIP_OK(launch_prefill(p, s));
+  return MOE_OK;
+}
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_layer_create(const moe_layer_desc* desc, moe_layer** out) {
+  if (!out) return fail(MOE_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  moe_status st = validate(desc);
+  if (st != MOE_OK) return st;
+  moe_layer* L = new (std::nothrow) moe_layer();
+  if (!L) return fail(MOE_ERR_NOMEM, "host allocation failed");
+  st = create_impl(desc, L);
+  if (st != MOE_OK) {
+    std::string keep = g_err;
+    free_layer(L);
+    g_err = keep;
+    return st;
+  }
+  *out = L;
+  return MOE_OK;
+}
+
+moe_status moe_layer_destroy(moe_layer* layer) {
+  free_layer(layer);
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_ex(const void* x, moe_layer* L, void* out, int32_t n_tokens, const moe_fwd_opts* o,
+                                void* stream) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (n_tokens > 0 && (!x || !out)) return fail(MOE_ERR_INVALID, "x/out is NULL");
+  if (x == out && n_tokens > 0) return fail(MOE_ERR_INVALID, "x and out may not alias");
+  LayerArgs a = base_args(L, x, out, n_tokens);
+  return forward_impl(L, a, o, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_layer_forward(const void* x, moe_layer* L, void* out, int32_t n_tokens, void* stream) {
+  return moe_layer_forward_ex(x, L, out, n_tokens, nullptr, stream);
+}
+
+moe_status moe_layer_route(const void* x, moe_layer* L, int32_t* ids, float* w, int32_t n_tokens, void* stream) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (n_tokens == 0) return MOE_OK;
+  if (n_tokens < 0 || n_tokens > L->max_tokens)
+    return fail(MOE_ERR_INVALID, "n_tokens=%d not in 0..%d", n_tokens, L->max_tokens);
+  if (!x || !ids || !w) return fail(MOE_ERR_INVALID, "x/ids/w is NULL");
+  HIP_OK(hipSetDevice(L->dev));
+  LayerArgs a = base_args(L, x, nullptr, n_tokens);
+  a.stages = kStageRouter;
+  a.ids_out = ids;
+  a.w_out = w;
+  HIP_OK(launch_decode(a, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_layer_sort(const int32_t* ids, moe_layer* L, int32_t n_tokens, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, void* stream) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (n_tokens < 0 || n_tokens > L->max_tokens)
+    return fail(MOE_ERR_INVALID, "n_tokens=%d not in 0..%d", n_tokens, L->max_tokens);
+  if (!counts || !offsets || (n_tokens > 0 && (!ids || !perm || !inv)))
+    return fail(MOE_ERR_INVALID, "a sort buffer is NULL");
+  HIP_OK(hipSetDevice(L->dev));
+  HIP_OK(launch_sort(ids, n_tokens, L->K, L->E, counts, offsets, perm, inv, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_layer_bytes(const moe_layer* L, uint64_t* device_bytes, uint64_t* expert_bytes) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (device_bytes) *device_bytes = L->device_bytes;
+  if (expert_bytes) *expert_bytes = L->rl.stride;
+  return MOE_OK;
+}
+
+moe_status moe_layer_check_errors(moe_layer* L, int32_t* flags) {
+  if (!L || !flags) return fail(MOE_ERR_INVALID, "layer/flags is NULL");
+  HIP_OK(hipSetDevice(L->dev));
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(flags, L->d_err, 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemset(L->d_err, 0, 4));
+  return MOE_OK;
+}
+
+// ---- cache ----
+moe_status moe_cache_attach(moe_layer* L, int32_t n_slots, void* side_stream) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (L->residency != MOE_STREAMED) return fail(MOE_ERR_STATE, "layer is not MOE_STREAMED");
+  if (L->lfu) return fail(MOE_ERR_STATE, "layer already has a cache");
+  if (n_slots < L->K || n_slots > L->E) return fail(MOE_ERR_INVALID, "n_slots=%d not in top_k..n_experts", n_slots);
+  HIP_OK(hipSetDevice(L->dev));
+  const size_t bytes = (size_t)n_slots * L->rl.stride;
+  if (dalloc(&L->d_slots, bytes) != hipSuccess) return fail(MOE_ERR_NOMEM, "slot pool of %zu bytes failed", bytes);
+  if (hipHostMalloc(reinterpret_cast<void**>(&L->h_ids), (size_t)L->max_tokens * L->K * 4, hipHostMallocDefault) !=
+      hipSuccess)
+    return fail(MOE_ERR_NOMEM, "pinned routing buffer failed");
+  if (side_stream) {
+    L->side = static_cast<hipStream_t>(side_stream);
+  } else {
+    HIP_OK(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
+    L->own_side = true;
+  }
+  HIP_OK(hipEventCreate(&L->ev_fill));
+  HIP_OK(hipEventCreate(&L->ev_fill_start));
+  L->n_slots = n_slots;
+  L->lfu.reset(new LfuPolicy(n_slots));
+  L->device_bytes += bytes;
+  return MOE_OK;
+}
+
+moe_status moe_cache_stats_get(const moe_layer* L, moe_cache_stats* out) {
+  if (!L || !out) return fail(MOE_ERR_INVALID, "layer/out is NULL");
+  moe_layer* M = const_cast<moe_layer*>(L);
+  if (M->fill_pending) {
+    HIP_OK(hipEventSynchronize(M->ev_fill));
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, M->ev_fill_start, M->ev_fill) == hipSuccess) M->stats.h2d_ns += (uint64_t)(ms * 1e6);
+    M->fill_pending = false;
+  }
+  *out = L->stats;
+  return MOE_OK;
+}
+
+moe_status moe_cache_reset(moe_layer* L, int32_t drop_contents) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (!L->lfu) return fail(MOE_ERR_STATE, "layer has no cache");
+  HIP_OK(hipSetDevice(L->dev));
+  HIP_OK(hipDeviceSynchronize());
+  L->fill_pending = false;
+  L->stats = moe_cache_stats{};
+  L->lfu->clear_counters();
+  if (drop_contents) {
+    L->lfu->clear_contents();
+    std::memset(L->h_addr, 0, (size_t)L->E * 8);
+    HIP_OK(hipMemcpy(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_cache_contents(const moe_layer* L, int32_t* expert_of_slot, uint32_t* use_count) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (!L->lfu) return fail(MOE_ERR_STATE, "layer has no cache");
+  for (int s = 0; s < L->n_slots; ++s) {
+    if (expert_of_slot) expert_of_slot[s] = L->lfu->slots[s].expert;
+    if (use_count) use_count[s] = L->lfu->slots[s].count;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_cache_fail_expert(moe_layer* L, int32_t expert, int32_t failflag) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (L->residency != MOE_STREAMED) return fail(MOE_ERR_STATE, "layer is not MOE_STREAMED");
+  if (expert < 0 || expert >= L->E) return fail(MOE_ERR_INVALID, "expert %d out of range", expert);
+  L->fail_expert[expert] = failflag ? 1 : 0;
+  return MOE_OK;
+}
+
+// ---- stack ----
+moe_status moe_stack_create(moe_layer* const* layers, int32_t n, float eps, moe_stack** out) {
+  if (!out) return fail(MOE_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!layers || n < 1) return fail(MOE_ERR_INVALID, "need at least one layer");
+  for (int i = 0; i < n; ++i) {
+    if (!layers[i]) return fail(MOE_ERR_INVALID, "layer %d is NULL", i);
+    if (layers[i]->d != layers[0]->d || layers[i]->act != layers[0]->act)
+      return fail(MOE_ERR_INVALID, "layer %d has a different d_model or activation type", i);
+  }
+  if (!(eps > 0.f)) return fail(MOE_ERR_INVALID, "rms_eps must be positive");
+  moe_stack* S = new (std::nothrow) moe_stack();
+  if (!S) return fail(MOE_ERR_NOMEM, "host allocation failed");
+  S->layers.assign(layers, layers + n);
+  S->eps = eps;
+  *out = S;
+  return MOE_OK;
+}
+
+moe_status moe_stack_forward(void* h, moe_stack* S, int32_t n_tokens, const uint8_t* reuse_mask, int32_t* ids_out,
+                             void* stream) {
+  if (!S || !h) return fail(MOE_ERR_INVALID, "stack/h is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (size_t l = 0; l < S->layers.size(); ++l) {
+    moe_layer* L = S->layers[l];
+    LayerArgs a = base_args(L, h, h, n_tokens);
+    a.rms = 1;
+    a.eps = S->eps;
+    a.resid = h;
+    moe_fwd_opts o{};
+    o.reuse_previous = reuse_mask ? reuse_mask[l] : 0;
+    o.topk_ids = ids_out ? ids_out + l * (size_t)n_tokens * L->K : nullptr;
+    o.path = MOE_PATH_DECODE;
+    moe_status st = forward_impl(L, a, &o, s);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_stack_destroy(moe_stack* S) {
+  delete S;
+  return MOE_OK;
+}
+
+// ---- host-only policy ----
+moe_status moe_lfu_create(int32_t n_slots, moe_lfu** out) {
+  if (!out) return fail(MOE_ERR_INVALID, "out is NULL");
+  if (n_slots < 1 || n_slots > 1 << 20) return fail(MOE_ERR_INVALID, "n_slots=%d invalid", n_slots);
+  *out = new (std::nothrow) moe_lfu(n_slots);
+  return *out ? MOE_OK : fail(MOE_ERR_NOMEM, "host allocation failed");
+}
+
+moe_status moe_lfu_step(moe_lfu* P, const int32_t* chosen, int32_t n, int32_t* slot_out, int32_t* miss_out) {
+  if (!P || (n > 0 && (!chosen || !slot_out || !miss_out))) return fail(MOE_ERR_INVALID, "NULL argument");
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < i; ++j)
+      if (chosen[i] == chosen[j]) return fail(MOE_ERR_INVALID, "chosen ids must be distinct");
+  if (!P->policy.step(chosen, n, slot_out, miss_out, nullptr))
+    return fail(MOE_ERR_STATE, "%d chosen experts exceed %zu slots", n, P->policy.slots.size());
+  return MOE_OK;
+}
+
+moe_status moe_lfu_stats(const moe_lfu* P, moe_cache_stats* out) {
+  if (!P || !out) return fail(MOE_ERR_INVALID, "NULL argument");
+  *out = moe_cache_stats{P->policy.accesses, P->policy.hits, P->policy.misses, P->policy.evictions, 0, 0};
+  return MOE_OK;
+}
+
+moe_status moe_lfu_destroy(moe_lfu* P) {
+  delete P;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Device helpers shared by the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+// Packed dot products with fp32 accumulation (v_dot2_f32_bf16 / v_dot2_f32_f16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// Nibbles m and m+4 of a packed word as a pair of 16-bit floats whose value
+// is OFFSET + q: 0x4300|q is the bf16 128+q, 0x6400|q is the fp16 1024+q
+// (the nibble lands in the low mantissa bits, whose weight is exactly 1).
+template <uint32_t MAGIC>
+__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int m) {
+  return ((w >> (4 * m)) & 0x000F000Fu) | MAGIC;
+}
+constexpr uint32_t kMagicBf16 = 0x43004300u;  // 128 + q
+constexpr uint32_t kMagicF16 = 0x64006400u;   // 1024 + q
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {  // round to nearest even (finite inputs)
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f32_to_f16(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Sum over lanes that differ in the given xor bits (fixed butterfly order).
+__device__ __forceinline__ float xor_sum(float v, int mask_lo, int mask_hi) {
+  for (int m = mask_lo; m <= mask_hi; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace moe

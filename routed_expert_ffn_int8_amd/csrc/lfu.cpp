@@ -1,0 +1,72 @@
+#include "lfu.hpp"
+
+#include <algorithm>
+
+namespace moe {
+
+int LfuPolicy::find(int32_t expert) const {
+  for (size_t s = 0; s < slots.size(); ++s)
+    if (slots[s].expert == expert) return (int)s;
+  return -1;
+}
+
+void LfuPolicy::clear_contents() {
+  for (auto& s : slots) s = Slot{};
+}
+
+bool LfuPolicy::step(const int32_t* chosen, int n, int32_t* slot_out, int32_t* miss_out, int32_t* evicted_out) {
+  const int ns = (int)slots.size();
+  if (n > ns) return false;
+  ++now;
+  std::vector<char> pinned(ns, 0);
+  std::vector<int> miss_idx;
+  // hits first
+  for (int i = 0; i < n; ++i) {
+    int s = find(chosen[i]);
+    ++accesses;
+    if (s >= 0) {
+      ++hits;
+      slots[s].count += 1;
+      slots[s].tick = now;
+      pinned[s] = 1;
+      slot_out[i] = s;
+      miss_out[i] = 0;
+      if (evicted_out) evicted_out[i] = -1;
+    } else {
+      miss_idx.push_back(i);
+    }
+  }
+  // misses in ascending expert order
+  std::sort(miss_idx.begin(), miss_idx.end(), [&](int a, int b) { return chosen[a] < chosen[b]; });
+  for (int i : miss_idx) {
+    int victim = -1;
+    for (int s = 0; s < ns; ++s)
+      if (slots[s].expert < 0) {
+        victim = s;
+        break;
+      }
+    if (victim < 0) {
+      for (int s = 0; s < ns; ++s) {
+        if (pinned[s]) continue;
+        if (victim < 0) {
+          victim = s;
+          continue;
+        }
+        const Slot &a = slots[s], &v = slots[victim];
+        if (a.count < v.count || (a.count == v.count && a.tick < v.tick)) victim = s;
+      }
+      ++evictions;
+    }
+    if (evicted_out) evicted_out[i] = slots[victim].expert;
+    slots[victim].expert = chosen[i];
+    slots[victim].count = 1;
+    slots[victim].tick = now;
+    pinned[victim] = 1;
+    ++misses;
+    slot_out[i] = victim;
+    miss_out[i] = 1;
+  }
+  return true;
+}
+
+}  // namespace moe
