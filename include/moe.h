@@ -164,6 +164,26 @@ moe_status moe_layer_bytes(const moe_layer* layer, uint64_t* device_bytes, uint6
  * 0..E-1 (it was replaced by 0), bit 1 = a chosen expert was not resident. */
 moe_status moe_layer_check_errors(moe_layer* layer, int32_t* flags);
 
+/* Per-kernel timing.  enable != 0 brackets every kernel the layer launches
+ * with HIP events on the launch stream; 0 stops and discards the record.
+ * moe_layer_profile_read waits for the device, then fills HOST arrays
+ * launches[MOE_N_KERNELS] and total_ms[MOE_N_KERNELS] (index = MOE_KERNEL_*)
+ * with the launches timed since the last read and their summed durations. */
+enum {
+  MOE_KERNEL_ROUTE_SHARED = 0,   /* router GEMV + shared gate/up (decode) */
+  MOE_KERNEL_ROUTED_GATE_UP = 1, /* top-K + chosen experts' gate/up + SiLU*mul (decode) */
+  MOE_KERNEL_DOWN_COMBINE = 2,   /* down projections + weighted combine (decode) */
+  MOE_KERNEL_SORT = 3,           /* token->expert grouping (prefill) */
+  MOE_KERNEL_PREFILL_GATE_UP = 4,
+  MOE_KERNEL_PREFILL_DOWN = 5,
+  MOE_KERNEL_PREFILL_COMBINE = 6,
+  MOE_KERNEL_PREFILL_ROUTE = 7,
+  MOE_KERNEL_TOPK = 8,           /* stand-alone softmax top-K */
+  MOE_N_KERNELS = 9
+};
+moe_status moe_layer_profile(moe_layer* layer, int32_t enable);
+moe_status moe_layer_profile_read(moe_layer* layer, int64_t* launches, double* total_ms);
+
 /* ---- expert cache (MOE_STREAMED layers) --------------------------------
  * Rockchip-NPU plan §6.2.2/§6.2.3/§9.5: per-layer slots, LFU eviction; the
  * cache entry keeps a use count and a last-used tick.  Policy: a hit adds

@@ -34,6 +34,19 @@
 
 #include "moe_oracle.h"
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the OpenMP loops of this library will use. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 /* ---- exact storage-format decoding ------------------------------------- */
 
 double oracle_f16_to_f64(uint16_t h) {

@@ -18,6 +18,7 @@ typedef struct {
   const uint16_t *sh_gate_s, *sh_gate_b, *sh_up_s, *sh_up_b, *sh_down_s, *sh_down_b;
 } oracle_layer;
 
+int oracle_threads(void);
 double oracle_f16_to_f64(uint16_t h);
 double oracle_bf16_to_f64(uint16_t b);
 uint16_t oracle_f64_to_bf16(double v);

@@ -46,6 +46,8 @@ def lib():
             build()
         L = C.CDLL(_LIB_PATH)
         P, I = C.c_void_p, C.c_int
+        L.oracle_threads.restype = C.c_int
+        L.oracle_threads.argtypes = []
         L.oracle_f16_to_f64.restype = C.c_double
         L.oracle_f16_to_f64.argtypes = [C.c_uint16]
         L.oracle_bf16_to_f64.restype = C.c_double
@@ -150,6 +152,10 @@ def sort(ids: np.ndarray, E: int):
     inv = np.empty(T * K, np.int32)
     lib().oracle_sort(_p(ids), T, K, E, _p(counts), _p(offsets), _p(perm), _p(inv))
     return counts, offsets, perm, inv
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
 
 
 def f16_to_f64(h: int) -> float:

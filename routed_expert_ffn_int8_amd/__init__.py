@@ -66,6 +66,8 @@ _SIGS = {
     "moe_layer_sort": [_P, _P, C.c_int32, _P, _P, _P, _P, _P],
     "moe_layer_bytes": [_P, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)],
     "moe_layer_check_errors": [_P, C.POINTER(C.c_int32)],
+    "moe_layer_profile": [_P, C.c_int32],
+    "moe_layer_profile_read": [_P, _P, _P],
     "moe_cache_attach": [_P, C.c_int32, _P],
     "moe_cache_stats_get": [_P, C.POINTER(moe_cache_stats)],
     "moe_cache_reset": [_P, C.c_int32],
@@ -197,6 +199,22 @@ def moe_layer_check_errors(layer: int) -> int:
     f = C.c_int32()
     _check(load().moe_layer_check_errors(layer, C.byref(f)))
     return f.value
+
+
+MOE_KERNEL_NAMES = ["route_shared", "routed_gate_up", "down_combine", "sort", "prefill_gate_up",
+                    "prefill_down", "prefill_combine", "prefill_route", "topk"]
+
+
+def moe_layer_profile(layer: int, enable: bool = True):
+    _check(load().moe_layer_profile(layer, 1 if enable else 0))
+
+
+def moe_layer_profile_read(layer: int) -> dict:
+    n = len(MOE_KERNEL_NAMES)
+    launches = np.zeros(n, np.int64)
+    ms = np.zeros(n, np.float64)
+    _check(load().moe_layer_profile_read(layer, launches.ctypes.data, ms.ctypes.data))
+    return {MOE_KERNEL_NAMES[i]: (int(launches[i]), float(ms[i])) for i in range(n) if launches[i]}
 
 
 # ----------------------------------------------------------------- cache

@@ -52,6 +52,41 @@ hipError_t dalloc(T** p, size_t bytes) {
   return hipMalloc(reinterpret_cast<void**>(p), bytes ? bytes : 16);
 }
 
+// Brackets kernel launches with pooled HIP events; durations are read back
+// (after a device sync) by moe_layer_profile_read.
+struct EventProfiler : Profiler {
+  struct Rec {
+    int kernel;
+    hipEvent_t a, b;
+  };
+  std::vector<hipEvent_t> pool;
+  std::vector<Rec> recs;
+  hipError_t err = hipSuccess;
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) err = r;
+    return e;
+  }
+  void pair(int kernel, hipEvent_t* a, hipEvent_t* b) override {
+    *a = take();
+    *b = take();
+    if (*a && *b) recs.push_back(Rec{kernel, *a, *b});
+  }
+  ~EventProfiler() override {
+    for (auto& r : recs) {
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
+    }
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+};
+
 }  // namespace
 
 struct moe_layer {
@@ -62,6 +97,7 @@ struct moe_layer {
   // device weights
   uint8_t* d_experts = nullptr;  // resident: E blobs at stride rl.stride
   uint8_t* d_shared = nullptr;
+  uint8_t* d_zero = nullptr;  // one all-zero routed blob
   int8_t* d_router_w = nullptr;
   uint16_t* d_router_scale = nullptr;
   float* d_router_bias = nullptr;
@@ -69,6 +105,7 @@ struct moe_layer {
   // decode workspace
   float* d_logits = nullptr;
   int32_t* d_ids = nullptr;
+  uint64_t* d_sel = nullptr;  // [T][K] blob address per chosen expert
   float* d_wts = nullptr;
   uint32_t* d_counter = nullptr;
   void* d_abuf = nullptr;
@@ -93,6 +130,7 @@ struct moe_layer {
   std::vector<char> fail_expert;
   moe_cache_stats stats{};
   uint64_t device_bytes = 0;
+  std::unique_ptr<EventProfiler> prof;
 };
 
 moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_opts* o, hipStream_t s);
@@ -170,12 +208,14 @@ void free_layer(moe_layer* L) {
   (void)hipDeviceSynchronize();
   (void)hipFree(L->d_experts);
   (void)hipFree(L->d_shared);
+  (void)hipFree(L->d_zero);
   (void)hipFree(L->d_router_w);
   (void)hipFree(L->d_router_scale);
   (void)hipFree(L->d_router_bias);
   (void)hipFree(L->d_expert_addr);
   (void)hipFree(L->d_logits);
   (void)hipFree(L->d_ids);
+  (void)hipFree(L->d_sel);
   (void)hipFree(L->d_wts);
   (void)hipFree(L->d_counter);
   (void)hipFree(L->d_abuf);
@@ -224,11 +264,15 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
     if (hipHostMalloc(reinterpret_cast<void**>(&L->h_store), E * stride, hipHostMallocDefault) != hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned host store of %zu bytes failed", E * stride);
     pack_parallel(D, L->rl, L->h_store);
-    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_addr), E * 8, hipHostMallocDefault) != hipSuccess)
+    // pinned: expert table [E] followed by the chosen-blob table [max_tokens*K]
+    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_addr), (E + (size_t)L->max_tokens * L->K) * 8,
+                      hipHostMallocDefault) != hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned expert table failed");
     std::memset(L->h_addr, 0, E * 8);
     L->fail_expert.assign(E, 0);
   }
+  if (dalloc(&L->d_zero, stride) != hipSuccess) return fail(MOE_ERR_NOMEM, "zero blob alloc failed");
+  HIP_OK(hipMemset(L->d_zero, 0, stride));
   // shared expert
   if (L->fs > 0) {
     std::vector<uint8_t> blob(L->sl.stride, 0);
@@ -256,12 +300,16 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
   const size_t T = L->max_tokens, K = L->K;
   const size_t F = L->fs + K * L->f;
   if (dalloc(&L->d_logits, T * E * 4) != hipSuccess || dalloc(&L->d_ids, T * K * 4) != hipSuccess ||
-      dalloc(&L->d_wts, T * K * 4) != hipSuccess || dalloc(&L->d_counter, T * 4) != hipSuccess ||
+      dalloc(&L->d_wts, T * K * 4) != hipSuccess || dalloc(&L->d_sel, T * K * 8) != hipSuccess || dalloc(&L->d_counter, T * 4) != hipSuccess ||
       dalloc(&L->d_abuf, T * F * 4) != hipSuccess || dalloc(&L->d_asum, T * (F / 8) * 4) != hipSuccess ||
       dalloc(&L->d_err, 64) != hipSuccess)
     return fail(MOE_ERR_NOMEM, "decode workspace alloc failed");
   HIP_OK(hipMemset(L->d_ids, 0, T * K * 4));
   HIP_OK(hipMemset(L->d_wts, 0, T * K * 4));
+  {  // a valid address in every slot until the first routing
+    std::vector<uint64_t> z(T * K, reinterpret_cast<uint64_t>(L->d_zero));
+    HIP_OK(hipMemcpy(L->d_sel, z.data(), T * K * 8, hipMemcpyHostToDevice));
+  }
   HIP_OK(hipMemset(L->d_counter, 0, T * 4));
   HIP_OK(hipMemset(L->d_err, 0, 64));
   // prefill workspace (bf16 only)
@@ -286,17 +334,22 @@ LayerArgs base_args(moe_layer* L, const void* x, void* out, int T) {
   a.router_scale = L->d_router_scale;
   a.router_bias = L->d_router_bias;
   a.expert_addr = L->d_expert_addr;
+  a.expert_base = L->d_experts;
+  a.expert_stride = L->rl.stride;
   a.shared_blob = L->d_shared;
+  a.zero_blob = L->d_zero;
   a.ro = L->ro;
   a.so = L->so;
   a.logits = L->d_logits;
   a.ids = L->d_ids;
+  a.sel_addr = L->d_sel;
   a.wts = L->d_wts;
   a.counter = L->d_counter;
   a.abuf = L->d_abuf;
   a.asum_part = L->d_asum;
   a.err = L->d_err;
   a.out = out;
+  a.prof = L->prof.get();
   return a;
 }
 
@@ -347,6 +400,9 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream) {
     L->fill_pending = true;
   }
   HIP_OK(hipMemcpyAsync(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice, stream));
+  uint64_t* h_sel = reinterpret_cast<uint64_t*>(L->h_addr + L->E);
+  for (size_t i = 0; i < n; ++i) h_sel[i] = L->h_addr[L->h_ids[i]];
+  HIP_OK(hipMemcpyAsync(L->d_sel, h_sel, n * 8, hipMemcpyHostToDevice, stream));
   return MOE_OK;
 }
 
@@ -390,6 +446,7 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
     a2.stages = kStageRouted | kStageDown;
     HIP_OK(launch_decode(a2, s));
   } else {
+    a.topk_in_gate_up = 1;
     HIP_OK(launch_decode(a, s));
   }
   L->prev_T = T;
@@ -488,6 +545,41 @@ moe_status moe_layer_check_errors(moe_layer* L, int32_t* flags) {
   HIP_OK(hipDeviceSynchronize());
   HIP_OK(hipMemcpy(flags, L->d_err, 4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemset(L->d_err, 0, 4));
+  return MOE_OK;
+}
+
+moe_status moe_layer_profile(moe_layer* L, int32_t enable) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (enable && !L->prof) L->prof.reset(new EventProfiler());
+  if (!enable) {
+    if (L->prof) (void)hipDeviceSynchronize();
+    L->prof.reset();
+  }
+  return MOE_OK;
+}
+
+moe_status moe_layer_profile_read(moe_layer* L, int64_t* launches, double* total_ms) {
+  if (!L || !launches || !total_ms) return fail(MOE_ERR_INVALID, "NULL argument");
+  for (int k = 0; k < MOE_N_KERNELS; ++k) {
+    launches[k] = 0;
+    total_ms[k] = 0.0;
+  }
+  if (!L->prof) return MOE_OK;
+  EventProfiler* P = L->prof.get();
+  if (P->err != hipSuccess) return fail(MOE_ERR_HIP, "profiling event failed: %s", hipGetErrorString(P->err));
+  HIP_OK(hipSetDevice(L->dev));
+  HIP_OK(hipDeviceSynchronize());
+  for (auto& r : P->recs) {
+    float ms = 0.f;
+    HIP_OK(hipEventElapsedTime(&ms, r.a, r.b));
+    if (r.kernel >= 0 && r.kernel < MOE_N_KERNELS) {
+      launches[r.kernel] += 1;
+      total_ms[r.kernel] += ms;
+    }
+    P->pool.push_back(r.a);
+    P->pool.push_back(r.b);
+  }
+  P->recs.clear();
   return MOE_OK;
 }
 

@@ -1,30 +1,33 @@
 // Decode path (few tokens per call): three kernels per layer.
 //
-//   A  route_shared : int8 router GEMV for every expert (8 rows per workgroup)
-//                     with the softmax top-K run by the last router workgroup
-//                     of each token, side by side with the shared expert's
-//                     gate/up GEMV + SiLU*mul (routing-independent, so it
-//                     overlaps the router; Rockchip-NPU plan §2.4 runs the
-//                     shared expert while the routed experts are fetched).
+//   A  route_shared : int8 router GEMV (one router row per wavefront) with the
+//                     softmax top-K run by the last router workgroup of each
+//                     token, side by side with the shared expert's gate/up
+//                     GEMV + SiLU*mul (routing-independent, so it overlaps the
+//                     router; Rockchip-NPU plan §2.4 computes the shared
+//                     expert while routed experts are still being fetched).
 //   B  routed_gu    : gate/up GEMV + SiLU*mul of the K chosen experts.
-//   C  down_combine : down GEMV of the shared and K chosen experts, weighted
-//                     sum y = shared + sum_k w_k * down_k (BigMoeOnEdge,
-//                     "re-routing at every token and layer": weighted merge of
-//                     the chosen experts), optional residual, one store.
+//   C  down_combine : down GEMV of the shared and K chosen experts and the
+//                     weighted sum y = shared + sum_k w_k * down_k
+//                     (BigMoeOnEdge, "re-routing at every token and layer":
+//                     weighted merge of the chosen experts), optional
+//                     residual, one store per output element.
 //
-// Each workgroup owns an 8-row block of one matrix: lane (r = tid & 7,
-// jj = tid >> 3) reads 16-byte pieces of row r for the 64-wide groups
-// g = jj + 16 i, so every wavefront load instruction covers eight full
-// 128-byte lines.  All of a lane's weight loads are issued before the token
-// input is staged in LDS, to keep many bytes in flight.
+// Gate/up and down workgroups own an 8-row block of a matrix: lane
+// (r = tid & 7, jj = tid >> 3) reads the 16-byte halves of row r for the
+// 64-wide groups g = jj + 16 i, so every wavefront load instruction covers
+// eight whole 128-byte lines.  Each lane issues all of its weight loads in
+// straight-line code (clamped addresses, no branches) right after the token
+// or activation loads, so LDS staging overlaps the weight fetch and every
+// byte of the kernel is requested within its first microseconds.
 //
 // Arithmetic per 64-wide group (affine weights w = s*q + b, Rockchip-NPU
 // plan §2.1): sum_c w_c x_c = s * sum_c q_c x_c + b * sum_c x_c.
-// bf16 activations: nibble pairs become bf16 (128 + q) with one and-or and
-// feed v_dot2_f32_bf16 against bf16 pairs of x, then the 128 * sum(x) offset
-// is folded into the bias term.  The down projection uses fp16 (1024 + q)
-// against fp16-rounded activations the same way.  fp32 activations use an
-// exact byte->float convert and fp32 FMAs.
+// bf16 activations: a nibble pair becomes two bf16 values 128 + q with one
+// and-or and feeds v_dot2_f32_bf16 against bf16 pairs of x; the 128*sum(x)
+// offset is folded into the bias term.  The down projection does the same
+// with fp16 (1024 + q) against fp16-rounded activations.  fp32 activations
+// use an exact byte->float convert and fp32 FMAs.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -32,79 +35,122 @@ namespace moe {
 
 namespace {
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Load through the global address space (the pointers come from tables, so
+// the compiler cannot infer it and would emit flat loads).
+template <class T>
+__device__ __forceinline__ T ldg(const void* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) T*>(reinterpret_cast<uintptr_t>(p));
+}
+
 struct XStage {
   float* xf;   // [d] input as fp32 (after rounding to the activation type)
-  uint4* xp;   // [d/8] bf16 pairs (x[8j+m], x[8j+m+4]) for m = 0..3
+  v4u* xp;     // [d/8] bf16 pairs (x[8j+m], x[8j+m+4]) for m = 0..3
   float* xs;   // [d/64] group sums
-  float* red;  // [32] cross-wave scratch
+  float* red;  // [64] cross-wave scratch
 };
 
 __device__ __forceinline__ XStage carve_x(char* smem, int d) {
   XStage S;
   S.xf = reinterpret_cast<float*>(smem);
-  S.xp = reinterpret_cast<uint4*>(smem + (size_t)d * 4);
+  S.xp = reinterpret_cast<v4u*>(smem + (size_t)d * 4);
   S.xs = reinterpret_cast<float*>(smem + (size_t)d * 6);
   S.red = S.xs + d / 64;
   return S;
 }
 
-__host__ __device__ inline size_t x_stage_bytes(int d) { return (size_t)d * 6 + (size_t)(d / 64) * 4 + 32 * 4; }
+__host__ __device__ inline size_t x_stage_bytes(int d) { return (size_t)d * 6 + (size_t)(d / 64) * 4 + 64 * 4; }
 
-// Load token t, optionally apply rmsnorm (unit gain) and round to the
-// activation type, and fill xf / xp / xs.  Called by all threads.
+// Token loads issued before the weights: words j = tid + 256 i, i < kXPre.
+constexpr int kXPre = 2;
+struct XRegs {
+  v4u w[kXPre * 2];  // bf16: one 16-byte word per slot; fp32: two per slot
+};
+
 template <int ACT>
-__device__ void stage_x(const LayerArgs& a, int t, const XStage& S) {
-  const int tid = threadIdx.x;
-  const int d = a.d, W = d >> 3;
-  float ss = 0.f;
-  for (int j = tid; j < W; j += kThreads) {
-    float v[8];
+__device__ __forceinline__ void x_issue(const LayerArgs& a, int t, XRegs& R) {
+  const int tid = threadIdx.x, W = a.d >> 3;
+  const char* base = static_cast<const char*>(a.x) + (size_t)t * a.d * (ACT == 1 ? 2 : 4);
+#pragma unroll
+  for (int i = 0; i < kXPre; ++i) {
+    const int j = min(tid + kThreads * i, W - 1);
     if (ACT == 1) {
-      const uint4 raw = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * d)[j];
-      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        v[2 * m] = __uint_as_float(w4[m] << 16);
-        v[2 * m + 1] = __uint_as_float(w4[m] & 0xFFFF0000u);
-      }
+      R.w[i] = ldg<v4u>(base + (size_t)j * 16);
     } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)t * d);
-      const float4 p0 = src[2 * j], p1 = src[2 * j + 1];
-      v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
-      v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      S.xf[8 * j + m] = v[m];
-      ss = fmaf(v[m], v[m], ss);
+      R.w[2 * i] = ldg<v4u>(base + (size_t)j * 32);
+      R.w[2 * i + 1] = ldg<v4u>(base + (size_t)j * 32 + 16);
     }
   }
+}
+
+template <int ACT>
+__device__ __forceinline__ void word_values(const LayerArgs& a, int t, const XRegs& R, int i, int j, float v[8]) {
+  v4u p0, p1;
+  if (i < kXPre) {
+    p0 = R.w[ACT == 1 ? i : 2 * i];
+    p1 = R.w[ACT == 1 ? i : 2 * i + 1];
+  } else {  // words beyond the pre-issued ones (d > 4096)
+    const char* base = static_cast<const char*>(a.x) + (size_t)t * a.d * (ACT == 1 ? 2 : 4);
+    if (ACT == 1) {
+      p0 = ldg<v4u>(base + (size_t)j * 16);
+    } else {
+      p0 = ldg<v4u>(base + (size_t)j * 32);
+      p1 = ldg<v4u>(base + (size_t)j * 32 + 16);
+    }
+  }
+  if (ACT == 1) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      v[2 * m] = __uint_as_float(p0[m] << 16);
+      v[2 * m + 1] = __uint_as_float(p0[m] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      v[m] = __uint_as_float(p0[m]);
+      v[4 + m] = __uint_as_float(p1[m]);
+    }
+  }
+}
+
+// Finish staging token t: optional rmsnorm (unit gain) + rounding to the
+// activation type, then xf / xp / xs in LDS.  Called by all threads.
+template <int ACT>
+__device__ void x_commit(const LayerArgs& a, int t, const XRegs& R, const XStage& S) {
+  const int tid = threadIdx.x;
+  const int d = a.d, W = d >> 3;
   float inv = 1.f;
   if (a.rms) {
+    float ss = 0.f;
+    for (int i = 0, j = tid; j < W; ++i, j += kThreads) {
+      float v[8];
+      word_values<ACT>(a, t, R, i, j, v);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ss = fmaf(v[m], v[m], ss);
+    }
     ss = xor_sum(ss, 1, 32);
     if ((tid & 63) == 0) S.red[tid >> 6] = ss;
     __syncthreads();
-    const float tot = S.red[0] + S.red[1];
-    inv = 1.0f / sqrtf(tot / (float)d + a.eps);
+    inv = 1.0f / sqrtf(((S.red[0] + S.red[1]) + (S.red[2] + S.red[3])) / (float)d + a.eps);
   }
-  for (int j = tid; j < W; j += kThreads) {
+  for (int i = 0, j = tid; j < W; ++i, j += kThreads) {
     float v[8];
+    word_values<ACT>(a, t, R, i, j, v);
+    if (a.rms) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      float u = S.xf[8 * j + m];
-      if (a.rms) {
-        u *= inv;
-        if (ACT == 1) u = bf16_to_f32(f32_to_bf16(u));
-        S.xf[8 * j + m] = u;
+      for (int m = 0; m < 8; ++m) {
+        v[m] *= inv;
+        if (ACT == 1) v[m] = bf16_to_f32(f32_to_bf16(v[m]));
       }
-      v[m] = u;
     }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) S.xf[8 * j + m] = v[m];
     if (ACT == 1) {
-      uint4 p;
-      p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[4]) << 16);
-      p.y = (uint32_t)f32_to_bf16(v[1]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-      p.z = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[6]) << 16);
-      p.w = (uint32_t)f32_to_bf16(v[3]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+      v4u p;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        p[m] = (uint32_t)f32_to_bf16(v[m]) | ((uint32_t)f32_to_bf16(v[m + 4]) << 16);
       S.xp[j] = p;
     }
     float part = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
@@ -114,23 +160,23 @@ __device__ void stage_x(const LayerArgs& a, int t, const XStage& S) {
   __syncthreads();
 }
 
-// One 64-wide group: returns sum_c q_c * x_c (bf16 mode: sum_c (128+q_c) x_c).
+// One 64-wide group: sum_c q_c * x_c (bf16 mode: sum_c (128+q_c) x_c).
 template <int ACT>
-__device__ __forceinline__ float group_dot(const uint4 q[2], const XStage& S, int g) {
+__device__ __forceinline__ float group_dot(const v4u& q0, const v4u& q1, const XStage& S, int g) {
   float p = 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t w4[4] = {q[h].x, q[h].y, q[h].z, q[h].w};
+    const v4u q = h ? q1 : q0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t w = w4[m];
+      const uint32_t w = q[m];
       const int word = g * 8 + h * 4 + m;
       if (ACT == 1) {
-        const uint4 xw = S.xp[word];
-        p = dot2_bf16(nib_pair<kMagicBf16>(w, 0), xw.x, p);
-        p = dot2_bf16(nib_pair<kMagicBf16>(w, 1), xw.y, p);
-        p = dot2_bf16(nib_pair<kMagicBf16>(w, 2), xw.z, p);
-        p = dot2_bf16(nib_pair<kMagicBf16>(w, 3), xw.w, p);
+        const v4u xw = S.xp[word];
+        p = dot2_bf16(nib_pair<kMagicBf16>(w, 0), xw[0], p);
+        p = dot2_bf16(nib_pair<kMagicBf16>(w, 1), xw[1], p);
+        p = dot2_bf16(nib_pair<kMagicBf16>(w, 2), xw[2], p);
+        p = dot2_bf16(nib_pair<kMagicBf16>(w, 3), xw[3], p);
       } else {
         const float4 x0 = reinterpret_cast<const float4*>(S.xf)[word * 2];
         const float4 x1 = reinterpret_cast<const float4*>(S.xf)[word * 2 + 1];
@@ -149,12 +195,12 @@ __device__ __forceinline__ float group_dot(const uint4 q[2], const XStage& S, in
   return p;
 }
 
-// Group contribution s*sum(q x) + b*sum(x), with the bf16 magic offset folded in.
+// Group contribution s*sum(q x) + b*sum(x), with the magic offset folded in.
 template <int ACT>
-__device__ __forceinline__ float group_term(float p, uint32_t sb, float xsum) {
+__device__ __forceinline__ float group_term(float p, uint32_t sb, float xsum, float offset) {
   const float s = f16_to_f32((uint16_t)(sb & 0xFFFFu));
   const float b = f16_to_f32((uint16_t)(sb >> 16));
-  const float bb = (ACT == 1) ? b - 128.f * s : b;
+  const float bb = (ACT == 1) ? b - offset * s : b;
   return fmaf(s, p, bb * xsum);
 }
 
@@ -173,7 +219,13 @@ __device__ __forceinline__ float store_a(void* abuf_t, int P, float v) {
   return v;
 }
 
-// gate/up GEMV + SiLU*mul for the 8-row block `rb` of one expert blob.
+__device__ __forceinline__ char* abuf_of(const LayerArgs& a, int t, int act) {
+  const int F = a.fs + a.K * a.f;
+  return static_cast<char*>(a.abuf) + (size_t)t * F * (act == 1 ? 2 : 4);
+}
+
+// gate/up GEMV + SiLU*mul for the 8-row block `rb` of one expert blob;
+// the result goes to positions apos + rows of the activation vector.
 template <int ACT, int MAXI>
 __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, const BlobOffsets& o, int rb,
                               int apos, const XStage& S) {
@@ -182,32 +234,32 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
   const int row = rb * 8 + r;
   const uint8_t* gq = blob + o.gq;
   const uint8_t* uq = blob + o.uq;
-  const uint32_t* gsb = reinterpret_cast<const uint32_t*>(blob + o.gsb);
-  const uint32_t* usb = reinterpret_cast<const uint32_t*>(blob + o.usb);
+  const uint8_t* gsb = blob + o.gsb + (size_t)row * G * 4;
+  const uint8_t* usb = blob + o.usb + (size_t)row * G * 4;
+  XRegs xr;
+  x_issue<ACT>(a, t, xr);
   float accg = 0.f, accu = 0.f;
-  for (int base = 0; base < G; base += 16 * MAXI) {
-    uint4 qg[MAXI][2], qu[MAXI][2];
+  for (int base = 0; base < G; base += 32 * MAXI) {
+    v4u qg0[MAXI], qg1[MAXI], qu0[MAXI], qu1[MAXI];
     uint32_t sg[MAXI], su[MAXI];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-      const int g = base + jj + 16 * i;
-      if (g < G) {
-        const size_t off = (((size_t)rb * G + g) * 2) * 128 + r * 16;
-        qg[i][0] = *reinterpret_cast<const uint4*>(gq + off);
-        qg[i][1] = *reinterpret_cast<const uint4*>(gq + off + 128);
-        qu[i][0] = *reinterpret_cast<const uint4*>(uq + off);
-        qu[i][1] = *reinterpret_cast<const uint4*>(uq + off + 128);
-        sg[i] = gsb[(size_t)row * G + g];
-        su[i] = usb[(size_t)row * G + g];
-      }
+      const int g = min(base + jj + 32 * i, G - 1);
+      const size_t off = (((size_t)rb * G + g) * 2) * 128 + r * 16;
+      qg0[i] = ldg<v4u>(gq + off);
+      qg1[i] = ldg<v4u>(gq + off + 128);
+      qu0[i] = ldg<v4u>(uq + off);
+      qu1[i] = ldg<v4u>(uq + off + 128);
+      sg[i] = ldg<uint32_t>(gsb + g * 4);
+      su[i] = ldg<uint32_t>(usb + g * 4);
     }
-    if (base == 0) stage_x<ACT>(a, t, S);
+    if (base == 0) x_commit<ACT>(a, t, xr, S);
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-      const int g = base + jj + 16 * i;
+      const int g = base + jj + 32 * i;
       if (g < G) {
-        accg += group_term<ACT>(group_dot<ACT>(qg[i], S, g), sg[i], S.xs[g]);
-        accu += group_term<ACT>(group_dot<ACT>(qu[i], S, g), su[i], S.xs[g]);
+        accg += group_term<ACT>(group_dot<ACT>(qg0[i], qg1[i], S, g), sg[i], S.xs[g], 128.f);
+        accu += group_term<ACT>(group_dot<ACT>(qu0[i], qu1[i], S, g), su[i], S.xs[g], 128.f);
       }
     }
   }
@@ -219,33 +271,20 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
   }
   __syncthreads();
   if (tid < 8) {
-    const float gsum = S.red[r * 2] + S.red[16 + r * 2];
-    const float usum = S.red[r * 2 + 1] + S.red[16 + r * 2 + 1];
+    const float gsum = (S.red[r * 2] + S.red[16 + r * 2]) + (S.red[32 + r * 2] + S.red[48 + r * 2]);
+    const float usum = (S.red[r * 2 + 1] + S.red[16 + r * 2 + 1]) + (S.red[32 + r * 2 + 1] + S.red[48 + r * 2 + 1]);
     const int F = a.fs + a.K * a.f;
-    char* abuf_t = static_cast<char*>(a.abuf) + (size_t)t * F * (ACT == 1 ? 2 : 4);
     const int P = apos + row;
-    float seen = store_a<ACT>(abuf_t, P, silu(gsum) * usum);
+    float seen = store_a<ACT>(abuf_of(a, t, ACT), P, silu(gsum) * usum);
     seen = xor_sum(seen, 1, 4);
     if (tid == 0) a.asum_part[(size_t)t * (F / 8) + (P >> 3)] = seen;
   }
 }
 
-// Orderable 64-bit key: larger logit first, then lower expert index.
-__device__ __forceinline__ uint64_t topk_key(float l, int e) {
-  uint32_t u = __float_as_uint(l + 0.0f);  // -0 -> +0
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// Orderable 32-bit key of a logit: larger logit -> larger key (-0 == +0).
+__device__ __forceinline__ uint32_t order_key(float l) {
+  uint32_t u = __float_as_uint(l + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -254,14 +293,27 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return v;
 }
 
-// Softmax top-K of token t by one wavefront (lane = threadIdx.x < 64).
-// Ordering (logit desc, index asc); ids written ascending; weights are a
-// softmax over the chosen set (= softmax over all experts renormalised).
-__device__ void topk_token(const LayerArgs& a, int t) {
-  const int lane = threadIdx.x;
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Softmax top-K of token t by one wavefront (lane = threadIdx.x & 63).
+// Selection order: logit descending, expert index ascending on ties.  The
+// K-th largest key is found by a radix search over the 32 key bits with
+// wavefront ballots (no cross-lane data movement), ties at that key are
+// taken in index order, and the chosen experts are compacted in ascending
+// index order.  Weights: softmax over the chosen set, i.e. a softmax over
+// all experts renormalised to the chosen ones.  On return lane k < K holds
+// the k-th chosen expert (ascending) in *id and its weight in *w.
+// `scratch` is LDS space for 2*K words private to this wavefront.
+// NE = logits held per lane (E <= 64 * NE), a compile-time constant so the
+// radix loop has no per-slice branches.
+template <int NE>
+__device__ void topk_wave(const LayerArgs& a, int t, const float* lt, int* id_out, float* w_out, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.K;
-  const float* lt = a.logits + (size_t)t * E;
   int my_id = 0;
+  float my_l = -INFINITY;
   if (a.forced) {
     if (lane < K) {
       my_id = a.forced[(size_t)t * K + lane];
@@ -269,72 +321,196 @@ __device__ void topk_token(const LayerArgs& a, int t) {
         atomicOr(a.err, kErrBadForcedId);
         my_id = 0;
       }
+      my_l = lt[my_id];
+    }
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {  // ascending order, unique rank even for repeated ids
+      const int o = __shfl(my_id, j, 64);
+      rank += (o < my_id || (o == my_id && j < lane)) ? 1 : 0;
+    }
+    if (lane < K) {
+      scratch[rank] = (uint32_t)my_id;
+      scratch[K + rank] = __float_as_uint(my_l);
     }
   } else {
-    uint64_t key[16];
+    uint32_t key[NE];
+    float lv[NE];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NE; ++i) {
       const int e = lane + 64 * i;
-      key[i] = (e < E) ? topk_key(lt[e], e) : 0ull;
+      const bool ok = e < E;
+      lv[i] = ok ? lt[e] : -INFINITY;
+      key[i] = ok ? order_key(lv[i]) : 0u;
     }
-    for (int k = 0; k < K; ++k) {
-      uint64_t m = key[0];
+    uint32_t prefix = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) m = key[i] > m ? key[i] : m;
-      m = wave_max_u64(m);
-      const int win = (int)(0xFFFFFFFFu - (uint32_t)m);
+      for (int i = 0; i < NE; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+      if (cnt >= K) prefix = cand;
+    }
+    int gt = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (lane + 64 * i == win) key[i] = 0ull;
-      if (lane == k) my_id = win;
+    for (int i = 0; i < NE; ++i) gt += __popcll(__ballot(key[i] > prefix));
+    const int need = K - gt;
+    int eq_before = 0, pos_base = 0;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      {
+        const int e = lane + 64 * i;
+        const bool valid = e < E;
+        const uint64_t eqm = __ballot(valid && key[i] == prefix);
+        const bool take_eq = valid && key[i] == prefix && (eq_before + lanes_below(eqm)) < need;
+        eq_before += __popcll(eqm);
+        const bool sel = key[i] > prefix || take_eq;
+        const uint64_t sm = __ballot(sel);
+        if (sel) {
+          const int pos = pos_base + lanes_below(sm);
+          scratch[pos] = (uint32_t)e;
+          scratch[K + pos] = __float_as_uint(lv[i]);
+        }
+        pos_base += __popcll(sm);
+      }
     }
   }
-  const float l = (lane < K) ? lt[my_id] : -INFINITY;
-  const float lmax = wave_max_f32(l);
-  const float v = (lane < K) ? expf(l - lmax) : 0.f;
-  const float den = xor_sum(v, 1, 32);
-  int rank = 0;
-  for (int j = 0; j < K; ++j) {  // unique rank even if a forced set repeats an id
-    const int o = __shfl(my_id, j, 64);
-    rank += (o < my_id || (o == my_id && j < lane)) ? 1 : 0;
-  }
+  __threadfence_block();
   if (lane < K) {
-    const float w = v / den;
-    a.ids[(size_t)t * K + rank] = my_id;
-    a.wts[(size_t)t * K + rank] = w;
-    if (a.ids_out) a.ids_out[(size_t)t * K + rank] = my_id;
-    if (a.w_out) a.w_out[(size_t)t * K + rank] = w;
+    my_id = (int)scratch[lane];
+    my_l = __uint_as_float(scratch[K + lane]);
+  } else {
+    my_l = -INFINITY;
+  }
+  const float lmax = wave_max_f32(my_l);
+  const float v = (lane < K) ? expf(my_l - lmax) : 0.f;
+  const float den = xor_sum(v, 1, 32);
+  *id_out = my_id;
+  *w_out = v / den;
+}
+
+// The k-th chosen expert of token t (ascending order), uniform across the
+// calling wavefront: the same radix search as topk_wave, then the lane whose
+// compacted position is k is located with a ballot; no data leaves a lane.
+template <int NE>
+__device__ int topk_kth(const LayerArgs& a, int t, const float* lt, int k) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, K = a.K;
+  if (a.forced) {
+    int my_id = 0;
+    if (lane < K) {  // an out-of-range id is replaced by 0 (and flagged by topk_wave)
+      const int v = a.forced[(size_t)t * K + lane];
+      my_id = (v < 0 || v >= E) ? 0 : v;
+    }
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {
+      const int o = __shfl(my_id, j, 64);
+      rank += (o < my_id || (o == my_id && j < lane)) ? 1 : 0;
+    }
+    const uint64_t m = __ballot(lane < K && rank == k);
+    return __shfl(my_id, (int)__builtin_ctzll(m), 64);
+  }
+  uint32_t key[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = (e < E) ? order_key(lt[e]) : 0u;
+  }
+  uint32_t prefix = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= K) prefix = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) gt += __popcll(__ballot(key[i] > prefix));
+  const int need = K - gt;
+  int eq_before = 0, pos_base = 0, found = 0;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    {
+      const int e = lane + 64 * i;
+      const bool valid = e < E;
+      const uint64_t eqm = __ballot(valid && key[i] == prefix);
+      const bool take_eq = valid && key[i] == prefix && (eq_before + lanes_below(eqm)) < need;
+      eq_before += __popcll(eqm);
+      const bool sel = key[i] > prefix || take_eq;
+      const uint64_t sm = __ballot(sel);
+      const uint64_t hit = __ballot(sel && pos_base + lanes_below(sm) == k);
+      if (hit) found = (int)__builtin_ctzll(hit) + 64 * i;
+      pos_base += __popcll(sm);
+    }
+  }
+  return found;
+}
+
+// Copy the logits of token t into LDS with straight-line loads (E <= 1024),
+// ending with a workgroup barrier.  `nthreads` threads take part.
+template <int NTH>
+__device__ __forceinline__ void stage_logits(const LayerArgs& a, int t, float* s_logits) {
+  const float* lt = a.logits + (size_t)t * a.E;
+  constexpr int N = (1024 + NTH - 1) / NTH;
+  float v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = ldg<float>(lt + min((int)threadIdx.x + NTH * i, a.E - 1));
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int e = threadIdx.x + NTH * i;
+    if (e < a.E) s_logits[e] = v[i];
+  }
+  __syncthreads();
+}
+
+// Publish the routing of token t (lane k < K holds the k-th chosen expert).
+__device__ __forceinline__ void publish_routing(const LayerArgs& a, int t, int lane, int id, float w) {
+  if (lane < a.K) {
+    const size_t o = (size_t)t * a.K + lane;
+    a.ids[o] = id;
+    a.wts[o] = w;
+    a.sel_addr[o] = a.expert_addr[id];
+    if (a.ids_out) a.ids_out[o] = id;
+    if (a.w_out) a.w_out[o] = w;
   }
 }
 
 // ---------------------------------------------------------------- kernel A
+constexpr int kRouterPre = 8;  // 16-byte router chunks per lane issued up front (d <= 8192)
+constexpr int kWaves = kThreads / 64;
+
 template <int ACT, int MAXI>
 __global__ __launch_bounds__(kThreads) void route_shared_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const XStage S = carve_x(smem, a.d);
   const int t = blockIdx.y;
-  const int NR = (a.E + 7) >> 3;
-  const int tid = threadIdx.x;
+  const int NR = (a.E + kWaves - 1) / kWaves;  // one router row per wavefront
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if ((int)blockIdx.x >= NR) {
     gate_up_block<ACT, MAXI>(a, t, a.shared_blob, a.so, blockIdx.x - NR, 0, S);
     return;
   }
-  // router rows e0 .. e0+7
-  const int r = tid & 7, jj = tid >> 3;
-  const int e = blockIdx.x * 8 + r;
-  const int d = a.d, NC = d >> 4;
-  stage_x<ACT>(a, t, S);
+  const int e = blockIdx.x * kWaves + wave;
+  const int ec = min(e, a.E - 1);
+  const int NC = a.d >> 4;  // 16-byte chunks per router row
+  const int8_t* wrow = a.router_w + (size_t)ec * a.d;
+  XRegs xr;
+  x_issue<ACT>(a, t, xr);
+  v4u wr[kRouterPre];
+#pragma unroll
+  for (int i = 0; i < kRouterPre; ++i) wr[i] = ldg<v4u>(wrow + (size_t)min(lane + 64 * i, NC - 1) * 16);
+  x_commit<ACT>(a, t, xr, S);
   float acc = 0.f;
-  if (e < a.E) {
-    const int8_t* wrow = a.router_w + (size_t)e * d;
-    for (int c = jj; c < NC; c += 16) {
-      const int4 w16 = *reinterpret_cast<const int4*>(wrow + c * 16);
-      const int w4[4] = {w16.x, w16.y, w16.z, w16.w};
+#pragma unroll
+  for (int i = 0; i < kRouterPre; ++i) {
+    const int c = lane + 64 * i;
+    if (c < NC) {
       const float4* xv = reinterpret_cast<const float4*>(S.xf + c * 16);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float4 xx = xv[m];
-        const int w = w4[m];
+        const int w = (int)wr[i][m];
         acc = fmaf((float)((w << 24) >> 24), xx.x, acc);
         acc = fmaf((float)((w << 16) >> 24), xx.y, acc);
         acc = fmaf((float)((w << 8) >> 24), xx.z, acc);
@@ -342,47 +518,57 @@ __global__ __launch_bounds__(kThreads) void route_shared_kernel(LayerArgs a) {
       }
     }
   }
-  acc = xor_sum(acc, 8, 32);
-  if ((tid & 63) < 8) S.red[(tid >> 6) * 8 + r] = acc;
-  __syncthreads();
-  if (tid < 8 && e < a.E) {
-    const float tot = S.red[r] + S.red[8 + r];
+  acc = xor_sum(acc, 1, 32);
+  if (lane == 0 && e < a.E) {
     const float s = f16_to_f32(a.router_scale[e]);
     const float b = a.router_bias ? a.router_bias[e] : 0.f;
-    a.logits[(size_t)t * a.E + e] = fmaf(s, tot, b);
+    a.logits[(size_t)t * a.E + e] = fmaf(s, acc, b);
   }
-  // last router workgroup of this token runs the top-K
-  __threadfence();
-  __syncthreads();
-  __shared__ int last;
-  if (tid == 0) last = (atomicAdd(a.counter + t, 1u) == (unsigned)(NR - 1));
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (tid < 64) topk_token(a, t);
-  if (tid == 0) atomicExch(a.counter + t, 0u);
+}
+
+// Stand-alone top-K (one wavefront per token), used when the routing must be
+// known before the expert kernels are enqueued.
+template <int NE>
+__global__ __launch_bounds__(64) void topk_kernel(LayerArgs a) {
+  __shared__ uint32_t scratch[128];
+  __shared__ float s_logits[1024];
+  stage_logits<64>(a, blockIdx.x, s_logits);
+  int id;
+  float w;
+  topk_wave<NE>(a, blockIdx.x, s_logits, &id, &w, scratch);
+  publish_routing(a, blockIdx.x, threadIdx.x, id, w);
 }
 
 // ---------------------------------------------------------------- kernel B
-template <int ACT, int MAXI>
+template <int ACT, int MAXI, int NE>
 __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
+  __shared__ uint32_t scratch[128];
+  __shared__ float s_logits[1024];
   const XStage S = carve_x(smem, a.d);
   const int t = blockIdx.y;
   const int RB = a.f >> 3;
-  const int k = blockIdx.x / RB, rb = blockIdx.x % RB;
-  const int id = a.ids[(size_t)t * a.K + k];
-  const uint8_t* blob = reinterpret_cast<const uint8_t*>(a.expert_addr[id]);
-  if (blob == nullptr) {  // expert not resident: leave a marker, contribute zeros
-    if (threadIdx.x == 0) atomicOr(a.err, kErrMissingExpert);
-    const int F = a.fs + a.K * a.f;
-    const int P = a.fs + k * a.f + rb * 8;
-    if (threadIdx.x < 8) {
-      char* abuf_t = static_cast<char*>(a.abuf) + (size_t)t * F * (ACT == 1 ? 2 : 4);
-      store_a<ACT>(abuf_t, P + threadIdx.x, 0.f);
+  const int k = blockIdx.x / RB, rb = blockIdx.x - k * RB;
+  const uint8_t* blob;
+  if (a.topk_in_gate_up) {  // resident experts: every wavefront finds its expert itself
+    stage_logits<kThreads>(a, t, s_logits);
+    if (k == a.K) {  // one extra workgroup publishes ids and weights for the combine kernel
+      if (threadIdx.x < 64) {
+        int id;
+        float w;
+        topk_wave<NE>(a, t, s_logits, &id, &w, scratch);
+        publish_routing(a, t, threadIdx.x, id, w);
+      }
+      return;
     }
-    if (threadIdx.x == 0) a.asum_part[(size_t)t * (F / 8) + (P >> 3)] = 0.f;
-    return;
+    const int id = topk_kth<NE>(a, t, s_logits, k);
+    blob = a.expert_base + (size_t)id * a.expert_stride;
+  } else {
+    blob = reinterpret_cast<const uint8_t*>(a.sel_addr[(size_t)t * a.K + k]);
+  }
+  if (blob == nullptr) {  // expert not resident: flag it and read the zero blob
+    if (threadIdx.x == 0) atomicOr(a.err, kErrMissingExpert);
+    blob = a.zero_blob;
   }
   gate_up_block<ACT, MAXI>(a, t, blob, a.ro, rb, a.fs + k * a.f, S);
 }
@@ -391,6 +577,8 @@ __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
 __host__ __device__ inline size_t down_lds_bytes(int F, int NI, int K, int act) {
   return (size_t)F * (act == 1 ? 2 : 4) + (size_t)NI * 4 + (size_t)K * 4 + 32 * 4;
 }
+
+constexpr int kAPre = 4;  // 16-byte activation words per thread loaded before the weights
 
 template <int ACT, int MAXI>
 __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
@@ -405,43 +593,45 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
   float* asum = reinterpret_cast<float*>(smem + (size_t)F * (ACT == 1 ? 2 : 4));
   float* wk = asum + NI;
   float* red = wk + K;
-  const int32_t* ids_t = a.ids + (size_t)t * K;
+  const uint64_t* sel_t = a.sel_addr + (size_t)t * K;
+  const char* abuf_t = abuf_of(a, t, ACT);
+  const int NW = F * (ACT == 1 ? 2 : 4) / 16;  // 16-byte words of the activation vector
+  v4u ar[kAPre];
+#pragma unroll
+  for (int i = 0; i < kAPre; ++i) ar[i] = ldg<v4u>(abuf_t + (size_t)min(tid + kThreads * i, NW - 1) * 16);
   float acc = 0.f;
-  for (int base = 0; base < NI; base += 16 * MAXI) {
-    uint4 q[MAXI][2];
+  for (int base = 0; base < NI; base += 32 * MAXI) {
+    v4u q0[MAXI], q1[MAXI];
     uint32_t sb[MAXI];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-      const int it = base + jj + 16 * i;
-      if (it < NI) {
-        const uint8_t* blob;
-        int G, g;
-        uint32_t oq, osb;
-        if (it < Gs) {
-          blob = a.shared_blob; G = Gs; g = it; oq = a.so.dq; osb = a.so.dsb;
-        } else {
-          const int k = (it - Gs) / Gf;
-          g = (it - Gs) - k * Gf;
-          G = Gf;
-          blob = reinterpret_cast<const uint8_t*>(a.expert_addr[ids_t[k]]);
-          oq = a.ro.dq; osb = a.ro.dsb;
-        }
-        if (blob != nullptr) {
-          const size_t off = (((size_t)rb * G + g) * 2) * 128 + r * 16;
-          q[i][0] = *reinterpret_cast<const uint4*>(blob + oq + off);
-          q[i][1] = *reinterpret_cast<const uint4*>(blob + oq + off + 128);
-          sb[i] = reinterpret_cast<const uint32_t*>(blob + osb)[(size_t)row * G + g];
-        } else {
-          q[i][0] = q[i][1] = make_uint4(0, 0, 0, 0);
-          sb[i] = 0;  // scale 0, bias 0
-        }
+      const int it = min(base + jj + 32 * i, NI - 1);
+      const uint8_t* blob;
+      int G, g;
+      uint32_t oq, osb;
+      if (it < Gs) {
+        blob = a.shared_blob; G = Gs; g = it; oq = a.so.dq; osb = a.so.dsb;
+      } else {
+        const int k = (it - Gs) / Gf;
+        g = (it - Gs) - k * Gf;
+        G = Gf;
+        blob = reinterpret_cast<const uint8_t*>(sel_t[k]);
+        if (blob == nullptr) blob = a.zero_blob;  // flagged by the gate/up kernel
+        oq = a.ro.dq; osb = a.ro.dsb;
       }
+      const size_t off = (((size_t)rb * G + g) * 2) * 128 + r * 16;
+      q0[i] = ldg<v4u>(blob + oq + off);
+      q1[i] = ldg<v4u>(blob + oq + off + 128);
+      sb[i] = ldg<uint32_t>(blob + osb + ((size_t)row * G + g) * 4);
     }
     if (base == 0) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.abuf) +
-                                                        (size_t)t * F * (ACT == 1 ? 2 : 4));
-      const int nw = F * (ACT == 1 ? 2 : 4) / 16;
-      for (int j = tid; j < nw; j += kThreads) reinterpret_cast<uint4*>(lds_a)[j] = src[j];
+#pragma unroll
+      for (int i = 0; i < kAPre; ++i) {
+        const int j = tid + kThreads * i;
+        if (j < NW) reinterpret_cast<v4u*>(lds_a)[j] = ar[i];
+      }
+      for (int j = tid + kThreads * kAPre; j < NW; j += kThreads)
+        reinterpret_cast<v4u*>(lds_a)[j] = ldg<v4u>(abuf_t + (size_t)j * 16);
       const float* part = a.asum_part + (size_t)t * (F / 8);
       for (int i = tid; i < NI; i += kThreads) {
         float s = 0.f;
@@ -454,22 +644,22 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-      const int it = base + jj + 16 * i;
+      const int it = base + jj + 32 * i;
       if (it < NI) {
         float p = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint32_t w4[4] = {q[i][h].x, q[i][h].y, q[i][h].z, q[i][h].w};
+          const v4u q = h ? q1[i] : q0[i];
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const uint32_t w = w4[m];
+            const uint32_t w = q[m];
             const int word = it * 8 + h * 4 + m;
             if (ACT == 1) {
-              const uint4 av = reinterpret_cast<const uint4*>(lds_a)[word];
-              p = dot2_f16(nib_pair<kMagicF16>(w, 0), av.x, p);
-              p = dot2_f16(nib_pair<kMagicF16>(w, 1), av.y, p);
-              p = dot2_f16(nib_pair<kMagicF16>(w, 2), av.z, p);
-              p = dot2_f16(nib_pair<kMagicF16>(w, 3), av.w, p);
+              const v4u av = reinterpret_cast<const v4u*>(lds_a)[word];
+              p = dot2_f16(nib_pair<kMagicF16>(w, 0), av[0], p);
+              p = dot2_f16(nib_pair<kMagicF16>(w, 1), av[1], p);
+              p = dot2_f16(nib_pair<kMagicF16>(w, 2), av[2], p);
+              p = dot2_f16(nib_pair<kMagicF16>(w, 3), av[3], p);
             } else {
               const float4 x0 = reinterpret_cast<const float4*>(lds_a)[word * 2];
               const float4 x1 = reinterpret_cast<const float4*>(lds_a)[word * 2 + 1];
@@ -485,10 +675,7 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
             }
           }
         }
-        const float s = f16_to_f32((uint16_t)(sb[i] & 0xFFFFu));
-        const float b = f16_to_f32((uint16_t)(sb[i] >> 16));
-        const float bb = (ACT == 1) ? b - 1024.f * s : b;
-        const float term = fmaf(s, p, bb * asum[it]);
+        const float term = group_term<ACT>(p, sb[i], asum[it], 1024.f);
         const float wgt = (it < Gs) ? 1.f : wk[(it - Gs) / Gf];
         acc = fmaf(wgt, term, acc);
       }
@@ -498,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
   if ((tid & 63) < 8) red[(tid >> 6) * 8 + r] = acc;
   __syncthreads();
   if (tid < 8) {
-    const float y = red[r] + red[8 + r];
+    const float y = (red[r] + red[8 + r]) + (red[16 + r] + red[24 + r]);
     const size_t o = (size_t)t * a.d + row;
     if (ACT == 1) {
       float v = y;
@@ -512,15 +699,21 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
   }
 }
 
-template <int ACT, int MAXI>
+template <int ACT, int MAXI, int NE>
 hipError_t launch_ab(const LayerArgs& a, int stages, hipStream_t s) {
   const size_t lds = x_stage_bytes(a.d);
   if (stages & (kStageRouter | kStageShared)) {
-    const int NR = (a.E + 7) / 8;
+    const int NR = (a.E + kWaves - 1) / kWaves;
     const int NS = (stages & kStageShared) ? a.fs / 8 : 0;
-    route_shared_kernel<ACT, MAXI><<<dim3(NR + NS, a.T), kThreads, lds, s>>>(a);
+    launch_timed(a.prof, kKRouteShared, route_shared_kernel<ACT, MAXI>, dim3(NR + NS, a.T), dim3(kThreads), lds, s,
+                 a);
+    if (!a.topk_in_gate_up) launch_timed(a.prof, kKTopK, topk_kernel<NE>, dim3(a.T), dim3(64), 0, s, a);
   }
-  if (stages & kStageRouted) routed_gu_kernel<ACT, MAXI><<<dim3(a.K * (a.f / 8), a.T), kThreads, lds, s>>>(a);
+  if (stages & kStageRouted) {
+    const int extra = a.topk_in_gate_up ? 1 : 0;  // the publishing workgroup
+    launch_timed(a.prof, kKRoutedGateUp, routed_gu_kernel<ACT, MAXI, NE>, dim3(a.K * (a.f / 8) + extra, a.T),
+                 dim3(kThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -529,27 +722,34 @@ hipError_t launch_c(const LayerArgs& a, hipStream_t s) {
   const int NI = a.fs / 64 + a.K * (a.f / 64);
   const int F = a.fs + a.K * a.f;
   const size_t lds = down_lds_bytes(F, NI, a.K, ACT);
-  if (NI <= 64)
-    down_combine_kernel<ACT, 4><<<dim3(a.d / 8, a.T), kThreads, lds, s>>>(a);
+  if (NI <= 128)
+    launch_timed(a.prof, kKDownCombine, down_combine_kernel<ACT, 4>, dim3(a.d / 8, a.T), dim3(kThreads), lds, s, a);
   else
-    down_combine_kernel<ACT, 8><<<dim3(a.d / 8, a.T), kThreads, lds, s>>>(a);
+    launch_timed(a.prof, kKDownCombine, down_combine_kernel<ACT, 8>, dim3(a.d / 8, a.T), dim3(kThreads), lds, s, a);
   return hipGetLastError();
+}
+
+template <int ACT, int NE>
+hipError_t launch_ab_ne(const LayerArgs& a, int stages, hipStream_t s) {
+  const int maxi = (a.d / 64 + 31) / 32;
+  if (maxi <= 1) return launch_ab<ACT, 1, NE>(a, stages, s);
+  if (maxi == 2) return launch_ab<ACT, 2, NE>(a, stages, s);
+  if (maxi == 3) return launch_ab<ACT, 3, NE>(a, stages, s);
+  return launch_ab<ACT, 4, NE>(a, stages, s);
 }
 
 template <int ACT>
 hipError_t launch_all(const LayerArgs& a, hipStream_t s) {
   const int stages = a.stages ? a.stages : kStageAll;
-  const int G = a.d / 64;
-  const int maxi = (G + 15) / 16;
   hipError_t e;
-  if (maxi <= 1)
-    e = launch_ab<ACT, 1>(a, stages, s);
-  else if (maxi == 2)
-    e = launch_ab<ACT, 2>(a, stages, s);
-  else if (maxi == 3)
-    e = launch_ab<ACT, 3>(a, stages, s);
+  if (a.E <= 64)
+    e = launch_ab_ne<ACT, 1>(a, stages, s);
+  else if (a.E <= 128)
+    e = launch_ab_ne<ACT, 2>(a, stages, s);
+  else if (a.E <= 256)
+    e = launch_ab_ne<ACT, 4>(a, stages, s);
   else
-    e = launch_ab<ACT, 4>(a, stages, s);
+    e = launch_ab_ne<ACT, 16>(a, stages, s);
   if (e != hipSuccess || !(stages & kStageDown)) return e;
   return launch_c<ACT>(a, s);
 }

@@ -1,12 +1,36 @@
 // Kernel-side argument blocks and launchers shared by the host library code.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 namespace moe {
 
-constexpr int kThreads = 128;  // every kernel: 2 wavefronts of 64
+constexpr int kThreads = 256;  // decode kernels: 4 wavefronts of 64
+
+// Optional host-side hook for live per-kernel timing: hands out a pair of HIP
+// events that the launch attaches to the kernel's own start and stop.
+struct Profiler {
+  virtual void pair(int kernel, hipEvent_t* start, hipEvent_t* stop) = 0;
+  virtual ~Profiler() = default;
+};
+
+// Launch `kernel`; with a profiler, through hipExtLaunchKernelGGL so the
+// events record the kernel's start and end on stream `s`.
+template <class Kern, class... Args>
+inline void launch_timed(Profiler* prof, int kid, Kern kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                         Args... args) {
+  if (prof) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    prof->pair(kid, &e0, &e1);
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, e0, e1, 0, args...);
+  } else {
+    kernel<<<grid, block, lds, s>>>(args...);
+  }
+}
+enum : int { kKRouteShared = 0, kKRoutedGateUp = 1, kKDownCombine = 2, kKSort = 3, kKPrefillGateUp = 4,
+             kKPrefillDown = 5, kKPrefillCombine = 6, kKPrefillRoute = 7, kKTopK = 8, kNumKernels = 9 };
 
 // Offsets of gate/up/down Q and SB regions inside an expert blob.
 struct BlobOffsets {
@@ -25,11 +49,15 @@ struct LayerArgs {
   const float* router_bias;  // nullable
   // experts
   const uint64_t* expert_addr;  // [E] device address of each expert blob (0 = absent)
+  const uint8_t* expert_base;   // resident layers: blob of expert e at expert_base + e * expert_stride
+  uint64_t expert_stride;
   const uint8_t* shared_blob;   // nullable when fs == 0
+  const uint8_t* zero_blob;     // one all-zero routed blob (read in place of a missing expert)
   BlobOffsets ro, so;           // routed / shared blob offsets
   // workspace
   float* logits;       // [T][E]
   int32_t* ids;        // [T][K]
+  uint64_t* sel_addr;  // [T][K] blob address of each chosen expert (written with the ids)
   float* wts;          // [T][K]
   uint32_t* counter;   // [T], zero between calls
   void* abuf;          // [T][F] F = fs + K*f: fp16 pair-permuted (bf16 mode) or fp32
@@ -44,6 +72,8 @@ struct LayerArgs {
   // which parts to run (0 = all): 1 router + top-K, 2 shared gate/up,
   // 4 routed gate/up, 8 down + combine
   int stages;
+  int topk_in_gate_up;  // 1: every routed gate/up workgroup runs the top-K itself
+  Profiler* prof;  // host pointer, never read by the kernels
 };
 
 enum : int { kStageRouter = 1, kStageShared = 2, kStageRouted = 4, kStageDown = 8, kStageAll = 15 };
