@@ -1,0 +1,169 @@
+"""Stack glue (residual + rmsnorm between layers), the streamed expert cache
+and the token->expert grouping, through the C ABI on the GPU."""
+import numpy as np
+import pytest
+
+import routed_expert_ffn_int8_amd as M
+from gen.workloads import WORKLOADS, Workload, make_layer, make_tokens, make_reuse_coins
+from oracle import oracle as O
+from oracle.lfu import LfuReplay
+from tests.helpers import GpuLayer, to_device, to_host, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_ulp(v):
+    a = np.abs(v.astype(np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0**-126)))
+    return 2.0 ** (e - 7)
+
+
+def _stack_layers(w, n, seed0=0):
+    arrays = [make_layer(w, layer=l, seed=seed0) for l in range(n)]
+    gls = [GpuLayer(w, a, 1) for a in arrays]
+    ols = [O.OracleLayer.from_workload(w, a) for a in arrays]
+    return arrays, gls, ols
+
+
+SMALL = Workload(85, "stack-small", d=512, E=64, K=8, f=128, fs=256, act="bf16", zipf=1.0, T=1,
+                 layers=4, steps=6, noise_sd=0.1)
+
+
+@pytest.mark.parametrize("w", [SMALL, Workload(86, "stack-d2816", d=2816, E=128, K=8, f=704, fs=2112,
+                                                act="bf16", zipf=1.0, T=1, layers=3, steps=2, noise_sd=0.1)],
+                         ids=["small", "decode-shape"])
+def test_stack_teacher_forced_and_composed(w):
+    torch = torch_mod()
+    arrays, gls, ols = _stack_layers(w, w.layers)
+    stack = M.moe_stack_create([g.handle for g in gls], 1e-6)
+    singles = [M.moe_stack_create([g.handle], 1e-6) for g in gls]
+    h0 = make_tokens(w, 1, stream=21)
+    # whole stack in one call
+    h = to_device(h0)
+    ids_all = torch.empty((w.layers, 1, w.K), dtype=torch.int32, device="cuda")
+    M.moe_stack_forward(h, stack, 1, ids_out=ids_all)
+    torch.cuda.synchronize()
+    h_stack = to_host(h)
+    # layer by layer, checking each layer against the oracle on the GPU's own input
+    hl = to_device(h0)
+    for l in range(w.layers):
+        h_in = to_host(hl)
+        M.moe_stack_forward(hl, singles[l], 1)
+        torch.cuda.synchronize()
+        h_out = to_host(hl)[0]
+        n = O.rmsnorm_bf16(h_in[0])
+        y_ref, ids_ref, _, margin = ols[l].forward(n[None, :])
+        ref = O.residual_bf16(h_in[0], y_ref[0])
+        got, want = O.tokens_to_f64(h_out), O.tokens_to_f64(ref)
+        ynorm = np.linalg.norm(y_ref[0])
+        slack = np.linalg.norm(_bf16_ulp(want))
+        assert np.linalg.norm(got - want) <= 5e-3 * ynorm + slack, f"layer {l}"
+    assert np.array_equal(h_stack, to_host(hl)), "a stack must equal its layers applied one by one"
+    for s in singles:
+        M.moe_stack_destroy(s)
+    M.moe_stack_destroy(stack)
+    for g in gls:
+        g.close()
+
+
+def test_stack_reuse_mask_reuses_previous_sets():
+    torch = torch_mod()
+    w = SMALL
+    arrays, gls, ols = _stack_layers(w, 2, seed0=3)
+    stack = M.moe_stack_create([g.handle for g in gls], 1e-6)
+    h = to_device(make_tokens(w, 1, stream=22))
+    ids1 = torch.empty((2, 1, w.K), dtype=torch.int32, device="cuda")
+    ids2 = torch.empty_like(ids1)
+    M.moe_stack_forward(h, stack, 1, ids_out=ids1)
+    M.moe_stack_forward(h, stack, 1, reuse_mask=[1, 0], ids_out=ids2)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids1.cpu().numpy()[0], ids2.cpu().numpy()[0])
+    M.moe_stack_destroy(stack)
+
+
+CACHE_W = Workload(87, "cache", d=512, E=64, K=8, f=128, fs=128, act="bf16", zipf=1.1, T=1,
+                   layers=1, steps=60, reuse_p=0.6, slots=16)
+
+
+@pytest.mark.parametrize("w", [CACHE_W, Workload(88, "cache-d2048-e256", d=2048, E=256, K=8, f=512, fs=512,
+                                                  act="bf16", zipf=1.1, T=1, layers=1, steps=40,
+                                                  reuse_p=0.6, slots=16)],
+                         ids=["small", "stream-shape"])
+def test_streamed_layer_bit_identical_and_counters_replay(w):
+    torch = torch_mod()
+    arrays = make_layer(w)
+    res = GpuLayer(w, arrays, 1)
+    st = GpuLayer(w, arrays, 1, residency=M.MOE_STREAMED)
+    M.moe_cache_attach(st.handle, w.slots)
+    _, stride = M.moe_layer_bytes(st.handle)
+    x = make_tokens(w, w.steps, stream=23)
+    coins = make_reuse_coins(w, w.steps)[:, 0]
+    replay = LfuReplay(w.slots)
+    for t in range(w.steps):
+        reuse = bool(coins[t])
+        y_r, ids_r, w_r = res.forward(x[t:t + 1], path=M.MOE_PATH_DECODE, reuse=reuse)
+        y_s, ids_s, w_s = st.forward(x[t:t + 1], path=M.MOE_PATH_DECODE, reuse=reuse)
+        assert np.array_equal(y_r, y_s), f"step {t}: streamed output differs from resident"
+        assert np.array_equal(ids_r, ids_s) and np.array_equal(w_r, w_s)
+        replay.step(ids_s[0].tolist())
+    stats = M.moe_cache_stats_get(st.handle)
+    assert (stats["accesses"], stats["hits"], stats["misses"], stats["evictions"]) == \
+        (replay.accesses, replay.hits, replay.misses, replay.evictions)
+    assert stats["h2d_bytes"] == replay.misses * stride
+    experts, counts = M.moe_cache_contents(st.handle, w.slots)
+    assert list(experts) == replay.expert and list(counts) == replay.count
+    assert M.moe_layer_check_errors(st.handle) == 0
+    res.close()
+    st.close()
+
+
+def test_streamed_fault_injection_leaves_state_unchanged():
+    w = CACHE_W
+    arrays = make_layer(w)
+    st = GpuLayer(w, arrays, 1, residency=M.MOE_STREAMED)
+    with pytest.raises(M.MoeError) as ei:
+        st.forward(make_tokens(w, 1, stream=24), path=M.MOE_PATH_DECODE)
+    assert ei.value.status == M.MOE_ERR_STATE  # no cache attached yet
+    M.moe_cache_attach(st.handle, w.slots)
+    x = make_tokens(w, 3, stream=25)
+    _, ids, _ = st.forward(x[:1], path=M.MOE_PATH_DECODE)
+    before = M.moe_cache_contents(st.handle, w.slots)
+    stats0 = M.moe_cache_stats_get(st.handle)
+    # make every expert that is not cached unreadable, then route a fresh token
+    cached = set(int(e) for e in before[0] if e >= 0)
+    for e in range(w.E):
+        if e not in cached:
+            M.moe_cache_fail_expert(st.handle, e, True)
+    with pytest.raises(M.MoeError) as ei:
+        st.forward(x[1:2], path=M.MOE_PATH_DECODE, forced=np.array([[e for e in range(w.E) if e not in cached][:w.K]]))
+    assert ei.value.status == M.MOE_ERR_IO
+    after = M.moe_cache_contents(st.handle, w.slots)
+    assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+    assert M.moe_cache_stats_get(st.handle)["misses"] == stats0["misses"]
+    for e in range(w.E):
+        M.moe_cache_fail_expert(st.handle, e, False)
+    st.forward(x[2:3], path=M.MOE_PATH_DECODE)  # recovers
+    st.close()
+
+
+@pytest.mark.parametrize("T", [0, 1, 37, 128, 512])
+def test_sort_bit_exact(T):
+    torch = torch_mod()
+    w = WORKLOADS[3]
+    wl = Workload(89, "sort", d=256, E=w.E, K=w.K, f=64, fs=64, act="bf16", zipf=1.0, T=max(T, 1))
+    gl = GpuLayer(wl, make_layer(wl), max(T, 1))
+    rng = np.random.default_rng(T)
+    ids = np.array([np.sort(rng.choice(wl.E, wl.K, replace=False)) for _ in range(T)], np.int32).reshape(T, wl.K)
+    di = torch.from_numpy(ids).cuda() if T else torch.zeros((1, wl.K), dtype=torch.int32, device="cuda")
+    counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(wl.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(max(T, 1) * wl.K, dtype=torch.int32, device="cuda")
+    inv = torch.empty_like(perm)
+    M.moe_layer_sort(di, gl.handle, T, counts, offsets, perm, inv)
+    torch.cuda.synchronize()
+    c, o, p, iv = O.sort(ids, wl.E)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(perm.cpu().numpy()[:T * wl.K], p)
+    assert np.array_equal(inv.cpu().numpy()[:T * wl.K], iv)
+    gl.close()
