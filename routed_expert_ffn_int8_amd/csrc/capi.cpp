@@ -426,11 +426,16 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
     }
   }
   int path = o ? o->path : MOE_PATH_AUTO;
-  if (path == MOE_PATH_AUTO) path = (L->act == MOE_ACT_BF16 && T >= 16 && L->d_prefill) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
+  if (path == MOE_PATH_AUTO)
+    path = (L->act == MOE_ACT_BF16 && T >= 16 && L->d_prefill && L->d <= 4096 && L->residency == MOE_RESIDENT && !a.rms)
+               ? MOE_PATH_PREFILL
+               : MOE_PATH_DECODE;
   if (path == MOE_PATH_PREFILL) {
     if (L->act != MOE_ACT_BF16 || !L->d_prefill)
       return fail(MOE_ERR_INVALID, "the prefill path needs bf16 activations and max_tokens > 1");
     if (L->residency == MOE_STREAMED) return fail(MOE_ERR_INVALID, "the prefill path needs resident experts");
+    if (L->d > 4096) return fail(MOE_ERR_INVALID, "the prefill path supports d_model <= 4096");
+    if (a.rms) return fail(MOE_ERR_INVALID, "the prefill path takes the layer input directly (no rmsnorm)");
     moe_status st = launch_prefill_path(L, a, o, s);
     if (st == MOE_OK) L->prev_T = T;
     return st;

@@ -92,7 +92,8 @@ struct PrefillArgs {
   void* xact;        // [T][d] bf16 layer input (after rmsnorm in stack mode)
   uint16_t* A;       // [T*K][f] bf16 routed activations, in perm order
   uint16_t* As;      // [T][fs] bf16 shared activations
-  float* Y;          // [T*K][d] fp32 routed outputs, in perm order
+  float* Y;          // [T*K][d] fp32 routed outputs, in grouped order
+  float* Ys;         // [T][d] fp32 shared-expert outputs
   int32_t* sort_offsets_out;
   int32_t* sort_perm_out;
 };

@@ -1,5 +1,22 @@
-// Prefill path (a chunk of many tokens): token->expert grouping and the
-// grouped expert GEMMs.
+// Prefill path: a chunk of many tokens per call.
+//
+// Rockchip-NPU MoE streaming plan, §2.5 and §8.4: prompts are processed in
+// 128-token chunks so that one fetched expert serves every row of the chunk
+// that chose it.  Per chunk:
+//   1. router GEMV + softmax top-K per token (the decode kernels, T rows);
+//   2. token->expert grouping: counting sort, stable in token order, plus a
+//      list of 16-token tiles per expert (and per shared-expert row block);
+//   3. grouped gate/up GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16): the
+//      tile's 16 token rows are staged in LDS, each wavefront owns 16 weight
+//      rows and streams their packed nibbles straight from HBM into the MFMA
+//      B operand (nibble pair -> bf16 128+q with one and-or), one fresh
+//      accumulator per 64-wide group so the group's (scale, bias) is applied
+//      in an fp32 epilogue; SiLU(gate)*up is stored as bf16;
+//   4. grouped down GEMM the same way, fp32 outputs in grouped order;
+//   5. gather-combine y_t = shared_t + sum_k w_{t,k} * Y[pos(t,k)] in fixed
+//      k order (no atomics), optional residual, bf16 store.
+// BigMoeOnEdge, "re-routing at every token and layer": every token of the
+// chunk is routed on its own, and the union of chosen experts can be large.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -7,13 +24,30 @@ namespace moe {
 
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <class T>
+__device__ __forceinline__ T ldg(const void* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) T*>(reinterpret_cast<uintptr_t>(p));
+}
+
+constexpr int kTile = 16;      // tokens per MFMA tile
+constexpr int kPWaves = 8;     // wavefronts per prefill GEMM workgroup
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kRowsPerWG = 16 * kPWaves;  // weight rows per workgroup
+
+// ------------------------------------------------------------ sort + tiles
 // Deterministic token->expert grouping by one workgroup of 1024 threads:
-// histogram (LDS integer atomics: the counts do not depend on their order),
+// histogram (LDS integer atomics; counts do not depend on their order),
 // exclusive scan, then one thread per expert walks the pairs in (token, slot)
-// order, so pairs of an expert appear in ascending token order.  Rockchip-NPU
-// plan §8.4: one fetched expert serves every row of the chunk that chose it.
+// order, so the pairs of an expert are in ascending token order.  With a tile
+// list it also emits (expert, tile) entries: ceil(n_e/16) per chosen expert,
+// then ceil(T/16) for the shared expert (expert id E).
 __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ ids, int T, int K, int E,
-                                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv) {
+                                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                                   int32_t* tiles, int with_shared) {
   extern __shared__ int32_t sh[];  // cnt[E], off[E+1]
   int32_t* cnt = sh;
   int32_t* off = sh + E;
@@ -26,12 +60,27 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
   }
   __syncthreads();
   if (tid == 0) {  // E <= 1024: a serial scan is cheaper than its barriers
-    int run = 0;
+    int run = 0, nt = 0;
     for (int e = 0; e < E; ++e) {
       off[e] = run;
       run += cnt[e];
+      if (tiles)
+        for (int tt = 0; tt * kTile < cnt[e]; ++tt) {
+          tiles[1 + 2 * nt] = e;
+          tiles[2 + 2 * nt] = tt;
+          ++nt;
+        }
     }
     off[E] = run;
+    if (tiles) {
+      if (with_shared)
+        for (int tt = 0; tt * kTile < T; ++tt) {
+          tiles[1 + 2 * nt] = E;
+          tiles[2 + 2 * nt] = tt;
+          ++nt;
+        }
+      tiles[0] = nt;
+    }
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
@@ -48,27 +97,369 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
   if (tid == 0) offsets[E] = off[E];
 }
 
+// ------------------------------------------------------------ tile staging
+struct TileInfo {
+  bool valid;
+  bool shared;
+  int e, tt, rows, base;  // rows of this expert (or T), first grouped row
+  int m_valid;             // valid token rows in this tile
+  const uint8_t* blob;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const PrefillArgs& p, int tile) {
+  TileInfo ti{};
+  const LayerArgs& a = p.L;
+  if (tile >= p.tiles[0]) return ti;
+  ti.valid = true;
+  ti.e = p.tiles[1 + 2 * tile];
+  ti.tt = p.tiles[2 + 2 * tile];
+  ti.shared = (ti.e == a.E);
+  ti.rows = ti.shared ? a.T : p.counts[ti.e];
+  ti.base = ti.shared ? 0 : p.offsets[ti.e];
+  ti.m_valid = min(kTile, ti.rows - ti.tt * kTile);
+  ti.blob = ti.shared ? a.shared_blob : a.expert_base + (size_t)ti.e * a.expert_stride;
+  return ti;
+}
+
+// Stage 16 rows of bf16 activations into LDS: pair-permuted words
+// (v[8j+m], v[8j+m+4]) per 16-byte word, rows padded by 16 bytes against bank
+// conflicts, and per-group sums gsum[g][m].  `src_row(m)` gives the source
+// row pointer (16-byte aligned, natural order when `permute`, already paired
+// otherwise) or nullptr for an empty row.
+template <bool PERMUTE, class RowFn>
+__device__ void stage_rows(int width, RowFn src_row, v4u* lds, float* gsum) {
+  const int W = width >> 3, stride = W + 1;  // words per row (+1 pad word)
+  const int G = width >> 6;
+  for (int idx = threadIdx.x; idx < kTile * W; idx += kPThreads) {
+    const int m = idx / W, j = idx - m * W;
+    const uint16_t* src = src_row(m);
+    v4u w = {0u, 0u, 0u, 0u};
+    if (src) w = ldg<v4u>(src + (size_t)j * 8);
+    float v[8];
+    if (PERMUTE) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+      v4u pw;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        pw[q] = (uint32_t)f32_to_bf16(v[q]) | ((uint32_t)f32_to_bf16(v[q + 4]) << 16);
+      lds[m * stride + j] = pw;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+      lds[m * stride + j] = w;
+    }
+    float part = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    part = xor_sum(part, 1, 4);  // 8 consecutive words (one group) sit in 8 consecutive lanes
+    if ((j & 7) == 0) gsum[(j >> 3) * kTile + m] = part;
+  }
+  (void)G;
+  __syncthreads();
+}
+
+__device__ __forceinline__ bf16x8 b_operand(uint32_t w) {
+  v4u v;
+  v[0] = nib_pair<kMagicBf16>(w, 0);
+  v[1] = nib_pair<kMagicBf16>(w, 1);
+  v[2] = nib_pair<kMagicBf16>(w, 2);
+  v[3] = nib_pair<kMagicBf16>(w, 3);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ void group_epilogue(f32x4& acc, const f32x4& t, uint32_t sb, const float* xs4) {
+  const float s = f16_to_f32((uint16_t)(sb & 0xFFFFu));
+  const float bb = f16_to_f32((uint16_t)(sb >> 16)) - 128.f * s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, t[i], fmaf(bb, xs4[i], acc[i]));
+}
+
+constexpr int kPre = 4;  // groups of weights in flight per lane
+
+// ------------------------------------------------------------ gate/up GEMM
+// One workgroup: one (expert, 16-token tile) x 128 rows of gate and up.
+// Lane (n = lane & 15, kb = lane >> 4) of wavefront w owns weight row
+// n0 + n; for MFMA j of a group it feeds word 4j + kb of the row (B operand)
+// and of the tile rows (A operand, from LDS), so both operands share one
+// order of the 64 k values.
+__global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
+  extern __shared__ __align__(16) char smem[];
+  const LayerArgs& a = p.L;
+  const int nch = (max(a.f, a.fs) + kRowsPerWG - 1) / kRowsPerWG;
+  const int tile = blockIdx.x / nch, ch = blockIdx.x - tile * nch;
+  const TileInfo ti = tile_info(p, tile);
+  if (!ti.valid) return;
+  const int fdim = ti.shared ? a.fs : a.f;
+  if (ch * kRowsPerWG >= fdim) return;
+  const int d = a.d, G = d >> 6, W = d >> 3;
+  v4u* xs_lds = reinterpret_cast<v4u*>(smem);
+  float* gsum = reinterpret_cast<float*>(smem + (size_t)kTile * (W + 1) * 16);
+  const BlobOffsets& o = ti.shared ? a.so : a.ro;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kb = lane >> 4;
+  const int n0 = ch * kRowsPerWG + wave * 16;
+  const bool wave_on = n0 < fdim;
+  const int row = min(n0, fdim - 16) + n;
+  const int rb = row >> 3, r = row & 7;
+  const uint8_t* gq = ti.blob + o.gq + (size_t)rb * G * 256 + r * 16 + kb * 4;
+  const uint8_t* uq = ti.blob + o.uq + (size_t)rb * G * 256 + r * 16 + kb * 4;
+  const uint32_t* gsb = reinterpret_cast<const uint32_t*>(ti.blob + o.gsb) + (size_t)row * G;
+  const uint32_t* usb = reinterpret_cast<const uint32_t*>(ti.blob + o.usb) + (size_t)row * G;
+  // weights of the first kPre groups go out before the activations are staged
+  uint32_t wg0[kPre], wg1[kPre], wu0[kPre], wu1[kPre], sg[kPre], su[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int g = min(i, G - 1);
+    wg0[i] = ldg<uint32_t>(gq + (size_t)g * 256);
+    wg1[i] = ldg<uint32_t>(gq + (size_t)g * 256 + 128);
+    wu0[i] = ldg<uint32_t>(uq + (size_t)g * 256);
+    wu1[i] = ldg<uint32_t>(uq + (size_t)g * 256 + 128);
+    sg[i] = ldg<uint32_t>(gsb + g);
+    su[i] = ldg<uint32_t>(usb + g);
+  }
+  const int K = a.K;
+  stage_rows<true>(d, [&](int m) -> const uint16_t* {
+    if (m >= ti.m_valid) return nullptr;
+    const int q = ti.tt * kTile + m;
+    const int tok = ti.shared ? q : p.perm[ti.base + q] / K;
+    return static_cast<const uint16_t*>(p.xact) + (size_t)tok * d;
+  }, xs_lds, gsum);
+  if (!wave_on) return;  // no barrier follows
+  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const v4u* arow = xs_lds + n * (W + 1);  // A operand: tile row m = lane & 15
+  for (int g0 = 0; g0 < G; g0 += kPre) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int g = g0 + i;
+      if (g < G) {
+        const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[g * 8 + kb]);
+        const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[g * 8 + 4 + kb]);
+        f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg0[i]), zero, 0, 0, 0);
+        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg1[i]), tg, 0, 0, 0);
+        f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu0[i]), zero, 0, 0, 0);
+        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu1[i]), tu, 0, 0, 0);
+        const float* xs4 = gsum + g * kTile + 4 * kb;
+        group_epilogue(accg, tg, sg[i], xs4);
+        group_epilogue(accu, tu, su[i], xs4);
+        // refill this slot with group g + kPre
+        const int gn = min(g + kPre, G - 1);
+        wg0[i] = ldg<uint32_t>(gq + (size_t)gn * 256);
+        wg1[i] = ldg<uint32_t>(gq + (size_t)gn * 256 + 128);
+        wu0[i] = ldg<uint32_t>(uq + (size_t)gn * 256);
+        wu1[i] = ldg<uint32_t>(uq + (size_t)gn * 256 + 128);
+        sg[i] = ldg<uint32_t>(gsb + gn);
+        su[i] = ldg<uint32_t>(usb + gn);
+      }
+    }
+  }
+  // D layout: lane holds column n (weight row) for tile rows 4*kb + i
+  uint16_t* dst = ti.shared ? p.As : p.A;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * kb + i;
+    if (m < ti.m_valid) {
+      const float v = silu(accg[i]) * accu[i];
+      const size_t grow = (size_t)(ti.base + ti.tt * kTile + m);
+      const int c = n0 + n, j = c >> 3, q = c & 7;
+      dst[grow * fdim + j * 8 + (q & 3) * 2 + (q >> 2)] = f32_to_bf16(v);
+    }
+  }
+}
+
+// ------------------------------------------------------------ down GEMM
+// One workgroup: one (expert, 16-token tile) x 128 rows of the down
+// projection; outputs fp32 rows in grouped order (shared: token order).
+__global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
+  extern __shared__ __align__(16) char smem[];
+  const LayerArgs& a = p.L;
+  const int nch = (a.d + kRowsPerWG - 1) / kRowsPerWG;
+  const int tile = blockIdx.x / nch, ch = blockIdx.x - tile * nch;
+  const TileInfo ti = tile_info(p, tile);
+  if (!ti.valid) return;
+  const int fdim = ti.shared ? a.fs : a.f;
+  const int G = fdim >> 6, W = fdim >> 3;
+  v4u* as_lds = reinterpret_cast<v4u*>(smem);
+  float* gsum = reinterpret_cast<float*>(smem + (size_t)kTile * (W + 1) * 16);
+  const BlobOffsets& o = ti.shared ? a.so : a.ro;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kb = lane >> 4;
+  const int n0 = ch * kRowsPerWG + wave * 16;
+  const bool wave_on = n0 < a.d;
+  const int row = min(n0, a.d - 16) + n;
+  const int rb = row >> 3, r = row & 7;
+  const uint8_t* dq = ti.blob + o.dq + (size_t)rb * G * 256 + r * 16 + kb * 4;
+  const uint32_t* dsb = reinterpret_cast<const uint32_t*>(ti.blob + o.dsb) + (size_t)row * G;
+  uint32_t w0[kPre], w1[kPre], sb[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int g = min(i, G - 1);
+    w0[i] = ldg<uint32_t>(dq + (size_t)g * 256);
+    w1[i] = ldg<uint32_t>(dq + (size_t)g * 256 + 128);
+    sb[i] = ldg<uint32_t>(dsb + g);
+  }
+  const uint16_t* src = ti.shared ? p.As : p.A;
+  stage_rows<false>(fdim, [&](int m) -> const uint16_t* {
+    if (m >= ti.m_valid) return nullptr;
+    return src + (size_t)(ti.base + ti.tt * kTile + m) * fdim;
+  }, as_lds, gsum);
+  if (!wave_on) return;  // no barrier follows
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const v4u* arow = as_lds + n * (W + 1);
+  for (int g0 = 0; g0 < G; g0 += kPre) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int g = g0 + i;
+      if (g < G) {
+        const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[g * 8 + kb]);
+        const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[g * 8 + 4 + kb]);
+        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w0[i]), zero, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w1[i]), t, 0, 0, 0);
+        group_epilogue(acc, t, sb[i], gsum + g * kTile + 4 * kb);
+        const int gn = min(g + kPre, G - 1);
+        w0[i] = ldg<uint32_t>(dq + (size_t)gn * 256);
+        w1[i] = ldg<uint32_t>(dq + (size_t)gn * 256 + 128);
+        sb[i] = ldg<uint32_t>(dsb + gn);
+      }
+    }
+  }
+  float* dst = ti.shared ? p.Ys : p.Y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * kb + i;
+    if (m < ti.m_valid) dst[(size_t)(ti.base + ti.tt * kTile + m) * a.d + n0 + n] = acc[i];
+  }
+}
+
+// ------------------------------------------------------------ combine
+// y_t = shared_t + sum_k w_{t,k} * Y[inv[t*K + k]] (k ascending), + residual.
+__global__ __launch_bounds__(256) void pf_combine_kernel(PrefillArgs p) {
+  const LayerArgs& a = p.L;
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.d) return;
+  float y = a.fs > 0 ? p.Ys[(size_t)t * a.d + c] : 0.f;
+  for (int k = 0; k < a.K; ++k) {
+    const int pos = p.inv[t * a.K + k];
+    y = fmaf(a.wts[t * a.K + k], p.Y[(size_t)pos * a.d + c], y);
+  }
+  const size_t o = (size_t)t * a.d + c;
+  if (a.resid) y += bf16_to_f32(static_cast<const uint16_t*>(a.resid)[o]);
+  static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(y);
+}
+
 }  // namespace
 
 hipError_t launch_sort(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                        int32_t* inv, hipStream_t s) {
   const size_t lds = (size_t)(2 * E + 1) * 4;
-  sort_kernel<<<1, 1024, lds, s>>>(ids, T, K, E, counts, offsets, perm, inv);
+  sort_kernel<<<1, 1024, lds, s>>>(ids, T, K, E, counts, offsets, perm, inv, nullptr, 0);
   return hipGetLastError();
 }
 
+constexpr int kChunkTokens = 128;  // prefill chunk (Rockchip-NPU plan §8.4)
+
+static size_t max_tiles(int T, int K, int E) { return (size_t)T * K / kTile + E + (T + kTile - 1) / kTile + 1; }
+
+static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
 size_t prefill_workspace_bytes(int T, int d, int E, int K, int f, int fs) {
-  (void)T; (void)d; (void)E; (void)K; (void)f; (void)fs;
-  return 256;
+  const int C = T < kChunkTokens ? T : kChunkTokens;
+  size_t b = 0;
+  b += align_up((size_t)E * 4) + align_up((size_t)(E + 1) * 4);  // counts, offsets
+  b += 2 * align_up((size_t)C * K * 4);                            // perm, inv
+  b += align_up((1 + 2 * max_tiles(C, K, E)) * 4);                 // tiles
+  b += align_up((size_t)C * K * f * 2) + align_up((size_t)C * (fs > 0 ? fs : 64) * 2);  // A, As
+  b += align_up((size_t)C * K * d * 4) + align_up((size_t)C * d * 4);                  // Y, Ys
+  return b;
 }
 
 void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, int fs) {
-  (void)p; (void)ws; (void)T; (void)d; (void)E; (void)K; (void)f; (void)fs;
+  const int C = T < kChunkTokens ? T : kChunkTokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* q = ws + off;
+    off += align_up(bytes);
+    return q;
+  };
+  p.counts = reinterpret_cast<int32_t*>(take((size_t)E * 4));
+  p.offsets = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  p.perm = reinterpret_cast<int32_t*>(take((size_t)C * K * 4));
+  p.inv = reinterpret_cast<int32_t*>(take((size_t)C * K * 4));
+  p.tiles = reinterpret_cast<int32_t*>(take((1 + 2 * max_tiles(C, K, E)) * 4));
+  p.A = reinterpret_cast<uint16_t*>(take((size_t)C * K * f * 2));
+  p.As = reinterpret_cast<uint16_t*>(take((size_t)C * (fs > 0 ? fs : 64) * 2));
+  p.Y = reinterpret_cast<float*>(take((size_t)C * K * d * 4));
+  p.Ys = reinterpret_cast<float*>(take((size_t)C * d * 4));
 }
 
-hipError_t launch_prefill(const PrefillArgs& p, hipStream_t s) {
-  (void)p; (void)s;
-  return hipErrorNotSupported;
+hipError_t launch_decode(const LayerArgs& a, hipStream_t s);
+
+size_t prefill_lds_gate_up(int d) { return (size_t)kTile * (d / 8 + 1) * 16 + (size_t)(d / 64) * kTile * 4; }
+
+// Whole prefill forward over T tokens, in chunks of 128 tokens.
+hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
+  const LayerArgs& a0 = p0.L;
+  static bool lds_raised = false;  // the gate/up tile needs more than 64 KB of LDS for d > 1984
+  if (!lds_raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(pf_gate_up_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(pf_down_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    lds_raised = true;
+  }
+  for (int c0 = 0; c0 < a0.T; c0 += kChunkTokens) {
+    PrefillArgs p = p0;
+    LayerArgs& a = p.L;
+    const int C = (a0.T - c0 < kChunkTokens) ? a0.T - c0 : kChunkTokens;
+    a.T = C;
+    const size_t xo = (size_t)c0 * a.d * 2;
+    a.x = static_cast<const char*>(a0.x) + xo;
+    a.out = static_cast<char*>(a0.out) + xo;
+    if (a0.resid) a.resid = static_cast<const char*>(a0.resid) + xo;
+    if (a0.forced) a.forced = a0.forced + (size_t)c0 * a.K;
+    if (a0.ids_out) a.ids_out = a0.ids_out + (size_t)c0 * a.K;
+    if (a0.w_out) a.w_out = a0.w_out + (size_t)c0 * a.K;
+    p.xact = const_cast<void*>(a.x);
+    // 1. router + top-K (decode kernels over the chunk's tokens)
+    LayerArgs r = a;
+    r.stages = kStageRouter;
+    r.topk_in_gate_up = 0;
+    hipError_t e = launch_decode(r, s);
+    if (e != hipSuccess) return e;
+    // 2. grouping + tiles
+    launch_timed(a.prof, kKSort, sort_kernel, dim3(1), dim3(1024), (size_t)(2 * a.E + 1) * 4, s, (const int32_t*)a.ids,
+                 C, a.K, a.E, p.counts, p.offsets, p.perm, p.inv, p.tiles, a.fs > 0 ? 1 : 0);
+    // 3. gate/up, 4. down, 5. combine
+    const size_t mt = max_tiles(C, a.K, a.E);
+    const int nch_gu = (((a.f > a.fs) ? a.f : a.fs) + kRowsPerWG - 1) / kRowsPerWG;
+    const size_t lds_gu = prefill_lds_gate_up(a.d);
+    launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel, dim3((unsigned)(mt * nch_gu)), dim3(kPThreads), lds_gu,
+                 s, p);
+    const int fmax = (a.f > a.fs) ? a.f : a.fs;
+    const int nch_dn = (a.d + kRowsPerWG - 1) / kRowsPerWG;
+    const size_t lds_dn = (size_t)kTile * (fmax / 8 + 1) * 16 + (size_t)(fmax / 64) * kTile * 4;
+    launch_timed(a.prof, kKPrefillDown, pf_down_kernel, dim3((unsigned)(mt * nch_dn)), dim3(kPThreads), lds_dn, s, p);
+    launch_timed(a.prof, kKPrefillCombine, pf_combine_kernel, dim3((a.d + 255) / 256, C), dim3(256), 0, s, p);
+    if (p0.sort_offsets_out)
+      if ((e = hipMemcpyAsync(p0.sort_offsets_out, p.offsets, (a.E + 1) * 4, hipMemcpyDeviceToDevice, s)) !=
+          hipSuccess)
+        return e;
+    if (p0.sort_perm_out)
+      if ((e = hipMemcpyAsync(p0.sort_perm_out + (size_t)c0 * a.K, p.perm, (size_t)C * a.K * 4,
+                              hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace moe
