@@ -1,13 +1,26 @@
-"""Benchmark of the routed-expert MoE FFN layer on one MI355X.
+"""Benchmarks of the routed-expert MoE FFN layer on one MI355X.
 
-Default workload: one decode MoE layer at batch 1 (d_model 2816, 128 routed
-experts, top-8, expert d_ff 704, shared d_ff 2112, int4 group-64 experts,
-int8 router with a Zipf logit bias), one token per call, tokens iid N(0, 1)
-in bf16, already resident in HBM.  A step is one batch-1 forward of the whole
-layer (router GEMV, softmax top-K, shared + routed gate/up SiLU, down +
-weighted combine).  Prints one JSON line.
+Default (--workload decode): one decode MoE layer at batch 1 (d_model 2816,
+128 routed experts, top-8, expert d_ff 704, shared d_ff 2112, int4 group-64
+experts, int8 router with a Zipf logit bias), one token per call, tokens iid
+N(0, 1) in bf16, already resident in HBM.  A step is one batch-1 forward of
+the whole layer (router GEMV, softmax top-K, shared + routed gate/up SiLU,
+down + weighted combine).  The timed steps are replayed from HIP graphs; the
+per-kernel durations come from extended-launch HIP events in a second pass
+over the same tokens.  Prints one JSON line, which also carries a short
+prefill summary (128-token chunk of the d_model 2048 / 256-expert layer).
 
-  python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--no-cpu]
+Other workloads (one JSON line each):
+  --workload prefill : 128-token chunks, d_model 2048, 256 experts, top-8,
+                       d_ff 512, shared 512 (also 512 / 2048 tokens as chunks)
+  --workload stack   : 30 decode layers of the default shape, 256 steps,
+                       h <- h + MoE(rmsnorm(h)), next input = output + N(0, 0.1)
+  --workload stream  : 40 layers of the prefill shape, routed experts in
+                       pinned host memory behind a 16-slot LFU cache per layer,
+                       Zipf s = 1.1 and 60% reuse of the previous step's experts,
+                       256 steps, next to the same stack with all experts in HBM
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--workload ...]
 """
 from __future__ import annotations
 
@@ -23,12 +36,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "device.hpp", "kernels.hpp", "layout.hpp"):
+    for name in ("decode.hip", "prefill.hip", "device.hpp", "kernels.hpp", "layout.hpp"):
         with open(os.path.join(ROOT, "routed_expert_ffn_int8_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -53,7 +67,7 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(w, arrays, n_tokens: int):
+def cpu_baseline(w, arrays, n_tokens: int, tokens_per_call: int = 1):
     """The fp64 oracle, timed on this host's cores over a bounded sample."""
     from gen.workloads import make_tokens
     from oracle import oracle as O
@@ -61,12 +75,325 @@ def cpu_baseline(w, arrays, n_tokens: int):
     x = make_tokens(w, n_tokens, stream=4242)
     OL.forward(x[:1])  # warm (page in, thread pool)
     t0 = time.perf_counter()
-    for t in range(n_tokens):
-        OL.forward(x[t:t + 1])
+    for t in range(0, n_tokens, tokens_per_call):
+        OL.forward(x[t:t + tokens_per_call])
     dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tok/s", "cores": O.threads(), "kind": "oracle",
-            "sample": f"{n_tokens} batch-1 tokens of the same layer (fp64 plain loops, "
-                      f"OpenMP over output rows), {dt:.1f} s"}
+    return {"value": round(n_tokens / dt, 3), "unit": "tok/s", "cores": O.threads(), "kind": "oracle",
+            "sample": f"{n_tokens} tokens of the same layer in calls of {tokens_per_call} "
+                      f"(fp64 plain loops, OpenMP over output rows), {dt:.1f} s"}
+
+
+def kernel_table(prof: dict, alg: dict, flops: dict | None = None) -> dict:
+    out = {}
+    for k, (launches, ms) in prof.items():
+        avg_us = ms * 1e3 / launches
+        e = {"launches": launches, "avg_us": round(avg_us, 3)}
+        if k in alg:
+            e["alg_bytes"] = int(alg[k])
+            e["gbps"] = round(alg[k] / (avg_us * 1e3), 1)
+        if flops and k in flops:
+            e["tflops"] = round(flops[k] / (avg_us * 1e6), 2)
+        out[k] = e
+    return out
+
+
+def gated_profile(M, torch, layer, calls, stream, chunk):
+    """Per-kernel durations (extended-launch HIP events) over `calls`, each
+    chunk enqueued behind a short bounded spin on the stream."""
+    M.moe_layer_profile(layer, True)
+    gpu_ms = 0.0
+    for c0 in range(0, len(calls), chunk):
+        torch.cuda._sleep(20_000_000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for fn in calls[c0:c0 + chunk]:
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gpu_ms += e0.elapsed_time(e1)
+    prof = M.moe_layer_profile_read(layer)
+    M.moe_layer_profile(layer, False)
+    return prof, gpu_ms
+
+
+def graph_time(torch, calls, chunk):
+    """Capture `calls` into graphs of `chunk` calls, replay once to upload,
+    then time one replay of every graph.  Returns seconds."""
+    cap = torch.cuda.Stream()
+    graphs = []
+    for c0 in range(0, len(calls), chunk):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for fn in calls[c0:c0 + chunk]:
+                fn(cap)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+# --------------------------------------------------------------------- decode
+def run_decode(args, M, torch, np):
+    from gen.workloads import WORKLOADS, make_layer, make_tokens, matrix_bytes, router_bytes
+    w = WORKLOADS[1]
+    arrays = make_layer(w)
+    desc, keep = M.make_desc(arrays, w.d, w.E, w.K, w.f, w.fs, M.MOE_ACT_BF16, 1)
+    layer = M.moe_layer_create(desc)
+    del keep
+    n = args.steps + args.warmup
+    x = torch.from_numpy(make_tokens(w, n, stream=1).view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+    for i in range(args.warmup):
+        M.moe_layer_forward(x[i], layer, out[i], 1, stream)
+    torch.cuda.synchronize()
+    timed = range(args.warmup, n)
+    if args.mode == "graph":
+        dt = graph_time(torch, [lambda s, i=i: M.moe_layer_forward(x[i], layer, out[i], 1, s) for i in timed],
+                        args.chunk)
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in timed:
+            M.moe_layer_forward(x[i], layer, out[i], 1, stream)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+    prof, gated_ms = gated_profile(M, torch, layer,
+                                   [lambda i=i: M.moe_layer_forward(x[i], layer, out[i], 1, stream) for i in timed],
+                                   stream, args.chunk)
+    tok_s = args.steps / dt
+    gu, dn = matrix_bytes(w.f, w.d), matrix_bytes(w.d, w.f)
+    sgu, sdn = matrix_bytes(w.fs, w.d), matrix_bytes(w.d, w.fs)
+    act = 2 * w.d
+    alg = {"route_shared": router_bytes(w) + 2 * sgu + act,
+           "routed_gate_up": w.K * 2 * gu + act,
+           "down_combine": w.K * dn + sdn + act}
+    kernels = kernel_table(prof, alg)
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    achieved = kernels[dom]["gbps"]
+    bytes_token = w.K * (2 * gu + dn) + 2 * sgu + sdn + router_bytes(w)
+    result = {
+        "metric": "MoE FFN tok/s (decode b=1, one layer, int4 g64 experts, int8 router)",
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode-layer-d2816-e128-k8-f704-fs2112-b1", "tokens_per_call": 1,
+                   "d_model": w.d, "experts": w.E, "top_k": w.K, "d_ff": w.f, "d_ff_shared": w.fs,
+                   "weights": "int4 affine g64, int8 router"},
+        "mode": args.mode,
+        "direct_launch_gpu_tok_s": round(args.steps / (gated_ms / 1e3), 1),
+        "layer_hbm_gbps": round(bytes_token * tok_s / 1e9, 1),
+        "layer_hbm_frac": round(bytes_token * tok_s / 1e9 / PEAK_HBM_GBPS, 4),
+        "bytes_per_token": bytes_token,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": read_traffic(dom, "decode_layer"),
+                     "kernel": dom},
+        "kernels": kernels,
+    }
+    M.moe_layer_destroy(layer)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_tokens)
+    return result
+
+
+# --------------------------------------------------------------------- prefill
+def run_prefill(args, M, torch, np, chunks=None, summary=False):
+    from gen.workloads import WORKLOADS, make_layer, make_tokens, matrix_bytes, router_bytes
+    w = WORKLOADS[3]
+    arrays = make_layer(w)
+    desc, keep = M.make_desc(arrays, w.d, w.E, w.K, w.f, w.fs, M.MOE_ACT_BF16, 2048)
+    layer = M.moe_layer_create(desc)
+    del keep
+    C = 128
+    nch = chunks or (8 if summary else 40)
+    x = torch.from_numpy(make_tokens(w, C * nch, stream=3).view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.empty_like(x)
+    ids = torch.empty((C * nch, w.K), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i, s):
+        o = M.fwd_opts(topk_ids=ids[i * C:(i + 1) * C], path=M.MOE_PATH_PREFILL)
+        M.moe_layer_forward_ex(x[i * C:(i + 1) * C], layer, out[i * C:(i + 1) * C], C, o, s)
+
+    for i in range(min(nch, 3)):
+        call(i, stream)
+    torch.cuda.synchronize()
+    dt = graph_time(torch, [lambda s, i=i: call(i, s) for i in range(nch)], 10)
+    prof, _ = gated_profile(M, torch, layer, [lambda i=i: call(i, stream) for i in range(nch)], stream, 10)
+    ids_h = ids.cpu().numpy()
+    distinct = float(np.mean([len(np.unique(ids_h[i * C:(i + 1) * C])) for i in range(nch)]))
+    eb = 2 * matrix_bytes(w.f, w.d) + matrix_bytes(w.d, w.f)
+    gu_b, dn_b = 2 * matrix_bytes(w.f, w.d), matrix_bytes(w.d, w.f)
+    sgu, sdn = 2 * matrix_bytes(w.fs, w.d), matrix_bytes(w.d, w.fs)
+    chunk_bytes = distinct * eb + sgu + sdn + router_bytes(w)
+    flop_routed = C * w.K * (2 * 2 * w.d * w.f + 2 * w.f * w.d)
+    flop_shared = C * (2 * 2 * w.d * w.fs + 2 * w.fs * w.d)
+    flop_router = C * 2 * w.d * w.E
+    flops = flop_routed + flop_shared + flop_router
+    alg = {"prefill_gate_up": distinct * gu_b + sgu + C * w.d * 2,
+           "prefill_down": distinct * dn_b + sdn,
+           "route_shared": router_bytes(w) + C * w.d * 2}
+    kflops = {"prefill_gate_up": C * w.K * 2 * 2 * w.d * w.f + C * 2 * 2 * w.d * w.fs,
+              "prefill_down": C * w.K * 2 * w.f * w.d + C * 2 * w.fs * w.d}
+    kernels = kernel_table(prof, alg, kflops)
+    chunk_s = dt / nch
+    dom = max(("prefill_gate_up", "prefill_down"), key=lambda k: kernels[k]["avg_us"])
+    res = {
+        "metric": "MoE FFN prefill tok/s (128-token chunks, one layer) and MFMA utilisation",
+        "value": round(C / chunk_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1, "steps": nch, "warmup": 3, "ms_per_step": round(chunk_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill-chunk128-d2048-e256-k8-f512-fs512", "tokens_per_call": C},
+        "chunk_gflop": round(flops / 1e9, 3),
+        "mfma_util": round(flops / chunk_s / 1e12 / PEAK_BF16_TFLOPS, 5),
+        "tflops": round(flops / chunk_s / 1e12, 2),
+        "distinct_experts_per_chunk": round(distinct, 1),
+        "hbm_gbps_distinct_expert_bytes": round(chunk_bytes / chunk_s / 1e9, 1),
+        "hbm_frac": round(chunk_bytes / chunk_s / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(kernels[dom]["gbps"] / PEAK_HBM_GBPS, 4),
+                     "traffic": read_traffic(dom, "prefill_chunk"), "kernel": dom},
+        "kernels": kernels,
+    }
+    if not summary:
+        for T in (512, 2048):  # longer prompts as sequential 128-token chunks inside one call
+            if T > C * nch:
+                continue
+            xt = x[:T]
+            ot = torch.empty_like(xt)
+            M.moe_layer_forward_ex(xt, layer, ot, T, M.fwd_opts(path=M.MOE_PATH_PREFILL), stream)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(3):
+                M.moe_layer_forward_ex(xt, layer, ot, T, M.fwd_opts(path=M.MOE_PATH_PREFILL), stream)
+            torch.cuda.synchronize()
+            res[f"tok_s_T{T}"] = round(3 * T / (time.perf_counter() - t0), 1)
+        if not args.no_cpu:
+            res["cpu_baseline"] = cpu_baseline(w, arrays, 32, tokens_per_call=32)
+    M.moe_layer_destroy(layer)
+    return res
+
+
+# --------------------------------------------------------------------- stack
+def run_stack(args, M, torch, np):
+    from gen.workloads import WORKLOADS, make_layer, make_tokens, make_noise, matrix_bytes, router_bytes
+    w = WORKLOADS[2]
+    layers = []
+    for l in range(w.layers):
+        arrays = make_layer(w, layer=l)
+        desc, keep = M.make_desc(arrays, w.d, w.E, w.K, w.f, w.fs, M.MOE_ACT_BF16, 1)
+        layers.append(M.moe_layer_create(desc))
+        del keep, arrays
+        print(f"[bench] stack layer {l + 1}/{w.layers} created", file=sys.stderr, flush=True)
+    stack = M.moe_stack_create(layers, 1e-6)
+    steps = w.steps
+    noise = torch.from_numpy(make_noise(w, steps)).cuda()
+    h0 = torch.from_numpy(make_tokens(w, 1, stream=5).view(np.int16)).view(torch.bfloat16).cuda()
+    h = h0.clone()
+    stream = torch.cuda.current_stream()
+
+    def step(t, s):
+        M.moe_stack_forward(h, stack, 1, stream=s)
+        with torch.cuda.stream(s):
+            h.copy_((h.float() + noise[t]).to(torch.bfloat16))
+
+    for t in range(4):
+        step(t, stream)
+    torch.cuda.synchronize()
+    h.copy_(h0)
+    dt = graph_time(torch, [lambda s, t=t: step(t, s) for t in range(steps)], 32)
+    finite = bool(torch.isfinite(h.float()).all())
+    per_layer = w.K * (2 * matrix_bytes(w.f, w.d) + matrix_bytes(w.d, w.f)) + \
+        2 * matrix_bytes(w.fs, w.d) + matrix_bytes(w.d, w.fs) + router_bytes(w)
+    bytes_step = per_layer * w.layers
+    res = {
+        "metric": "MoE FFN stack tok/s (decode b=1, 30 layers, h <- h + MoE(rmsnorm(h)))",
+        "value": round(steps / dt, 1), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": 4,
+        "ms_per_step": round(dt * 1e3 / steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode-stack30-d2816-e128-k8-f704-fs2112-b1", "layers": w.layers},
+        "stack_hbm_gbps": round(bytes_step * steps / dt / 1e9, 1),
+        "stack_hbm_frac": round(bytes_step * steps / dt / 1e9 / PEAK_HBM_GBPS, 4),
+        "bytes_per_token": bytes_step, "finite": finite,
+    }
+    M.moe_stack_destroy(stack)
+    for L in layers:
+        M.moe_layer_destroy(L)
+    return res
+
+
+# --------------------------------------------------------------------- stream
+def run_stream(args, M, torch, np):
+    from gen.workloads import WORKLOADS, make_layer, make_tokens, make_noise, make_reuse_coins
+    w = WORKLOADS[4]
+    res_layers, st_layers = [], []
+    for l in range(w.layers):
+        arrays = make_layer(w, layer=l)
+        d1, k1 = M.make_desc(arrays, w.d, w.E, w.K, w.f, w.fs, M.MOE_ACT_BF16, 1)
+        res_layers.append(M.moe_layer_create(d1))
+        d2, k2 = M.make_desc(arrays, w.d, w.E, w.K, w.f, w.fs, M.MOE_ACT_BF16, 1, M.MOE_STREAMED)
+        L = M.moe_layer_create(d2)
+        M.moe_cache_attach(L, w.slots)
+        st_layers.append(L)
+        del k1, k2, arrays
+        print(f"[bench] stream layer {l + 1}/{w.layers} created", file=sys.stderr, flush=True)
+    steps = w.steps
+    coins = make_reuse_coins(w, steps).astype(np.uint8)
+    noise = torch.from_numpy(make_noise(w, steps)).cuda()
+    h0 = torch.from_numpy(make_tokens(w, 1, stream=6).view(np.int16)).view(torch.bfloat16).cuda()
+    out = {}
+    finals = {}
+    for name, layers in (("resident", res_layers), ("streamed", st_layers)):
+        stack = M.moe_stack_create(layers, 1e-6)
+        h = h0.clone()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(steps):
+            M.moe_stack_forward(h, stack, 1, reuse_mask=coins[t])
+            h.copy_((h.float() + noise[t]).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        out[name] = steps / (time.perf_counter() - t0)
+        print(f"[bench] {name}: {out[name]:.1f} tok/s", file=sys.stderr, flush=True)
+        finals[name] = h.clone()
+        M.moe_stack_destroy(stack)
+    stats = [M.moe_cache_stats_get(L) for L in st_layers]
+    tot = {k: sum(s[k] for s in stats) for k in stats[0]}
+    res = {
+        "metric": "MoE FFN expert-streaming stack tok/s (decode b=1, 40 layers, 16-slot LFU per layer)",
+        "value": round(out["streamed"], 2), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": 0,
+        "ms_per_step": round(1e3 / out["streamed"], 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "stream-stack40-d2048-e256-k8-f512-lfu16-zipf1.1-reuse0.6"},
+        "all_resident_tok_s": round(out["resident"], 1),
+        "hit_rate": round(tot["hits"] / max(1, tot["accesses"]), 4),
+        "h2d_bytes_per_token": tot["h2d_bytes"] / steps,
+        "h2d_gbps_during_fills": round(tot["h2d_bytes"] / max(1, tot["h2d_ns"]), 2),
+        "misses_per_token": tot["misses"] / steps,
+        "streamed_equals_resident": bool(torch.equal(finals["resident"], finals["streamed"])),
+    }
+    for L in res_layers + st_layers:
+        M.moe_layer_destroy(L)
+    return res
 
 
 def main():
@@ -74,12 +401,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", choices=("decode", "prefill", "stack", "stream"), default="decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="decode only, without the prefill summary")
     ap.add_argument("--cpu-tokens", type=int, default=48)
     ap.add_argument("--mode", choices=("graph", "direct"), default="graph",
-                    help="graph: the timed tokens are replayed from HIP graphs captured in chunks "
-                         "(no host launch cost); direct: one library call per token")
-    ap.add_argument("--chunk", type=int, default=100, help="tokens per captured graph")
+                    help="graph: timed decode tokens replayed from HIP graphs; direct: one call per token")
+    ap.add_argument("--chunk", type=int, default=100, help="decode tokens per captured graph")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device copy first (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -92,128 +420,22 @@ def main():
     import numpy as np
     import torch
     import routed_expert_ffn_int8_amd as M
-    from gen.workloads import WORKLOADS, make_layer, make_tokens, matrix_bytes, router_bytes
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    w = WORKLOADS[1]
-    arrays = make_layer(w)
-    desc, keep = M.make_desc(arrays, w.d, w.E, w.K, w.f, w.fs, M.MOE_ACT_BF16, 1)
-    layer = M.moe_layer_create(desc)
-    del keep
-
-    n = args.steps + args.warmup
-    x_host = make_tokens(w, n, stream=1)
-    x = torch.from_numpy(x_host.view(np.int16)).view(torch.bfloat16).cuda()
-    out = torch.empty_like(x)
-    stream = torch.cuda.current_stream()
-    if args.calib_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    for i in range(args.warmup):
-        M.moe_layer_forward(x[i], layer, out[i], 1, stream)
-    torch.cuda.synchronize()
-
-    graphs = []
-    if args.mode == "graph":
-        # the timed tokens (each a full batch-1 forward with its own input and
-        # output row) are captured into HIP graphs and replayed
-        cap = torch.cuda.Stream()
-        for c0 in range(args.warmup, n, args.chunk):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                for i in range(c0, min(n, c0 + args.chunk)):
-                    M.moe_layer_forward(x[i], layer, out[i], 1, cap)
-            graphs.append(g)
-        torch.cuda.synchronize()
-        for g in graphs:  # first replays upload the graphs
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for g in graphs:
-            g.replay()
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
+    if args.workload == "decode":
+        result = run_decode(args, M, torch, np)
+        if not args.no_extra:
+            p = run_prefill(args, M, torch, np, summary=True)
+            result["prefill_128"] = {k: p[k] for k in ("value", "unit", "ms_per_step", "mfma_util", "tflops",
+                                                       "hbm_gbps_distinct_expert_bytes", "hbm_frac",
+                                                       "distinct_experts_per_chunk")}
+    elif args.workload == "prefill":
+        result = run_prefill(args, M, torch, np)
+    elif args.workload == "stack":
+        result = run_stack(args, M, torch, np)
     else:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.warmup, n):
-            M.moe_layer_forward(x[i], layer, out[i], 1, stream)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-
-    # Per-kernel durations: HIP events around every kernel on the launch
-    # stream, over the same tokens launched directly.  Each chunk waits behind
-    # a short bounded spin on that stream so the host has enqueued the whole
-    # chunk before its first kernel starts: the events then time kernels that
-    # run back to back, not host launch latency.
-    M.moe_layer_profile(layer, True)
-    gated_ms = 0.0
-    for c0 in range(args.warmup, n, args.chunk):
-        torch.cuda._sleep(20_000_000)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(c0, min(n, c0 + args.chunk)):
-            M.moe_layer_forward(x[i], layer, out[i], 1, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        gated_ms += e0.elapsed_time(e1)
-    prof = M.moe_layer_profile_read(layer)
-    M.moe_layer_profile(layer, False)
-
-    tok_s = args.steps / dt
-    ms_step = dt * 1e3 / args.steps
-    gu, dn = matrix_bytes(w.f, w.d), matrix_bytes(w.d, w.f)
-    sgu, sdn = matrix_bytes(w.fs, w.d), matrix_bytes(w.d, w.fs)
-    act = 2 * w.d
-    alg = {  # algorithmic HBM bytes per launch (weights streamed + token in/out)
-        "route_shared": router_bytes(w) + 2 * sgu + act,
-        "routed_gate_up": w.K * 2 * gu + act,
-        "down_combine": w.K * dn + sdn + act,
-    }
-    kernels = {}
-    for k, (launches, ms) in prof.items():
-        avg_us = ms * 1e3 / launches
-        kernels[k] = {"launches": launches, "avg_us": round(avg_us, 3),
-                      "alg_bytes": alg.get(k), "gbps": round(alg[k] / (avg_us * 1e3), 1) if k in alg else None}
-    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
-    achieved = kernels[dom]["gbps"]
-    workload = "decode_layer"
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": read_traffic(dom, workload),
-                "kernel": dom}
-    bytes_token = w.K * (2 * gu + dn) + 2 * sgu + sdn + router_bytes(w)
-    result = {
-        "metric": "MoE FFN tok/s (decode b=1, one layer, int4 g64 experts, int8 router)",
-        "value": round(tok_s, 1),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "decode-layer-d2816-e128-k8-f704-fs2112-b1",
-                   "tokens_per_call": 1, "d_model": w.d, "experts": w.E, "top_k": w.K,
-                   "d_ff": w.f, "d_ff_shared": w.fs, "weights": "int4 affine g64, int8 router"},
-        "mode": args.mode,
-        "direct_launch_gpu_tok_s": round(args.steps / (gated_ms / 1e3), 1),
-        "layer_hbm_gbps": round(bytes_token * tok_s / 1e9, 1),
-        "bytes_per_token": bytes_token,
-        "roofline": roofline,
-        "kernels": kernels,
-    }
-    M.moe_layer_destroy(layer)
-    if rank == 0 and not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_tokens)
+        result = run_stream(args, M, torch, np)
     if rank == 0:
         print(json.dumps(result), flush=True)
 

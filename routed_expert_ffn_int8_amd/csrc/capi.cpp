@@ -533,6 +533,8 @@ moe_status moe_layer_sort(const int32_t* ids, moe_layer* L, int32_t n_tokens, in
   if (!counts || !offsets || (n_tokens > 0 && (!ids || !perm || !inv)))
     return fail(MOE_ERR_INVALID, "a sort buffer is NULL");
   HIP_OK(hipSetDevice(L->dev));
+  if (((size_t)L->E + 1 + (size_t)L->E * ((n_tokens + 31) / 32)) * 4 > 144 * 1024)
+    return fail(MOE_ERR_INVALID, "grouping %d tokens over %d experts needs more than 144 KB of LDS", n_tokens, L->E);
   HIP_OK(launch_sort(ids, n_tokens, L->K, L->E, counts, offsets, perm, inv, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }

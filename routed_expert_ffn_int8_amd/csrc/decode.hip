@@ -234,8 +234,8 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
   const int row = rb * 8 + r;
   const uint8_t* gq = blob + o.gq;
   const uint8_t* uq = blob + o.uq;
-  const uint8_t* gsb = blob + o.gsb + (size_t)row * G * 4;
-  const uint8_t* usb = blob + o.usb + (size_t)row * G * 4;
+  const uint8_t* gsb = blob + o.gsb + ((size_t)rb * G * 8 + r) * 4;  // + g * 32
+  const uint8_t* usb = blob + o.usb + ((size_t)rb * G * 8 + r) * 4;
   XRegs xr;
   x_issue<ACT>(a, t, xr);
   float accg = 0.f, accu = 0.f;
@@ -250,8 +250,8 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
       qg1[i] = ldg<v4u>(gq + off + 128);
       qu0[i] = ldg<v4u>(uq + off);
       qu1[i] = ldg<v4u>(uq + off + 128);
-      sg[i] = ldg<uint32_t>(gsb + g * 4);
-      su[i] = ldg<uint32_t>(usb + g * 4);
+      sg[i] = ldg<uint32_t>(gsb + g * 32);
+      su[i] = ldg<uint32_t>(usb + g * 32);
     }
     if (base == 0) x_commit<ACT>(a, t, xr, S);
 #pragma unroll
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
       const size_t off = (((size_t)rb * G + g) * 2) * 128 + r * 16;
       q0[i] = ldg<v4u>(blob + oq + off);
       q1[i] = ldg<v4u>(blob + oq + off + 128);
-      sb[i] = ldg<uint32_t>(blob + osb + ((size_t)row * G + g) * 4);
+      sb[i] = ldg<uint32_t>(blob + osb + (((size_t)rb * G + g) * 8 + r) * 4);
     }
     if (base == 0) {
 #pragma unroll

@@ -17,7 +17,12 @@ void pack_matrix(const MatLayout& m, const uint32_t* q, const uint16_t* s, const
           std::memcpy(dst, src, 16);
         }
   uint32_t* SB = reinterpret_cast<uint32_t*>(blob + m.sb_off);
-  for (size_t i = 0; i < (size_t)R * G; ++i) SB[i] = (uint32_t)s[i] | ((uint32_t)b[i] << 16);
+  for (int rb = 0; rb < R / kRowBlock; ++rb)
+    for (int g = 0; g < G; ++g)
+      for (int r = 0; r < kRowBlock; ++r) {
+        const size_t src = (size_t)(rb * kRowBlock + r) * G + g;
+        SB[((size_t)rb * G + g) * kRowBlock + r] = (uint32_t)s[src] | ((uint32_t)b[src] << 16);
+      }
 }
 
 }  // namespace moe

@@ -12,9 +12,9 @@
 //   Q  region: [R/8 row blocks][G groups][2 halves][8 rows][16 bytes]
 //              (16 bytes = the 4 packed words of 32 consecutive columns of
 //              one row, unchanged nibble order), 256 bytes per (block, group)
-//   SB region: [R][G] uint32 = fp16 scale | fp16 bias << 16
+//   SB region: [R/8 row blocks][G groups][8 rows] uint32 = fp16 scale | fp16 bias << 16
 // so a wavefront that reads 8 rows x 16 bytes touches one 128-byte line, and
-// the 64-lane B operand of a 32x32x16 MFMA (32 rows x 2 halves) is 8 lines.
+// the scale/bias words of 8 rows of one group are 32 contiguous bytes.
 #pragma once
 #include <cstddef>
 #include <cstdint>

@@ -39,39 +39,53 @@ constexpr int kPThreads = 64 * kPWaves;
 constexpr int kRowsPerWG = 16 * kPWaves;  // weight rows per workgroup
 
 // ------------------------------------------------------------ sort + tiles
-// Deterministic token->expert grouping by one workgroup of 1024 threads:
-// histogram (LDS integer atomics; counts do not depend on their order),
-// exclusive scan, then one thread per expert walks the pairs in (token, slot)
-// order, so the pairs of an expert are in ascending token order.  With a tile
-// list it also emits (expert, tile) entries: ceil(n_e/16) per chosen expert,
-// then ceil(T/16) for the shared expert (expert id E).
+// Deterministic token->expert grouping by one workgroup of 1024 threads.
+// Each expert gets a bitmask over the chunk's tokens (set with LDS atomic-or,
+// whose result does not depend on order); its count is the mask's popcount,
+// offsets are the exclusive scan, and a pair (t, k) choosing expert e lands at
+// offsets[e] + popcount of e's mask below bit t, i.e. the pairs of an expert
+// are in ascending token order.  With a tile list it also emits (expert, tile)
+// entries: ceil(n_e/16) per chosen expert, then ceil(T/16) for the shared
+// expert (expert id E).  Needs E * ceil(T/32) words of LDS; repeated ids in
+// one token's set are counted once.
 __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ ids, int T, int K, int E,
                                                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                                                    int32_t* tiles, int with_shared) {
-  extern __shared__ int32_t sh[];  // cnt[E], off[E+1]
-  int32_t* cnt = sh;
-  int32_t* off = sh + E;
+  extern __shared__ uint32_t sh[];  // off[E+1], mask[E][NW]
+  const int NW = (T + 31) >> 5;
+  int32_t* off = reinterpret_cast<int32_t*>(sh);
+  uint32_t* mask = sh + E + 1;
   const int tid = threadIdx.x, n = T * K;
-  for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+  for (int i = tid; i < E * NW; i += blockDim.x) mask[i] = 0u;
   __syncthreads();
   for (int i = tid; i < n; i += blockDim.x) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    const int e = ids[i], t = i / K;
+    if (e >= 0 && e < E) atomicOr(&mask[e * NW + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int c = 0;
+    for (int w = 0; w < NW; ++w) c += __popc(mask[e * NW + w]);
+    off[e] = c;  // count for now, turned into the offset below
   }
   __syncthreads();
   if (tid == 0) {  // E <= 1024: a serial scan is cheaper than its barriers
     int run = 0, nt = 0;
     for (int e = 0; e < E; ++e) {
+      const int c = off[e];
+      counts[e] = c;
       off[e] = run;
-      run += cnt[e];
+      offsets[e] = run;
+      run += c;
       if (tiles)
-        for (int tt = 0; tt * kTile < cnt[e]; ++tt) {
+        for (int tt = 0; tt * kTile < c; ++tt) {
           tiles[1 + 2 * nt] = e;
           tiles[2 + 2 * nt] = tt;
           ++nt;
         }
     }
     off[E] = run;
+    offsets[E] = run;
     if (tiles) {
       if (with_shared)
         for (int tt = 0; tt * kTile < T; ++tt) {
@@ -83,18 +97,16 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    counts[e] = cnt[e];
-    offsets[e] = off[e];
-    int pos = off[e];
-    for (int i = 0; i < n; ++i)
-      if (ids[i] == e) {
-        perm[pos] = i;
-        inv[i] = pos;
-        ++pos;
-      }
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int e = ids[i], t = i / K;
+    if (e < 0 || e >= E) continue;
+    const uint32_t* m = mask + e * NW;
+    int rank = __popc(m[t >> 5] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(m[w]);
+    const int pos = off[e] + rank;
+    perm[pos] = i;
+    inv[i] = pos;
   }
-  if (tid == 0) offsets[E] = off[E];
 }
 
 // ------------------------------------------------------------ tile staging
@@ -123,43 +135,50 @@ __device__ __forceinline__ TileInfo tile_info(const PrefillArgs& p, int tile) {
 
 // Stage 16 rows of bf16 activations into LDS: pair-permuted words
 // (v[8j+m], v[8j+m+4]) per 16-byte word, rows padded by 16 bytes against bank
-// conflicts, and per-group sums gsum[g][m].  `src_row(m)` gives the source
-// row pointer (16-byte aligned, natural order when `permute`, already paired
-// otherwise) or nullptr for an empty row.
-template <bool PERMUTE, class RowFn>
-__device__ void stage_rows(int width, RowFn src_row, v4u* lds, float* gsum) {
+// conflicts, and per-group sums gsum[g][m].  rows[m] is the source row (or
+// nullptr for an empty row), natural order when PERMUTE, already paired
+// otherwise.  Every thread issues all of its loads before touching LDS.
+// STG = 16-byte words per thread (16 rows x width columns / 512 threads).
+template <bool PERMUTE, int STG>
+__device__ void stage_rows(int width, const uint16_t* const* rows, v4u* lds, float* gsum) {
   const int W = width >> 3, stride = W + 1;  // words per row (+1 pad word)
-  const int G = width >> 6;
-  for (int idx = threadIdx.x; idx < kTile * W; idx += kPThreads) {
+  const int total = kTile * W;
+  v4u buf[STG];
+  const uint16_t* any_row = rows[0] ? rows[0] : rows[kTile - 1];  // a valid row (row 0 is never empty)
+#pragma unroll
+  for (int it = 0; it < STG; ++it) {  // branch-free so every load is in flight at once
+    const int idx = min((int)threadIdx.x + kPThreads * it, total - 1);
     const int m = idx / W, j = idx - m * W;
-    const uint16_t* src = src_row(m);
-    v4u w = {0u, 0u, 0u, 0u};
-    if (src) w = ldg<v4u>(src + (size_t)j * 8);
-    float v[8];
-    if (PERMUTE) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = __uint_as_float(w[q] << 16);
-        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-      }
-      v4u pw;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        pw[q] = (uint32_t)f32_to_bf16(v[q]) | ((uint32_t)f32_to_bf16(v[q + 4]) << 16);
-      lds[m * stride + j] = pw;
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = __uint_as_float(w[q] << 16);
-        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-      }
-      lds[m * stride + j] = w;
-    }
-    float part = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-    part = xor_sum(part, 1, 4);  // 8 consecutive words (one group) sit in 8 consecutive lanes
-    if ((j & 7) == 0) gsum[(j >> 3) * kTile + m] = part;
+    const uint16_t* src = rows[m] ? rows[m] : any_row;
+    const v4u w = ldg<v4u>(src + (size_t)j * 8);
+    buf[it] = rows[m] ? w : v4u{0u, 0u, 0u, 0u};
   }
-  (void)G;
+#pragma unroll
+  for (int it = 0; it < STG; ++it) {
+    const int idx = threadIdx.x + kPThreads * it;
+    if (idx < total) {  // uniform across each aligned group of 8 lanes
+      const int m = idx / W, j = idx - m * W;
+      const v4u w = buf[it];
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+      if (PERMUTE) {
+        v4u pw;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pw[q] = (uint32_t)f32_to_bf16(v[q]) | ((uint32_t)f32_to_bf16(v[q + 4]) << 16);
+        lds[m * stride + j] = pw;
+      } else {
+        lds[m * stride + j] = w;
+      }
+      float part = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+      part = xor_sum(part, 1, 4);  // the 8 words of one group sit in 8 consecutive lanes
+      if ((j & 7) == 0) gsum[(j >> 3) * kTile + m] = part;
+    }
+  }
   __syncthreads();
 }
 
@@ -172,14 +191,14 @@ __device__ __forceinline__ bf16x8 b_operand(uint32_t w) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ void group_epilogue(f32x4& acc, const f32x4& t, uint32_t sb, const float* xs4) {
-  const float s = f16_to_f32((uint16_t)(sb & 0xFFFFu));
-  const float bb = f16_to_f32((uint16_t)(sb >> 16)) - 128.f * s;
+__device__ __forceinline__ void group_epilogue(f32x4& acc, const f32x4& t, uint32_t sb, const float* xs4, float on) {
+  const float s = on * f16_to_f32((uint16_t)(sb & 0xFFFFu));
+  const float bb = on * f16_to_f32((uint16_t)(sb >> 16)) - 128.f * s;
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, t[i], fmaf(bb, xs4[i], acc[i]));
 }
 
-constexpr int kPre = 4;  // groups of weights in flight per lane
+constexpr int kPre = 6;  // groups of weights in flight per lane
 
 // ------------------------------------------------------------ gate/up GEMM
 // One workgroup: one (expert, 16-token tile) x 128 rows of gate and up.
@@ -187,6 +206,7 @@ constexpr int kPre = 4;  // groups of weights in flight per lane
 // n0 + n; for MFMA j of a group it feeds word 4j + kb of the row (B operand)
 // and of the tile rows (A operand, from LDS), so both operands share one
 // order of the 64 k values.
+template <int STG>
 __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
   extern __shared__ __align__(16) char smem[];
   const LayerArgs& a = p.L;
@@ -208,8 +228,8 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
   const int rb = row >> 3, r = row & 7;
   const uint8_t* gq = ti.blob + o.gq + (size_t)rb * G * 256 + r * 16 + kb * 4;
   const uint8_t* uq = ti.blob + o.uq + (size_t)rb * G * 256 + r * 16 + kb * 4;
-  const uint32_t* gsb = reinterpret_cast<const uint32_t*>(ti.blob + o.gsb) + (size_t)row * G;
-  const uint32_t* usb = reinterpret_cast<const uint32_t*>(ti.blob + o.usb) + (size_t)row * G;
+  const uint32_t* gsb = reinterpret_cast<const uint32_t*>(ti.blob + o.gsb) + (size_t)rb * G * 8 + r;  // + g * 8
+  const uint32_t* usb = reinterpret_cast<const uint32_t*>(ti.blob + o.usb) + (size_t)rb * G * 8 + r;
   // weights of the first kPre groups go out before the activations are staged
   uint32_t wg0[kPre], wg1[kPre], wu0[kPre], wu1[kPre], sg[kPre], su[kPre];
 #pragma unroll
@@ -219,43 +239,46 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
     wg1[i] = ldg<uint32_t>(gq + (size_t)g * 256 + 128);
     wu0[i] = ldg<uint32_t>(uq + (size_t)g * 256);
     wu1[i] = ldg<uint32_t>(uq + (size_t)g * 256 + 128);
-    sg[i] = ldg<uint32_t>(gsb + g);
-    su[i] = ldg<uint32_t>(usb + g);
+    sg[i] = ldg<uint32_t>(gsb + g * 8);
+    su[i] = ldg<uint32_t>(usb + g * 8);
   }
-  const int K = a.K;
-  stage_rows<true>(d, [&](int m) -> const uint16_t* {
-    if (m >= ti.m_valid) return nullptr;
-    const int q = ti.tt * kTile + m;
-    const int tok = ti.shared ? q : p.perm[ti.base + q] / K;
-    return static_cast<const uint16_t*>(p.xact) + (size_t)tok * d;
-  }, xs_lds, gsum);
+  __shared__ const uint16_t* rows[kTile];
+  if (threadIdx.x < kTile) {
+    const int m = threadIdx.x, q = ti.tt * kTile + m;
+    const int tok = (m >= ti.m_valid) ? -1 : (ti.shared ? q : p.perm[ti.base + q] / a.K);
+    rows[m] = tok < 0 ? nullptr : static_cast<const uint16_t*>(p.xact) + (size_t)tok * d;
+  }
+  __syncthreads();
+  stage_rows<true, STG>(d, rows, xs_lds, gsum);
   if (!wave_on) return;  // no barrier follows
   f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const v4u* arow = xs_lds + n * (W + 1);  // A operand: tile row m = lane & 15
+  // Branch-free body (clamped group index, zero factor past the end) so the
+  // compiler can keep kPre groups of loads in flight across iterations.
   for (int g0 = 0; g0 < G; g0 += kPre) {
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
       const int g = g0 + i;
-      if (g < G) {
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[g * 8 + kb]);
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[g * 8 + 4 + kb]);
-        f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg0[i]), zero, 0, 0, 0);
-        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg1[i]), tg, 0, 0, 0);
-        f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu0[i]), zero, 0, 0, 0);
-        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu1[i]), tu, 0, 0, 0);
-        const float* xs4 = gsum + g * kTile + 4 * kb;
-        group_epilogue(accg, tg, sg[i], xs4);
-        group_epilogue(accu, tu, su[i], xs4);
-        // refill this slot with group g + kPre
-        const int gn = min(g + kPre, G - 1);
-        wg0[i] = ldg<uint32_t>(gq + (size_t)gn * 256);
-        wg1[i] = ldg<uint32_t>(gq + (size_t)gn * 256 + 128);
-        wu0[i] = ldg<uint32_t>(uq + (size_t)gn * 256);
-        wu1[i] = ldg<uint32_t>(uq + (size_t)gn * 256 + 128);
-        sg[i] = ldg<uint32_t>(gsb + gn);
-        su[i] = ldg<uint32_t>(usb + gn);
-      }
+      const int gc = min(g, G - 1);
+      const float on = g < G ? 1.f : 0.f;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + kb]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 4 + kb]);
+      f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg0[i]), zero, 0, 0, 0);
+      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg1[i]), tg, 0, 0, 0);
+      f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu0[i]), zero, 0, 0, 0);
+      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu1[i]), tu, 0, 0, 0);
+      const float* xs4 = gsum + gc * kTile + 4 * kb;
+      group_epilogue(accg, tg, sg[i], xs4, on);
+      group_epilogue(accu, tu, su[i], xs4, on);
+      // refill this slot with group g + kPre
+      const int gn = min(g + kPre, G - 1);
+      wg0[i] = ldg<uint32_t>(gq + (size_t)gn * 256);
+      wg1[i] = ldg<uint32_t>(gq + (size_t)gn * 256 + 128);
+      wu0[i] = ldg<uint32_t>(uq + (size_t)gn * 256);
+      wu1[i] = ldg<uint32_t>(uq + (size_t)gn * 256 + 128);
+      sg[i] = ldg<uint32_t>(gsb + gn * 8);
+      su[i] = ldg<uint32_t>(usb + gn * 8);
     }
   }
   // D layout: lane holds column n (weight row) for tile rows 4*kb + i
@@ -275,6 +298,7 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
 // ------------------------------------------------------------ down GEMM
 // One workgroup: one (expert, 16-token tile) x 128 rows of the down
 // projection; outputs fp32 rows in grouped order (shared: token order).
+template <int STG>
 __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   extern __shared__ __align__(16) char smem[];
   const LayerArgs& a = p.L;
@@ -294,20 +318,23 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   const int row = min(n0, a.d - 16) + n;
   const int rb = row >> 3, r = row & 7;
   const uint8_t* dq = ti.blob + o.dq + (size_t)rb * G * 256 + r * 16 + kb * 4;
-  const uint32_t* dsb = reinterpret_cast<const uint32_t*>(ti.blob + o.dsb) + (size_t)row * G;
+  const uint32_t* dsb = reinterpret_cast<const uint32_t*>(ti.blob + o.dsb) + (size_t)rb * G * 8 + r;  // + g * 8
   uint32_t w0[kPre], w1[kPre], sb[kPre];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) {
     const int g = min(i, G - 1);
     w0[i] = ldg<uint32_t>(dq + (size_t)g * 256);
     w1[i] = ldg<uint32_t>(dq + (size_t)g * 256 + 128);
-    sb[i] = ldg<uint32_t>(dsb + g);
+    sb[i] = ldg<uint32_t>(dsb + g * 8);
   }
-  const uint16_t* src = ti.shared ? p.As : p.A;
-  stage_rows<false>(fdim, [&](int m) -> const uint16_t* {
-    if (m >= ti.m_valid) return nullptr;
-    return src + (size_t)(ti.base + ti.tt * kTile + m) * fdim;
-  }, as_lds, gsum);
+  __shared__ const uint16_t* rows[kTile];
+  if (threadIdx.x < kTile) {
+    const int m = threadIdx.x;
+    const uint16_t* src = ti.shared ? p.As : p.A;
+    rows[m] = (m >= ti.m_valid) ? nullptr : src + (size_t)(ti.base + ti.tt * kTile + m) * fdim;
+  }
+  __syncthreads();
+  stage_rows<false, STG>(fdim, rows, as_lds, gsum);
   if (!wave_on) return;  // no barrier follows
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -316,17 +343,17 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
       const int g = g0 + i;
-      if (g < G) {
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[g * 8 + kb]);
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[g * 8 + 4 + kb]);
-        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w0[i]), zero, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w1[i]), t, 0, 0, 0);
-        group_epilogue(acc, t, sb[i], gsum + g * kTile + 4 * kb);
-        const int gn = min(g + kPre, G - 1);
-        w0[i] = ldg<uint32_t>(dq + (size_t)gn * 256);
-        w1[i] = ldg<uint32_t>(dq + (size_t)gn * 256 + 128);
-        sb[i] = ldg<uint32_t>(dsb + gn);
-      }
+      const int gc = min(g, G - 1);
+      const float on = g < G ? 1.f : 0.f;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + kb]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 4 + kb]);
+      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w0[i]), zero, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w1[i]), t, 0, 0, 0);
+      group_epilogue(acc, t, sb[i], gsum + gc * kTile + 4 * kb, on);
+      const int gn = min(g + kPre, G - 1);
+      w0[i] = ldg<uint32_t>(dq + (size_t)gn * 256);
+      w1[i] = ldg<uint32_t>(dq + (size_t)gn * 256 + 128);
+      sb[i] = ldg<uint32_t>(dsb + gn * 8);
     }
   }
   float* dst = ti.shared ? p.Ys : p.Y;
@@ -356,9 +383,21 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillArgs p) {
 
 }  // namespace
 
+// Dynamic LDS granted to the prefill kernels (below the 160 KB per workgroup
+// so their few static LDS words still fit).
+constexpr int kMaxDynLds = 144 * 1024;
+
+size_t sort_lds_bytes(int T, int E) { return ((size_t)E + 1 + (size_t)E * ((T + 31) / 32)) * 4; }
+
 hipError_t launch_sort(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                        int32_t* inv, hipStream_t s) {
-  const size_t lds = (size_t)(2 * E + 1) * 4;
+  const size_t lds = sort_lds_bytes(T, E);
+  if (lds > kMaxDynLds) return hipErrorInvalidValue;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sort_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
+    if (e != hipSuccess) return e;
+  }
   sort_kernel<<<1, 1024, lds, s>>>(ids, T, K, E, counts, offsets, perm, inv, nullptr, 0);
   return hipGetLastError();
 }
@@ -401,6 +440,14 @@ void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, 
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s);
 
+// Staging words per thread for 16 rows of `width` bf16 values, rounded up to a power of two.
+static int stage_words(int width) {
+  const int need = (kTile * (width / 8) + kPThreads - 1) / kPThreads;
+  int s = 1;
+  while (s < need) s <<= 1;
+  return s;
+}
+
 size_t prefill_lds_gate_up(int d) { return (size_t)kTile * (d / 8 + 1) * 16 + (size_t)(d / 64) * kTile * 4; }
 
 // Whole prefill forward over T tokens, in chunks of 128 tokens.
@@ -408,12 +455,20 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
   const LayerArgs& a0 = p0.L;
   static bool lds_raised = false;  // the gate/up tile needs more than 64 KB of LDS for d > 1984
   if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(pf_gate_up_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(pf_down_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
+    const void* fns[] = {reinterpret_cast<const void*>(pf_gate_up_kernel<1>),
+                         reinterpret_cast<const void*>(pf_gate_up_kernel<2>),
+                         reinterpret_cast<const void*>(pf_gate_up_kernel<4>),
+                         reinterpret_cast<const void*>(pf_gate_up_kernel<8>),
+                         reinterpret_cast<const void*>(pf_gate_up_kernel<16>),
+                         reinterpret_cast<const void*>(pf_down_kernel<1>),
+                         reinterpret_cast<const void*>(pf_down_kernel<2>),
+                         reinterpret_cast<const void*>(pf_down_kernel<4>),
+                         reinterpret_cast<const void*>(pf_down_kernel<8>),
+                         reinterpret_cast<const void*>(pf_down_kernel<16>)};
+    for (const void* f : fns) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
+      if (e != hipSuccess) return e;
+    }
     lds_raised = true;
   }
   for (int c0 = 0; c0 < a0.T; c0 += kChunkTokens) {
@@ -436,18 +491,31 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
     hipError_t e = launch_decode(r, s);
     if (e != hipSuccess) return e;
     // 2. grouping + tiles
-    launch_timed(a.prof, kKSort, sort_kernel, dim3(1), dim3(1024), (size_t)(2 * a.E + 1) * 4, s, (const int32_t*)a.ids,
+    launch_timed(a.prof, kKSort, sort_kernel, dim3(1), dim3(1024), sort_lds_bytes(C, a.E), s, (const int32_t*)a.ids,
                  C, a.K, a.E, p.counts, p.offsets, p.perm, p.inv, p.tiles, a.fs > 0 ? 1 : 0);
     // 3. gate/up, 4. down, 5. combine
     const size_t mt = max_tiles(C, a.K, a.E);
     const int nch_gu = (((a.f > a.fs) ? a.f : a.fs) + kRowsPerWG - 1) / kRowsPerWG;
     const size_t lds_gu = prefill_lds_gate_up(a.d);
-    launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel, dim3((unsigned)(mt * nch_gu)), dim3(kPThreads), lds_gu,
-                 s, p);
+    const dim3 g_gu((unsigned)(mt * nch_gu)), blk(kPThreads);
+    switch (stage_words(a.d)) {
+      case 1: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<1>, g_gu, blk, lds_gu, s, p); break;
+      case 2: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<2>, g_gu, blk, lds_gu, s, p); break;
+      case 4: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<4>, g_gu, blk, lds_gu, s, p); break;
+      case 8: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<8>, g_gu, blk, lds_gu, s, p); break;
+      default: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<16>, g_gu, blk, lds_gu, s, p); break;
+    }
     const int fmax = (a.f > a.fs) ? a.f : a.fs;
     const int nch_dn = (a.d + kRowsPerWG - 1) / kRowsPerWG;
     const size_t lds_dn = (size_t)kTile * (fmax / 8 + 1) * 16 + (size_t)(fmax / 64) * kTile * 4;
-    launch_timed(a.prof, kKPrefillDown, pf_down_kernel, dim3((unsigned)(mt * nch_dn)), dim3(kPThreads), lds_dn, s, p);
+    const dim3 g_dn((unsigned)(mt * nch_dn));
+    switch (stage_words(fmax)) {
+      case 1: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<1>, g_dn, blk, lds_dn, s, p); break;
+      case 2: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<2>, g_dn, blk, lds_dn, s, p); break;
+      case 4: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<4>, g_dn, blk, lds_dn, s, p); break;
+      case 8: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<8>, g_dn, blk, lds_dn, s, p); break;
+      default: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<16>, g_dn, blk, lds_dn, s, p); break;
+    }
     launch_timed(a.prof, kKPrefillCombine, pf_combine_kernel, dim3((a.d + 255) / 256, C), dim3(256), 0, s, p);
     if (p0.sort_offsets_out)
       if ((e = hipMemcpyAsync(p0.sort_offsets_out, p.offsets, (a.E + 1) * 4, hipMemcpyDeviceToDevice, s)) !=
