@@ -155,30 +155,43 @@ def run_decode(args, M, torch, np):
         torch.empty_like(src).copy_(src)
         torch.cuda.synchronize()
         del src
-    for i in range(args.warmup):
-        M.moe_layer_forward(x[i], layer, out[i], 1, stream)
-    torch.cuda.synchronize()
     timed = range(args.warmup, n)
-    if args.mode == "graph":
-        dt = graph_time(torch, [lambda s, i=i: M.moe_layer_forward(x[i], layer, out[i], 1, s) for i in timed],
-                        args.chunk)
-    else:
+
+    def fwd(path):
+        def call(i, s):
+            M.moe_layer_forward_ex(x[i], layer, out[i], 1, M.fwd_opts(path=path), s)
+        return call
+
+    def measure(path):
+        call = fwd(path)
+        for i in range(args.warmup):
+            call(i, stream)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in timed:
-            M.moe_layer_forward(x[i], layer, out[i], 1, stream)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-    prof, gated_ms = gated_profile(M, torch, layer,
-                                   [lambda i=i: M.moe_layer_forward(x[i], layer, out[i], 1, stream) for i in timed],
-                                   stream, args.chunk)
-    tok_s = args.steps / dt
+        if args.mode == "graph":
+            dt = graph_time(torch, [lambda s, i=i: call(i, s) for i in timed], args.chunk)
+        else:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in timed:
+                call(i, stream)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+        prof, gated_ms = gated_profile(M, torch, layer, [lambda i=i: call(i, stream) for i in timed], stream,
+                                       args.chunk)
+        return dt, prof, gated_ms
+
     gu, dn = matrix_bytes(w.f, w.d), matrix_bytes(w.d, w.f)
     sgu, sdn = matrix_bytes(w.fs, w.d), matrix_bytes(w.d, w.fs)
     act = 2 * w.d
     alg = {"route_shared": router_bytes(w) + 2 * sgu + act,
            "routed_gate_up": w.K * 2 * gu + act,
-           "down_combine": w.K * dn + sdn + act}
+           "down_combine": w.K * dn + sdn + act,
+           "fused_layer": router_bytes(w) + 2 * sgu + sdn + w.K * (2 * gu + dn) + 2 * act}
+    # the split (three-kernel) path first, for context; then the production path
+    dt3, prof3, _ = measure(M.MOE_PATH_DECODE)
+    path = M.MOE_PATH_FUSED if args.decode_path == "fused" else M.MOE_PATH_DECODE
+    dt, prof, gated_ms = measure(path)
+    tok_s = args.steps / dt
     kernels = kernel_table(prof, alg)
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     achieved = kernels[dom]["gbps"]
@@ -207,7 +220,9 @@ def run_decode(args, M, torch, np):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": read_traffic(dom, "decode_layer"),
                      "kernel": dom},
+        "decode_path": args.decode_path,
         "kernels": kernels,
+        "three_kernel_path": {"tok_s": round(args.steps / dt3, 1), "kernels": kernel_table(prof3, alg)},
     }
     M.moe_layer_destroy(layer)
     if not args.no_cpu:
@@ -405,6 +420,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="decode only, without the prefill summary")
     ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--decode-path", choices=("fused", "split"), default="fused",
+                    help="fused: one kernel per layer and token; split: router+shared | routed gate/up | down")
     ap.add_argument("--mode", choices=("graph", "direct"), default="graph",
                     help="graph: timed decode tokens replayed from HIP graphs; direct: one call per token")
     ap.add_argument("--chunk", type=int, default=100, help="decode tokens per captured graph")

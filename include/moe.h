@@ -46,7 +46,16 @@ typedef enum {
 
 enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 };        /* activation dtype of x / out */
 enum { MOE_RESIDENT = 0, MOE_STREAMED = 1 };        /* where routed experts live */
-enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
+/* Execution paths of a forward call:
+ *   DECODE  three kernels per layer (router + shared gate/up | routed gate/up |
+ *           down + combine), any T, fp32 or bf16, resident or streamed;
+ *   FUSED   one kernel per layer for a single bf16 token on resident experts
+ *           (its workgroups hand results to each other through device-scope
+ *           counters), when its LDS fits; MOE_ERR_INVALID otherwise;
+ *   PREFILL grouped bf16 matrix-core GEMMs for token chunks on resident experts.
+ * AUTO takes FUSED where it applies, PREFILL for T >= 16 bf16 resident layers
+ * with d_model <= 4096 and no rmsnorm, DECODE otherwise. */
+enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, MOE_PATH_FUSED = 3 };
 
 typedef struct moe_layer moe_layer; /* opaque, owned by the library */
 typedef struct moe_stack moe_stack; /* opaque, owned by the library */
@@ -130,8 +139,7 @@ typedef struct {
   int32_t reuse_previous;     /* nonzero: use the expert sets of this layer's
                                  previous forward call (same n_tokens), with
                                  coefficients from this call's logits */
-  int32_t path;               /* MOE_PATH_*; AUTO picks DECODE for small T or
-                                 fp32 activations, PREFILL otherwise */
+  int32_t path;               /* MOE_PATH_* (see above) */
   int32_t residual;           /* nonzero: out = act(x_in + y) where x_in is the
                                  `residual_src` tensor (stack glue) */
   const void* residual_src;   /* DEVICE [T][d_model] of act_dtype, or NULL */
@@ -161,7 +169,9 @@ moe_status moe_layer_bytes(const moe_layer* layer, uint64_t* device_bytes, uint6
 
 /* Waits for the device, then returns and clears the layer's sticky kernel
  * error flags in *flags (HOST): bit 0 = a forced expert id was outside
- * 0..E-1 (it was replaced by 0), bit 1 = a chosen expert was not resident. */
+ * 0..E-1 (it was replaced by 0), bit 1 = a chosen expert was not resident,
+ * bit 2 = a workgroup of the fused kernel gave up waiting for its inputs
+ * (bounded wait; that call's output is not valid). */
 moe_status moe_layer_check_errors(moe_layer* layer, int32_t* flags);
 
 /* Per-kernel timing.  enable != 0 brackets every kernel the layer launches
@@ -179,7 +189,8 @@ enum {
   MOE_KERNEL_PREFILL_COMBINE = 6,
   MOE_KERNEL_PREFILL_ROUTE = 7,
   MOE_KERNEL_TOPK = 8,           /* stand-alone softmax top-K */
-  MOE_N_KERNELS = 9
+  MOE_KERNEL_FUSED_LAYER = 9,    /* whole layer for one token in one launch */
+  MOE_N_KERNELS = 10
 };
 moe_status moe_layer_profile(moe_layer* layer, int32_t enable);
 moe_status moe_layer_profile_read(moe_layer* layer, int64_t* launches, double* total_ms);

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_NOMEM, MOE_ERR_HIP, MOE_ERR_IO, MOE_ERR_STATE = range(6)
 MOE_ACT_F32, MOE_ACT_BF16 = 0, 1
 MOE_RESIDENT, MOE_STREAMED = 0, 1
-MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, MOE_PATH_FUSED = 0, 1, 2, 3
 
 _STATUS = {1: "MOE_ERR_INVALID", 2: "MOE_ERR_NOMEM", 3: "MOE_ERR_HIP", 4: "MOE_ERR_IO", 5: "MOE_ERR_STATE"}
 
@@ -202,7 +202,7 @@ def moe_layer_check_errors(layer: int) -> int:
 
 
 MOE_KERNEL_NAMES = ["route_shared", "routed_gate_up", "down_combine", "sort", "prefill_gate_up",
-                    "prefill_down", "prefill_combine", "prefill_route", "topk"]
+                    "prefill_down", "prefill_combine", "prefill_route", "topk", "fused_layer"]
 
 
 def moe_layer_profile(layer: int, enable: bool = True):

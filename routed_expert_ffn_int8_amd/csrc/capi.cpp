@@ -109,7 +109,6 @@ struct moe_layer {
   float* d_wts = nullptr;
   uint32_t* d_counter = nullptr;
   void* d_abuf = nullptr;
-  float* d_asum = nullptr;
   int32_t* d_err = nullptr;
   // prefill workspace
   char* d_prefill = nullptr;
@@ -219,7 +218,6 @@ void free_layer(moe_layer* L) {
   (void)hipFree(L->d_wts);
   (void)hipFree(L->d_counter);
   (void)hipFree(L->d_abuf);
-  (void)hipFree(L->d_asum);
   (void)hipFree(L->d_err);
   (void)hipFree(L->d_prefill);
   (void)hipFree(L->d_slots);
@@ -300,8 +298,8 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
   const size_t T = L->max_tokens, K = L->K;
   const size_t F = L->fs + K * L->f;
   if (dalloc(&L->d_logits, T * E * 4) != hipSuccess || dalloc(&L->d_ids, T * K * 4) != hipSuccess ||
-      dalloc(&L->d_wts, T * K * 4) != hipSuccess || dalloc(&L->d_sel, T * K * 8) != hipSuccess || dalloc(&L->d_counter, T * 4) != hipSuccess ||
-      dalloc(&L->d_abuf, T * F * 4) != hipSuccess || dalloc(&L->d_asum, T * (F / 8) * 4) != hipSuccess ||
+      dalloc(&L->d_wts, T * K * 4) != hipSuccess || dalloc(&L->d_sel, T * K * 8) != hipSuccess || dalloc(&L->d_counter, decode_sync_bytes(L->E)) != hipSuccess ||
+      dalloc(&L->d_abuf, T * F * 4) != hipSuccess ||
       dalloc(&L->d_err, 64) != hipSuccess)
     return fail(MOE_ERR_NOMEM, "decode workspace alloc failed");
   HIP_OK(hipMemset(L->d_ids, 0, T * K * 4));
@@ -310,7 +308,7 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
     std::vector<uint64_t> z(T * K, reinterpret_cast<uint64_t>(L->d_zero));
     HIP_OK(hipMemcpy(L->d_sel, z.data(), T * K * 8, hipMemcpyHostToDevice));
   }
-  HIP_OK(hipMemset(L->d_counter, 0, T * 4));
+  HIP_OK(hipMemset(L->d_counter, 0, decode_sync_bytes(L->E)));
   HIP_OK(hipMemset(L->d_err, 0, 64));
   // prefill workspace (bf16 only)
   if (L->act == MOE_ACT_BF16 && L->max_tokens > 1) {
@@ -346,7 +344,6 @@ LayerArgs base_args(moe_layer* L, const void* x, void* out, int T) {
   a.wts = L->d_wts;
   a.counter = L->d_counter;
   a.abuf = L->d_abuf;
-  a.asum_part = L->d_asum;
   a.err = L->d_err;
   a.out = out;
   a.prof = L->prof.get();
@@ -426,10 +423,23 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
     }
   }
   int path = o ? o->path : MOE_PATH_AUTO;
-  if (path == MOE_PATH_AUTO)
-    path = (L->act == MOE_ACT_BF16 && T >= 16 && L->d_prefill && L->d <= 4096 && L->residency == MOE_RESIDENT && !a.rms)
-               ? MOE_PATH_PREFILL
-               : MOE_PATH_DECODE;
+  const bool resident = L->residency == MOE_RESIDENT;
+  if (path == MOE_PATH_AUTO) {
+    if (resident && decode_fused_ok(a))
+      path = MOE_PATH_FUSED;
+    else if (L->act == MOE_ACT_BF16 && T >= 16 && L->d_prefill && L->d <= 4096 && resident && !a.rms)
+      path = MOE_PATH_PREFILL;
+    else
+      path = MOE_PATH_DECODE;
+  }
+  if (path == MOE_PATH_FUSED) {
+    if (!resident || !decode_fused_ok(a))
+      return fail(MOE_ERR_INVALID, "the fused path serves one bf16 token on resident experts within 64 KB of LDS");
+    a.fused = 1;
+    HIP_OK(launch_decode(a, s));
+    L->prev_T = T;
+    return MOE_OK;
+  }
   if (path == MOE_PATH_PREFILL) {
     if (L->act != MOE_ACT_BF16 || !L->d_prefill)
       return fail(MOE_ERR_INVALID, "the prefill path needs bf16 activations and max_tokens > 1");
@@ -695,7 +705,7 @@ moe_status moe_stack_forward(void* h, moe_stack* S, int32_t n_tokens, const uint
     moe_fwd_opts o{};
     o.reuse_previous = reuse_mask ? reuse_mask[l] : 0;
     o.topk_ids = ids_out ? ids_out + l * (size_t)n_tokens * L->K : nullptr;
-    o.path = MOE_PATH_DECODE;
+    o.path = MOE_PATH_AUTO;  // the rmsnorm input rules out the prefill path
     moe_status st = forward_impl(L, a, &o, s);
     if (st != MOE_OK) return st;
   }

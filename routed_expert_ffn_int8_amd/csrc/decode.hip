@@ -28,6 +28,8 @@
 // offset is folded into the bias term.  The down projection does the same
 // with fp16 (1024 + q) against fp16-rounded activations.  fp32 activations
 // use an exact byte->float convert and fp32 FMAs.
+#include <algorithm>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -44,9 +46,24 @@ __device__ __forceinline__ T ldg(const void* p) {
   return *reinterpret_cast<const __attribute__((address_space(1))) T*>(reinterpret_cast<uintptr_t>(p));
 }
 
+// Results handed from one workgroup to another inside the fused kernel are
+// written and read with device-scope relaxed atomics (coherent across the
+// XCDs' L2 caches without whole-cache write-back or invalidation); ordering
+// comes from waiting for the stores before the counter increment.
+template <class T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct XStage {
   float* xf;   // [d] input as fp32 (after rounding to the activation type)
-  v4u* xp;     // [d/8] bf16 pairs (x[8j+m], x[8j+m+4]) for m = 0..3
+  v4u* xp;     // [d/64][9] per group: 8 words of bf16 pairs (x[8j+m], x[8j+m+4]),
+               // m = 0..3, and one pad word so that the groups read by the 8
+               // lanes-groups of a wavefront fall in different LDS banks
   float* xs;   // [d/64] group sums
   float* red;  // [64] cross-wave scratch
 };
@@ -55,12 +72,12 @@ __device__ __forceinline__ XStage carve_x(char* smem, int d) {
   XStage S;
   S.xf = reinterpret_cast<float*>(smem);
   S.xp = reinterpret_cast<v4u*>(smem + (size_t)d * 4);
-  S.xs = reinterpret_cast<float*>(smem + (size_t)d * 6);
+  S.xs = reinterpret_cast<float*>(smem + (size_t)d * 4 + (size_t)(d / 64) * 144);
   S.red = S.xs + d / 64;
   return S;
 }
 
-__host__ __device__ inline size_t x_stage_bytes(int d) { return (size_t)d * 6 + (size_t)(d / 64) * 4 + 64 * 4; }
+__host__ __device__ inline size_t x_stage_bytes(int d) { return (size_t)d * 4 + (size_t)(d / 64) * 148 + 64 * 4; }
 
 // Token loads issued before the weights: words j = tid + 256 i, i < kXPre.
 constexpr int kXPre = 2;
@@ -151,7 +168,7 @@ __device__ void x_commit(const LayerArgs& a, int t, const XRegs& R, const XStage
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         p[m] = (uint32_t)f32_to_bf16(v[m]) | ((uint32_t)f32_to_bf16(v[m + 4]) << 16);
-      S.xp[j] = p;
+      S.xp[(j >> 3) * 9 + (j & 7)] = p;
     }
     float part = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     part = xor_sum(part, 1, 4);  // the 8 words of one group sit in 8 consecutive lanes
@@ -172,7 +189,7 @@ __device__ __forceinline__ float group_dot(const v4u& q0, const v4u& q1, const X
       const uint32_t w = q[m];
       const int word = g * 8 + h * 4 + m;
       if (ACT == 1) {
-        const v4u xw = S.xp[word];
+        const v4u xw = S.xp[g * 9 + h * 4 + m];
         p = dot2_bf16(nib_pair<kMagicBf16>(w, 0), xw[0], p);
         p = dot2_bf16(nib_pair<kMagicBf16>(w, 1), xw[1], p);
         p = dot2_bf16(nib_pair<kMagicBf16>(w, 2), xw[2], p);
@@ -205,18 +222,16 @@ __device__ __forceinline__ float group_term(float p, uint32_t sb, float xsum, fl
 }
 
 // Store one element of the intermediate activation vector a (position P of
-// the token's [shared | expert 0 | ... | expert K-1] vector) and return the
-// value as the down projection will see it.
+// the token's [shared | expert 0 | ... | expert K-1] vector); fp16 words hold
+// the pairs (P, P + 4) of each 8-aligned run.
 template <int ACT>
-__device__ __forceinline__ float store_a(void* abuf_t, int P, float v) {
+__device__ __forceinline__ void store_a(void* abuf_t, int P, float v) {
   if (ACT == 1) {
-    const uint16_t h = f32_to_f16(v);
     const int m = P & 7;
-    static_cast<uint16_t*>(abuf_t)[(P & ~7) + (m & 3) * 2 + (m >> 2)] = h;
-    return f16_to_f32(h);
+    st_dev(static_cast<uint16_t*>(abuf_t) + (P & ~7) + (m & 3) * 2 + (m >> 2), f32_to_f16(v));
+  } else {
+    st_dev(static_cast<float*>(abuf_t) + P, v);
   }
-  static_cast<float*>(abuf_t)[P] = v;
-  return v;
 }
 
 __device__ __forceinline__ char* abuf_of(const LayerArgs& a, int t, int act) {
@@ -226,9 +241,11 @@ __device__ __forceinline__ char* abuf_of(const LayerArgs& a, int t, int act) {
 
 // gate/up GEMV + SiLU*mul for the 8-row block `rb` of one expert blob;
 // the result goes to positions apos + rows of the activation vector.
+// `xr` holds the token loads, issued by the caller before it waited on
+// anything, so they overlap the weight fetch.
 template <int ACT, int MAXI>
 __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, const BlobOffsets& o, int rb,
-                              int apos, const XStage& S) {
+                              int apos, const XStage& S, const XRegs& xr) {
   const int tid = threadIdx.x, r = tid & 7, jj = tid >> 3;
   const int G = a.d >> 6;
   const int row = rb * 8 + r;
@@ -236,8 +253,6 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
   const uint8_t* uq = blob + o.uq;
   const uint8_t* gsb = blob + o.gsb + ((size_t)rb * G * 8 + r) * 4;  // + g * 32
   const uint8_t* usb = blob + o.usb + ((size_t)rb * G * 8 + r) * 4;
-  XRegs xr;
-  x_issue<ACT>(a, t, xr);
   float accg = 0.f, accu = 0.f;
   for (int base = 0; base < G; base += 32 * MAXI) {
     v4u qg0[MAXI], qg1[MAXI], qu0[MAXI], qu1[MAXI];
@@ -273,11 +288,7 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
   if (tid < 8) {
     const float gsum = (S.red[r * 2] + S.red[16 + r * 2]) + (S.red[32 + r * 2] + S.red[48 + r * 2]);
     const float usum = (S.red[r * 2 + 1] + S.red[16 + r * 2 + 1]) + (S.red[32 + r * 2 + 1] + S.red[48 + r * 2 + 1]);
-    const int F = a.fs + a.K * a.f;
-    const int P = apos + row;
-    float seen = store_a<ACT>(abuf_of(a, t, ACT), P, silu(gsum) * usum);
-    seen = xor_sum(seen, 1, 4);
-    if (tid == 0) a.asum_part[(size_t)t * (F / 8) + (P >> 3)] = seen;
+    store_a<ACT>(abuf_of(a, t, ACT), apos + row, silu(gsum) * usum);
   }
 }
 
@@ -468,7 +479,7 @@ __device__ __forceinline__ void stage_logits(const LayerArgs& a, int t, float* s
 __device__ __forceinline__ void publish_routing(const LayerArgs& a, int t, int lane, int id, float w) {
   if (lane < a.K) {
     const size_t o = (size_t)t * a.K + lane;
-    a.ids[o] = id;
+    if (a.ids != a.forced) a.ids[o] = id;  // reusing the stored sets: they stay as they are
     a.wts[o] = w;
     a.sel_addr[o] = a.expert_addr[id];
     if (a.ids_out) a.ids_out[o] = id;
@@ -480,18 +491,14 @@ __device__ __forceinline__ void publish_routing(const LayerArgs& a, int t, int l
 constexpr int kRouterPre = 8;  // 16-byte router chunks per lane issued up front (d <= 8192)
 constexpr int kWaves = kThreads / 64;
 
-template <int ACT, int MAXI>
-__global__ __launch_bounds__(kThreads) void route_shared_kernel(LayerArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  const XStage S = carve_x(smem, a.d);
-  const int t = blockIdx.y;
-  const int NR = (a.E + kWaves - 1) / kWaves;  // one router row per wavefront
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if ((int)blockIdx.x >= NR) {
-    gate_up_block<ACT, MAXI>(a, t, a.shared_blob, a.so, blockIdx.x - NR, 0, S);
-    return;
-  }
-  const int e = blockIdx.x * kWaves + wave;
+// Logit of router row e for token t by one wavefront (e >= E: no store).
+// rep == nullptr: store to the logits array.  Otherwise lane j stores the
+// logit, tagged with `tag` in the high word, to entry e of replica j of the
+// tagged table (replicas `rstride` entries apart).
+template <int ACT>
+__device__ void router_row(const LayerArgs& a, int t, int e, const XStage& S, uint64_t* rep = nullptr,
+                           size_t rstride = 0, uint32_t tag = 0) {
+  const int lane = threadIdx.x & 63;
   const int ec = min(e, a.E - 1);
   const int NC = a.d >> 4;  // 16-byte chunks per router row
   const int8_t* wrow = a.router_w + (size_t)ec * a.d;
@@ -518,12 +525,31 @@ __global__ __launch_bounds__(kThreads) void route_shared_kernel(LayerArgs a) {
       }
     }
   }
-  acc = xor_sum(acc, 1, 32);
-  if (lane == 0 && e < a.E) {
+  acc = xor_sum(acc, 1, 32);  // every lane holds the same sum
+  if (e < a.E) {
     const float s = f16_to_f32(a.router_scale[e]);
     const float b = a.router_bias ? a.router_bias[e] : 0.f;
-    a.logits[(size_t)t * a.E + e] = fmaf(s, acc, b);
+    const float v = fmaf(s, acc, b);
+    if (rep)
+      st_dev(rep + (size_t)lane * rstride + e, ((uint64_t)tag << 32) | __float_as_uint(v));
+    else if (lane == 0)
+      a.logits[(size_t)t * a.E + e] = v;
   }
+}
+
+template <int ACT, int MAXI>
+__global__ __launch_bounds__(kThreads) void route_shared_kernel(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const XStage S = carve_x(smem, a.d);
+  const int t = blockIdx.y;
+  const int NR = (a.E + kWaves - 1) / kWaves;  // one router row per wavefront
+  if ((int)blockIdx.x >= NR) {
+    XRegs xr;
+    x_issue<ACT>(a, t, xr);
+    gate_up_block<ACT, MAXI>(a, t, a.shared_blob, a.so, blockIdx.x - NR, 0, S, xr);
+    return;
+  }
+  router_row<ACT>(a, t, blockIdx.x * kWaves + (threadIdx.x >> 6), S);
 }
 
 // Stand-alone top-K (one wavefront per token), used when the routing must be
@@ -549,6 +575,8 @@ __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
   const int t = blockIdx.y;
   const int RB = a.f >> 3;
   const int k = blockIdx.x / RB, rb = blockIdx.x - k * RB;
+  XRegs xr;
+  x_issue<ACT>(a, t, xr);
   const uint8_t* blob;
   if (a.topk_in_gate_up) {  // resident experts: every wavefront finds its expert itself
     stage_logits<kThreads>(a, t, s_logits);
@@ -561,8 +589,12 @@ __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
       }
       return;
     }
-    const int id = topk_kth<NE>(a, t, s_logits, k);
-    blob = a.expert_base + (size_t)id * a.expert_stride;
+    if (threadIdx.x < 64) {
+      const int id = topk_kth<NE>(a, t, s_logits, k);
+      if (threadIdx.x == 0) scratch[0] = (uint32_t)id;
+    }
+    __syncthreads();
+    blob = a.expert_base + (size_t)scratch[0] * a.expert_stride;
   } else {
     blob = reinterpret_cast<const uint8_t*>(a.sel_addr[(size_t)t * a.K + k]);
   }
@@ -570,35 +602,73 @@ __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
     if (threadIdx.x == 0) atomicOr(a.err, kErrMissingExpert);
     blob = a.zero_blob;
   }
-  gate_up_block<ACT, MAXI>(a, t, blob, a.ro, rb, a.fs + k * a.f, S);
+  gate_up_block<ACT, MAXI>(a, t, blob, a.ro, rb, a.fs + k * a.f, S, xr);
 }
 
 // ---------------------------------------------------------------- kernel C
+// The activation vector sits in LDS as [group][WPG + 1] 16-byte words (WPG =
+// 8 fp16 or 16 fp32 words per 64-wide group, plus one pad word): the 8 groups
+// a wavefront reads at once then start in different LDS banks.
+__host__ __device__ constexpr int a_words(int act) { return act == 1 ? 8 : 16; }
 __host__ __device__ inline size_t down_lds_bytes(int F, int NI, int K, int act) {
-  return (size_t)F * (act == 1 ? 2 : 4) + (size_t)NI * 4 + (size_t)K * 4 + 32 * 4;
+  (void)F;
+  return (size_t)NI * (a_words(act) + 1) * 16 + (size_t)NI * 4 + (size_t)K * 4 + 32 * 4;
+}
+__device__ __forceinline__ int a_slot(int j, int wpg) { return (j / wpg) * (wpg + 1) + j % wpg; }
+
+constexpr int kAPre = 4;  // 16-byte activation words per thread held in registers for staging
+
+// asum[i] = sum of the 64 values of group i of the staged activation vector
+// (as the down projection reads them), ending with a workgroup barrier.
+template <int ACT>
+__device__ __forceinline__ void group_sums(const char* lds_a, float* asum, int NI) {
+  constexpr int WPG = a_words(ACT);  // 16-byte words per group, in consecutive lanes
+  for (int i = threadIdx.x; i < NI * WPG; i += kThreads) {
+    const v4u w = reinterpret_cast<const v4u*>(lds_a)[a_slot(i, WPG)];
+    float s;
+    if (ACT == 1) {
+      float h[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        h[2 * m] = f16_to_f32((uint16_t)(w[m] & 0xFFFFu));
+        h[2 * m + 1] = f16_to_f32((uint16_t)(w[m] >> 16));
+      }
+      s = ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
+    } else {
+      s = (__uint_as_float(w[0]) + __uint_as_float(w[1])) + (__uint_as_float(w[2]) + __uint_as_float(w[3]));
+    }
+    s = xor_sum(s, 1, WPG / 2);
+    if ((i & (WPG - 1)) == 0) asum[i / WPG] = s;
+  }
+  __syncthreads();
 }
 
-constexpr int kAPre = 4;  // 16-byte activation words per thread loaded before the weights
-
-template <int ACT, int MAXI>
-__global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
-  extern __shared__ __align__(16) char smem[];
+// Down GEMV of the shared and chosen experts for output rows 8*rb..8*rb+7 of
+// token t and the weighted combine.  sel[k] / wk_src[k]: blob address and
+// weight of the k-th chosen expert.  A_FIRST: the activation vector is
+// already complete, so its loads go out before the weights; otherwise the
+// weights go out first and `before_stage()` runs (it waits for the vector)
+// before the activations are read.
+template <int ACT, int MAXI, bool A_FIRST, class Hook>
+__device__ void down_block(const LayerArgs& a, int t, int rb, const uint64_t* sel, const float* wk_src,
+                           char* smem, Hook&& before_stage) {
   const int tid = threadIdx.x, r = tid & 7, jj = tid >> 3;
-  const int t = blockIdx.y, rb = blockIdx.x;
   const int row = rb * 8 + r;
   const int Gs = a.fs >> 6, Gf = a.f >> 6, K = a.K;
   const int NI = Gs + K * Gf;
   const int F = a.fs + K * a.f;
+  constexpr int WPG = a_words(ACT);
   char* lds_a = smem;
-  float* asum = reinterpret_cast<float*>(smem + (size_t)F * (ACT == 1 ? 2 : 4));
+  float* asum = reinterpret_cast<float*>(smem + (size_t)NI * (WPG + 1) * 16);
   float* wk = asum + NI;
   float* red = wk + K;
-  const uint64_t* sel_t = a.sel_addr + (size_t)t * K;
   const char* abuf_t = abuf_of(a, t, ACT);
   const int NW = F * (ACT == 1 ? 2 : 4) / 16;  // 16-byte words of the activation vector
   v4u ar[kAPre];
+  if (A_FIRST) {
 #pragma unroll
-  for (int i = 0; i < kAPre; ++i) ar[i] = ldg<v4u>(abuf_t + (size_t)min(tid + kThreads * i, NW - 1) * 16);
+    for (int i = 0; i < kAPre; ++i) ar[i] = ldg<v4u>(abuf_t + (size_t)min(tid + kThreads * i, NW - 1) * 16);
+  }
   float acc = 0.f;
   for (int base = 0; base < NI; base += 32 * MAXI) {
     v4u q0[MAXI], q1[MAXI];
@@ -615,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
         const int k = (it - Gs) / Gf;
         g = (it - Gs) - k * Gf;
         G = Gf;
-        blob = reinterpret_cast<const uint8_t*>(sel_t[k]);
+        blob = reinterpret_cast<const uint8_t*>(sel[k]);
         if (blob == nullptr) blob = a.zero_blob;  // flagged by the gate/up kernel
         oq = a.ro.dq; osb = a.ro.dsb;
       }
@@ -625,22 +695,33 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
       sb[i] = ldg<uint32_t>(blob + osb + (((size_t)rb * G + g) * 8 + r) * 4);
     }
     if (base == 0) {
+      if (A_FIRST) {
 #pragma unroll
-      for (int i = 0; i < kAPre; ++i) {
-        const int j = tid + kThreads * i;
-        if (j < NW) reinterpret_cast<v4u*>(lds_a)[j] = ar[i];
-      }
-      for (int j = tid + kThreads * kAPre; j < NW; j += kThreads)
-        reinterpret_cast<v4u*>(lds_a)[j] = ldg<v4u>(abuf_t + (size_t)j * 16);
-      const float* part = a.asum_part + (size_t)t * (F / 8);
-      for (int i = tid; i < NI; i += kThreads) {
-        float s = 0.f;
+        for (int i = 0; i < kAPre; ++i) {
+          const int j = tid + kThreads * i;
+          if (j < NW) reinterpret_cast<v4u*>(lds_a)[a_slot(j, WPG)] = ar[i];
+        }
+        for (int j = tid + kThreads * kAPre; j < NW; j += kThreads)
+          reinterpret_cast<v4u*>(lds_a)[a_slot(j, WPG)] = ldg<v4u>(abuf_t + (size_t)j * 16);
+      } else {  // written by other workgroups of this launch: device-coherent loads
+        before_stage();
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(abuf_t);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(lds_a);
+        constexpr int kAD = 8;  // device-scope loads in flight per thread
+        for (int j0 = 0; j0 < 2 * NW; j0 += kThreads * kAD) {
+          uint64_t v[kAD];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) s += part[i * 8 + p];
-        asum[i] = s;
+          for (int i = 0; i < kAD; ++i) v[i] = ld_dev(src + min(j0 + tid + kThreads * i, 2 * NW - 1));
+#pragma unroll
+          for (int i = 0; i < kAD; ++i) {
+            const int j = j0 + tid + kThreads * i;
+            if (j < 2 * NW) dst[a_slot(j >> 1, WPG) * 2 + (j & 1)] = v[i];
+          }
+        }
       }
-      if (tid < K) wk[tid] = a.wts[(size_t)t * K + tid];
+      if (tid < K) wk[tid] = wk_src[tid];
       __syncthreads();
+      group_sums<ACT>(lds_a, asum, NI);
     }
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
@@ -653,16 +734,15 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const uint32_t w = q[m];
-            const int word = it * 8 + h * 4 + m;
             if (ACT == 1) {
-              const v4u av = reinterpret_cast<const v4u*>(lds_a)[word];
+              const v4u av = reinterpret_cast<const v4u*>(lds_a)[it * 9 + h * 4 + m];
               p = dot2_f16(nib_pair<kMagicF16>(w, 0), av[0], p);
               p = dot2_f16(nib_pair<kMagicF16>(w, 1), av[1], p);
               p = dot2_f16(nib_pair<kMagicF16>(w, 2), av[2], p);
               p = dot2_f16(nib_pair<kMagicF16>(w, 3), av[3], p);
             } else {
-              const float4 x0 = reinterpret_cast<const float4*>(lds_a)[word * 2];
-              const float4 x1 = reinterpret_cast<const float4*>(lds_a)[word * 2 + 1];
+              const float4 x0 = reinterpret_cast<const float4*>(lds_a)[it * 17 + (h * 4 + m) * 2];
+              const float4 x1 = reinterpret_cast<const float4*>(lds_a)[it * 17 + (h * 4 + m) * 2 + 1];
               const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
               p = fmaf((float)(lo & 0xFFu), x0.x, p);
               p = fmaf((float)(hi & 0xFFu), x0.y, p);
@@ -697,6 +777,189 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
       static_cast<float*>(a.out)[o] = v;
     }
   }
+}
+
+template <int ACT, int MAXI>
+__global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int t = blockIdx.y;
+  down_block<ACT, MAXI, true>(a, t, blockIdx.x, a.sel_addr + (size_t)t * a.K, a.wts + (size_t)t * a.K, smem,
+                              [] {});
+}
+
+// ---------------------------------------------------------------- fused layer
+// One launch per batch-1 bf16 layer on resident experts.  Workgroups, in
+// block order: router rows | shared gate/up | routed gate/up | down+combine.
+// A workgroup only waits for results of lower-numbered workgroups, and
+// workgroups are dispatched in block order within each XCD, so the lowest
+// unfinished workgroup can always run: no deadlock even when the grid does
+// not fit the GPU at once.  Waits are bounded spins (a timeout raises an
+// error flag and the workgroup carries on).
+//
+// Hand-offs.  Each launch has a tag (launch count + 1, read from the
+// synchronisation area).  Router wavefronts store their logit with the tag
+// into 64 replicas of a logit table; a routed gate/up or down workgroup polls
+// its replica (workgroup index % 64) until every entry carries this launch's
+// tag, so the logits need no counter.  Gate/up workgroups count their
+// arrivals (8 sub-counters, then a top counter; counters only grow, and a
+// phase is complete when a counter reaches tag * members); the arrival that
+// completes the phase sets 64 ready flags to the tag, and down workgroups
+// poll one flag each.  The last workgroup to finish publishes the next tag.
+// Every polled or counted word has its own cache line, 4160 bytes from the
+// next, so the hundreds of pollers spread over memory channels instead of
+// queueing on one address.  Nothing is reset between launches, so graph
+// replays need no memset.
+constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kSyncStride = 4160 / 4;  // words between slots
+constexpr int kSyncSubs = 8, kSyncFlags = 64, kLogitReplicas = 64;
+constexpr int kSlotGateUp = 0;                                // subs, top, flags
+constexpr int kSlotDone = kSlotGateUp + kSyncSubs + 1 + kSyncFlags;  // subs, top
+constexpr int kSlotEpoch = kSlotDone + kSyncSubs + 1;         // replicas of the launch count
+constexpr int kSyncSlots = kSlotEpoch + kSyncFlags;
+
+__host__ __device__ inline size_t logit_rep_stride(int E) {  // uint64 entries between replicas
+  return ((size_t)E * 8 + 4095) / 4096 * 512 + 8;
+}
+__host__ __device__ inline size_t sync_area_bytes(int E) {
+  return (size_t)kSyncSlots * kSyncStride * 4 + (size_t)kLogitReplicas * logit_rep_stride(E) * 8;
+}
+
+__device__ __forceinline__ uint32_t* sync_slot(uint32_t* area, int slot) {
+  return area + (size_t)slot * kSyncStride;
+}
+
+// Member i of n arrives in the phase whose slots start at `base`; true (in
+// the calling lane) for the arrival that completes the phase.
+__device__ __forceinline__ bool phase_count(uint32_t* area, int base, int i, int n, uint32_t tag) {
+  const int j = i % kSyncSubs;
+  const uint32_t need = (uint32_t)((n - j + kSyncSubs - 1) / kSyncSubs);
+  if (atomicAdd(sync_slot(area, base + j), 1u) != tag * need - 1u) return false;
+  const uint32_t groups = (uint32_t)min(n, kSyncSubs);
+  return atomicAdd(sync_slot(area, base + kSyncSubs), 1u) == tag * groups - 1u;
+}
+
+// Gate/up member i of n arrives after its device-scope stores completed.
+__device__ __forceinline__ void gate_up_arrive(uint32_t* area, int i, int n, uint32_t tag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const bool last = threadIdx.x == 0 && phase_count(area, kSlotGateUp, i, n, tag);
+    if (__ballot(last)) st_dev(sync_slot(area, kSlotGateUp + kSyncSubs + 1 + (int)threadIdx.x), tag);
+  }
+}
+
+__device__ __forceinline__ void gate_up_wait(const LayerArgs& a, uint32_t* area, uint32_t tag) {
+  if (threadIdx.x == 0) {
+    const uint32_t* flag = sync_slot(area, kSlotGateUp + kSyncSubs + 1 + (int)(blockIdx.x % kSyncFlags));
+    uint32_t it = 0;
+    while (ld_dev(flag) != tag) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++it == kSpinLimit) {
+        atomicOr(a.err, kErrSyncTimeout);
+        break;
+      }
+    }
+  }
+  __syncthreads();  // the activations are then read with device-scope loads
+}
+
+// Copy this launch's logits from replica `rep` into LDS, polling each entry
+// until it carries `tag`; ends with a workgroup barrier.
+__device__ __forceinline__ void stage_tagged_logits(const LayerArgs& a, const uint64_t* rep, uint32_t tag,
+                                                    float* s_logits) {
+  constexpr int N = (1024 + kThreads - 1) / kThreads;
+  uint64_t v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = ld_dev(rep + min((int)threadIdx.x + kThreads * i, a.E - 1));
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int e = threadIdx.x + kThreads * i;
+    if (e < a.E) {
+      uint32_t it = 0;
+      while ((uint32_t)(v[i] >> 32) != tag) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++it == kSpinLimit) {
+          atomicOr(a.err, kErrSyncTimeout);
+          break;
+        }
+        v[i] = ld_dev(rep + e);
+      }
+      s_logits[e] = __uint_as_float((uint32_t)v[i]);
+    }
+  }
+  __syncthreads();
+}
+
+// Every workgroup arrives here last; the final one publishes the next tag.
+__device__ __forceinline__ void finish_launch(uint32_t* area, int total, uint32_t tag) {
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const bool last = threadIdx.x == 0 && phase_count(area, kSlotDone, blockIdx.x, total, tag);
+    if (__ballot(last)) st_dev(sync_slot(area, kSlotEpoch + (int)threadIdx.x), tag);
+  }
+}
+
+__host__ __device__ inline int fused_groups(int E, int K, int d, int f, int fs, int* NR, int* NS, int* NG, int* ND) {
+  *NR = (E + kWaves - 1) / kWaves;
+  *NS = fs / 8;
+  *NG = K * (f / 8);
+  *ND = d / 8;
+  return *NR + *NS + *NG + *ND;
+}
+
+template <int MAXI, int NE, int MAXID>
+__global__ __launch_bounds__(kThreads) void fused_layer_kernel(LayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ uint32_t scratch[128];
+  __shared__ float s_logits[1024];
+  __shared__ uint64_t s_sel[64];
+  __shared__ float s_w[64];
+  int NR, NS, NG, ND;
+  const int total = fused_groups(a.E, a.K, a.d, a.f, a.fs, &NR, &NS, &NG, &ND);
+  const int b = blockIdx.x;
+  uint32_t* area = a.counter;
+  const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kSyncFlags)) + 1u;
+  uint64_t* lrep = reinterpret_cast<uint64_t*>(area + (size_t)kSyncSlots * kSyncStride);
+  const size_t rstride = logit_rep_stride(a.E);
+  const XStage S = carve_x(smem, a.d);
+  if (b < NR) {
+    router_row<1>(a, 0, b * kWaves + (threadIdx.x >> 6), S, lrep, rstride, tag);
+  } else if (b < NR + NS) {
+    XRegs xr;
+    x_issue<1>(a, 0, xr);
+    gate_up_block<1, MAXI>(a, 0, a.shared_blob, a.so, b - NR, 0, S, xr);
+    gate_up_arrive(area, b - NR, NS + NG, tag);
+  } else if (b < NR + NS + NG) {
+    const int g = b - NR - NS, RB = a.f >> 3;
+    const int k = g / RB, rb = g - k * RB;
+    XRegs xr;
+    x_issue<1>(a, 0, xr);
+    stage_tagged_logits(a, lrep + (size_t)(b % kLogitReplicas) * rstride, tag, s_logits);
+    if (threadIdx.x < 64) {  // one wavefront finds the expert
+      const int id = topk_kth<NE>(a, 0, s_logits, k);
+      if (threadIdx.x == 0) scratch[0] = (uint32_t)id;
+    }
+    __syncthreads();
+    const int id = (int)scratch[0];
+    gate_up_block<1, MAXI>(a, 0, a.expert_base + (size_t)id * a.expert_stride, a.ro, rb, a.fs + k * a.f, S, xr);
+    gate_up_arrive(area, b - NR, NS + NG, tag);
+  } else {
+    const int rb = b - NR - NS - NG;
+    stage_tagged_logits(a, lrep + (size_t)(b % kLogitReplicas) * rstride, tag, s_logits);
+    if (threadIdx.x < 64) {
+      int id;
+      float w;
+      topk_wave<NE>(a, 0, s_logits, &id, &w, scratch);
+      if (threadIdx.x < a.K) {
+        s_sel[threadIdx.x] = reinterpret_cast<uint64_t>(a.expert_base + (size_t)id * a.expert_stride);
+        s_w[threadIdx.x] = w;
+      }
+      if (rb == 0) publish_routing(a, 0, threadIdx.x, id, w);
+    }
+    __syncthreads();
+    down_block<1, MAXID, false>(a, 0, rb, s_sel, s_w, smem, [&] { gate_up_wait(a, area, tag); });
+  }
+  finish_launch(area, total, tag);
 }
 
 template <int ACT, int MAXI, int NE>
@@ -754,13 +1017,56 @@ hipError_t launch_all(const LayerArgs& a, hipStream_t s) {
   return launch_c<ACT>(a, s);
 }
 
+size_t fused_lds_bytes(const LayerArgs& a) {
+  const int NI = a.fs / 64 + a.K * (a.f / 64);
+  const int F = a.fs + a.K * a.f;
+  return std::max(x_stage_bytes(a.d), down_lds_bytes(F, NI, a.K, 1));
+}
+
+template <int NE, int MAXI>
+hipError_t launch_fused_mi(const LayerArgs& a, hipStream_t s) {
+  int NR, NS, NG, ND;
+  const int total = fused_groups(a.E, a.K, a.d, a.f, a.fs, &NR, &NS, &NG, &ND);
+  const int NI = a.fs / 64 + a.K * (a.f / 64);
+  const size_t lds = fused_lds_bytes(a);
+  if (NI <= 128)
+    launch_timed(a.prof, kKFusedLayer, fused_layer_kernel<MAXI, NE, 4>, dim3(total), dim3(kThreads), lds, s, a);
+  else
+    launch_timed(a.prof, kKFusedLayer, fused_layer_kernel<MAXI, NE, 8>, dim3(total), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int NE>
+hipError_t launch_fused_ne(const LayerArgs& a, hipStream_t s) {
+  const int maxi = (a.d / 64 + 31) / 32;
+  if (maxi <= 1) return launch_fused_mi<NE, 1>(a, s);
+  if (maxi == 2) return launch_fused_mi<NE, 2>(a, s);
+  if (maxi == 3) return launch_fused_mi<NE, 3>(a, s);
+  return launch_fused_mi<NE, 4>(a, s);
+}
+
+hipError_t launch_fused(const LayerArgs& a, hipStream_t s) {
+  if (a.E <= 64) return launch_fused_ne<1>(a, s);
+  if (a.E <= 128) return launch_fused_ne<2>(a, s);
+  if (a.E <= 256) return launch_fused_ne<4>(a, s);
+  return launch_fused_ne<16>(a, s);
+}
+
 }  // namespace
 
 size_t decode_lds_bytes_x(int d) { return x_stage_bytes(d); }
+size_t decode_sync_bytes(int E) { return sync_area_bytes(E); }
 size_t decode_lds_bytes_down(int F, int NI, int K, int act) { return down_lds_bytes(F, NI, K, act); }
+
+// The fused layer kernel serves one bf16 token on resident experts, when its
+// LDS (dynamic part plus about 6 KB of static routing state) fits in 64 KB.
+bool decode_fused_ok(const LayerArgs& a) {
+  return a.T == 1 && a.act == 1 && a.E <= 1024 && fused_lds_bytes(a) + 6 * 1024 <= 64 * 1024;
+}
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  if (a.fused) return decode_fused_ok(a) ? launch_fused(a, s) : hipErrorInvalidValue;
   return a.act == 1 ? launch_all<1>(a, s) : launch_all<0>(a, s);
 }
 

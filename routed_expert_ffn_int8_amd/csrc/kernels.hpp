@@ -30,7 +30,8 @@ inline void launch_timed(Profiler* prof, int kid, Kern kernel, dim3 grid, dim3 b
   }
 }
 enum : int { kKRouteShared = 0, kKRoutedGateUp = 1, kKDownCombine = 2, kKSort = 3, kKPrefillGateUp = 4,
-             kKPrefillDown = 5, kKPrefillCombine = 6, kKPrefillRoute = 7, kKTopK = 8, kNumKernels = 9 };
+             kKPrefillDown = 5, kKPrefillCombine = 6, kKPrefillRoute = 7, kKTopK = 8, kKFusedLayer = 9,
+             kNumKernels = 10 };
 
 // Offsets of gate/up/down Q and SB regions inside an expert blob.
 struct BlobOffsets {
@@ -59,9 +60,8 @@ struct LayerArgs {
   int32_t* ids;        // [T][K]
   uint64_t* sel_addr;  // [T][K] blob address of each chosen expert (written with the ids)
   float* wts;          // [T][K]
-  uint32_t* counter;   // [T], zero between calls
+  uint32_t* counter;   // synchronisation area of the fused kernel (decode_sync_bytes(E)), zeroed at creation
   void* abuf;          // [T][F] F = fs + K*f: fp16 pair-permuted (bf16 mode) or fp32
-  float* asum_part;    // [T][F/8]
   int32_t* err;        // sticky error flags
   // options
   const int32_t* forced;  // [T][K] or null
@@ -73,14 +73,19 @@ struct LayerArgs {
   // 4 routed gate/up, 8 down + combine
   int stages;
   int topk_in_gate_up;  // 1: every routed gate/up workgroup runs the top-K itself
+  int fused;            // 1: one launch per layer (batch 1, bf16, resident experts)
   Profiler* prof;  // host pointer, never read by the kernels
 };
 
 enum : int { kStageRouter = 1, kStageShared = 2, kStageRouted = 4, kStageDown = 8, kStageAll = 15 };
 
-enum : int32_t { kErrBadForcedId = 1, kErrMissingExpert = 2 };
+enum : int32_t { kErrBadForcedId = 1, kErrMissingExpert = 2, kErrSyncTimeout = 4 };
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s);
+// Whether the single-launch decode kernel can serve these arguments.
+bool decode_fused_ok(const LayerArgs& a);
+// Bytes of its synchronisation area for E experts.
+size_t decode_sync_bytes(int E);
 
 struct PrefillArgs {
   LayerArgs L;
