@@ -51,7 +51,8 @@ enum { MOE_RESIDENT = 0, MOE_STREAMED = 1 };        /* where routed experts live
  *           down + combine), any T, fp32 or bf16, resident or streamed;
  *   FUSED   one kernel per layer for a single bf16 token on resident experts
  *           (its workgroups hand results to each other through device-scope
- *           counters), when its LDS fits; MOE_ERR_INVALID otherwise;
+ *           flags and counters), for d_model <= 4096 when its LDS fits;
+ *           MOE_ERR_INVALID otherwise;
  *   PREFILL grouped bf16 matrix-core GEMMs for token chunks on resident experts.
  * AUTO takes FUSED where it applies, PREFILL for T >= 16 bf16 resident layers
  * with d_model <= 4096 and no rmsnorm, DECODE otherwise. */

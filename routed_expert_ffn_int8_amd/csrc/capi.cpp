@@ -115,6 +115,7 @@ struct moe_layer {
   size_t prefill_bytes = 0;
   // previous call (for reuse_previous)
   int prev_T = -1;
+  int fused_ok = -1;  // whether the single-launch decode kernel serves this layer here (-1: not yet known)
   // streamed experts
   uint8_t* h_store = nullptr;  // pinned, E blobs
   uint8_t* d_slots = nullptr;
@@ -424,8 +425,14 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
   }
   int path = o ? o->path : MOE_PATH_AUTO;
   const bool resident = L->residency == MOE_RESIDENT;
+  if (L->fused_ok < 0) {  // shape, LDS and residency check, once per layer
+    LayerArgs one = a;
+    one.T = 1;
+    L->fused_ok = resident && decode_fused_ok(one) ? 1 : 0;
+  }
+  const bool fused_ok = L->fused_ok == 1 && T == 1;
   if (path == MOE_PATH_AUTO) {
-    if (resident && decode_fused_ok(a))
+    if (fused_ok)
       path = MOE_PATH_FUSED;
     else if (L->act == MOE_ACT_BF16 && T >= 16 && L->d_prefill && L->d <= 4096 && resident && !a.rms)
       path = MOE_PATH_PREFILL;
@@ -433,8 +440,10 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
       path = MOE_PATH_DECODE;
   }
   if (path == MOE_PATH_FUSED) {
-    if (!resident || !decode_fused_ok(a))
-      return fail(MOE_ERR_INVALID, "the fused path serves one bf16 token on resident experts within 64 KB of LDS");
+    if (!fused_ok)
+      return fail(MOE_ERR_INVALID,
+                  "the fused path serves one bf16 token on resident experts, d_model <= 4096, within 64 KB "
+                  "of LDS");
     a.fused = 1;
     HIP_OK(launch_decode(a, s));
     L->prev_T = T;

@@ -65,7 +65,7 @@ struct XStage {
                // m = 0..3, and one pad word so that the groups read by the 8
                // lanes-groups of a wavefront fall in different LDS banks
   float* xs;   // [d/64] group sums
-  float* red;  // [64] cross-wave scratch
+  float* red;  // [128] cross-wave scratch
 };
 
 __device__ __forceinline__ XStage carve_x(char* smem, int d) {
@@ -77,7 +77,7 @@ __device__ __forceinline__ XStage carve_x(char* smem, int d) {
   return S;
 }
 
-__host__ __device__ inline size_t x_stage_bytes(int d) { return (size_t)d * 4 + (size_t)(d / 64) * 148 + 64 * 4; }
+__host__ __device__ inline size_t x_stage_bytes(int d) { return (size_t)d * 4 + (size_t)(d / 64) * 148 + 128 * 4; }
 
 // Token loads issued before the weights: words j = tid + 256 i, i < kXPre.
 constexpr int kXPre = 2;
@@ -239,28 +239,32 @@ __device__ __forceinline__ char* abuf_of(const LayerArgs& a, int t, int act) {
   return static_cast<char*>(a.abuf) + (size_t)t * F * (act == 1 ? 2 : 4);
 }
 
-// gate/up GEMV + SiLU*mul for the 8-row block `rb` of one expert blob;
-// the result goes to positions apos + rows of the activation vector.
-// `xr` holds the token loads, issued by the caller before it waited on
-// anything, so they overlap the weight fetch.
-template <int ACT, int MAXI>
+// gate/up GEMV + SiLU*mul for rows ROWS*rb .. ROWS*rb+ROWS-1 (ROWS = 8 or
+// 16) of one expert blob; the results go to positions apos + row of the
+// activation vector.  Lane (r = tid % ROWS, jj = tid / ROWS) reads row r for
+// the groups jj + JJ i (JJ = 256 / ROWS): each wavefront load covers eight
+// whole 128-byte runs.  `xr` holds the token loads, issued by the caller
+// before it waited on anything, so they overlap the weight fetch.
+template <int ACT, int MAXI, int ROWS = 8>
 __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, const BlobOffsets& o, int rb,
                               int apos, const XStage& S, const XRegs& xr) {
-  const int tid = threadIdx.x, r = tid & 7, jj = tid >> 3;
+  constexpr int JJ = kThreads / ROWS;
+  const int tid = threadIdx.x, r = tid % ROWS, jj = tid / ROWS;
   const int G = a.d >> 6;
-  const int row = rb * 8 + r;
+  const int row = rb * ROWS + r;
+  const int rb8 = row >> 3, r8 = row & 7;  // 8-row block of the packed layout
   const uint8_t* gq = blob + o.gq;
   const uint8_t* uq = blob + o.uq;
-  const uint8_t* gsb = blob + o.gsb + ((size_t)rb * G * 8 + r) * 4;  // + g * 32
-  const uint8_t* usb = blob + o.usb + ((size_t)rb * G * 8 + r) * 4;
+  const uint8_t* gsb = blob + o.gsb + ((size_t)rb8 * G * 8 + r8) * 4;  // + g * 32
+  const uint8_t* usb = blob + o.usb + ((size_t)rb8 * G * 8 + r8) * 4;
   float accg = 0.f, accu = 0.f;
-  for (int base = 0; base < G; base += 32 * MAXI) {
+  for (int base = 0; base < G; base += JJ * MAXI) {
     v4u qg0[MAXI], qg1[MAXI], qu0[MAXI], qu1[MAXI];
     uint32_t sg[MAXI], su[MAXI];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-      const int g = min(base + jj + 32 * i, G - 1);
-      const size_t off = (((size_t)rb * G + g) * 2) * 128 + r * 16;
+      const int g = min(base + jj + JJ * i, G - 1);
+      const size_t off = (((size_t)rb8 * G + g) * 2) * 128 + r8 * 16;
       qg0[i] = ldg<v4u>(gq + off);
       qg1[i] = ldg<v4u>(gq + off + 128);
       qu0[i] = ldg<v4u>(uq + off);
@@ -271,23 +275,25 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
     if (base == 0) x_commit<ACT>(a, t, xr, S);
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-      const int g = base + jj + 32 * i;
+      const int g = base + jj + JJ * i;
       if (g < G) {
         accg += group_term<ACT>(group_dot<ACT>(qg0[i], qg1[i], S, g), sg[i], S.xs[g], 128.f);
         accu += group_term<ACT>(group_dot<ACT>(qu0[i], qu1[i], S, g), su[i], S.xs[g], 128.f);
       }
     }
   }
-  accg = xor_sum(accg, 8, 32);
-  accu = xor_sum(accu, 8, 32);
-  if ((tid & 63) < 8) {
-    S.red[(tid >> 6) * 16 + r * 2] = accg;
-    S.red[(tid >> 6) * 16 + r * 2 + 1] = accu;
+  accg = xor_sum(accg, ROWS, 32);  // lanes r, r + ROWS, ... of a wavefront
+  accu = xor_sum(accu, ROWS, 32);
+  if ((tid & 63) < ROWS) {
+    S.red[(tid >> 6) * 2 * ROWS + r * 2] = accg;
+    S.red[(tid >> 6) * 2 * ROWS + r * 2 + 1] = accu;
   }
   __syncthreads();
-  if (tid < 8) {
-    const float gsum = (S.red[r * 2] + S.red[16 + r * 2]) + (S.red[32 + r * 2] + S.red[48 + r * 2]);
-    const float usum = (S.red[r * 2 + 1] + S.red[16 + r * 2 + 1]) + (S.red[32 + r * 2 + 1] + S.red[48 + r * 2 + 1]);
+  if (tid < ROWS) {
+    constexpr int W = 2 * ROWS;  // one wavefront's partials
+    const float gsum = (S.red[r * 2] + S.red[W + r * 2]) + (S.red[2 * W + r * 2] + S.red[3 * W + r * 2]);
+    const float usum =
+        (S.red[r * 2 + 1] + S.red[W + r * 2 + 1]) + (S.red[2 * W + r * 2 + 1] + S.red[3 * W + r * 2 + 1]);
     store_a<ACT>(abuf_of(a, t, ACT), apos + row, silu(gsum) * usum);
   }
 }
@@ -306,6 +312,29 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Radix search for the K-th largest key over the wavefront's NE keys per lane:
+// returns a value P with at least K keys >= P and, below every key >= P that
+// is not equal to P, fewer than K keys.  Bits are decided from the top; the
+// search stops as soon as exactly K keys are >= P (then any key >= P is chosen
+// and ties cannot cross P), which for distinct logits happens after a few
+// bits instead of all 32.
+template <int NE>
+__device__ __forceinline__ uint32_t kth_prefix(const uint32_t (&key)[NE], int K) {
+  uint32_t prefix = 0;
+  int c = 64 * NE;  // keys >= prefix
+  for (int bit = 31; bit >= 0 && c != K; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= K) {
+      prefix = cand;
+      c = cnt;
+    }
+  }
+  return prefix;
 }
 
 // Softmax top-K of token t by one wavefront (lane = threadIdx.x & 63).
@@ -353,14 +382,7 @@ __device__ void topk_wave(const LayerArgs& a, int t, const float* lt, int* id_ou
       lv[i] = ok ? lt[e] : -INFINITY;
       key[i] = ok ? order_key(lv[i]) : 0u;
     }
-    uint32_t prefix = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = prefix | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < NE; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-      if (cnt >= K) prefix = cand;
-    }
+    const uint32_t prefix = kth_prefix<NE>(key, K);
     int gt = 0;
 #pragma unroll
     for (int i = 0; i < NE; ++i) gt += __popcll(__ballot(key[i] > prefix));
@@ -426,15 +448,7 @@ __device__ int topk_kth(const LayerArgs& a, int t, const float* lt, int k) {
     const int e = lane + 64 * i;
     key[i] = (e < E) ? order_key(lt[e]) : 0u;
   }
-  uint32_t prefix = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = prefix | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < NE; ++i)
-      cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= K) prefix = cand;
-  }
+  const uint32_t prefix = kth_prefix<NE>(key, K);
   int gt = 0;
 #pragma unroll
   for (int i = 0; i < NE; ++i) gt += __popcll(__ballot(key[i] > prefix));
@@ -645,13 +659,11 @@ __device__ __forceinline__ void group_sums(const char* lds_a, float* asum, int N
 
 // Down GEMV of the shared and chosen experts for output rows 8*rb..8*rb+7 of
 // token t and the weighted combine.  sel[k] / wk_src[k]: blob address and
-// weight of the k-th chosen expert.  A_FIRST: the activation vector is
-// already complete, so its loads go out before the weights; otherwise the
-// weights go out first and `before_stage()` runs (it waits for the vector)
-// before the activations are read.
-template <int ACT, int MAXI, bool A_FIRST, class Hook>
+// weight of the k-th chosen expert.  The activation vector is complete, so
+// its loads go out before the weights.
+template <int ACT, int MAXI>
 __device__ void down_block(const LayerArgs& a, int t, int rb, const uint64_t* sel, const float* wk_src,
-                           char* smem, Hook&& before_stage) {
+                           char* smem) {
   const int tid = threadIdx.x, r = tid & 7, jj = tid >> 3;
   const int row = rb * 8 + r;
   const int Gs = a.fs >> 6, Gf = a.f >> 6, K = a.K;
@@ -665,10 +677,8 @@ __device__ void down_block(const LayerArgs& a, int t, int rb, const uint64_t* se
   const char* abuf_t = abuf_of(a, t, ACT);
   const int NW = F * (ACT == 1 ? 2 : 4) / 16;  // 16-byte words of the activation vector
   v4u ar[kAPre];
-  if (A_FIRST) {
 #pragma unroll
-    for (int i = 0; i < kAPre; ++i) ar[i] = ldg<v4u>(abuf_t + (size_t)min(tid + kThreads * i, NW - 1) * 16);
-  }
+  for (int i = 0; i < kAPre; ++i) ar[i] = ldg<v4u>(abuf_t + (size_t)min(tid + kThreads * i, NW - 1) * 16);
   float acc = 0.f;
   for (int base = 0; base < NI; base += 32 * MAXI) {
     v4u q0[MAXI], q1[MAXI];
@@ -695,30 +705,13 @@ __device__ void down_block(const LayerArgs& a, int t, int rb, const uint64_t* se
       sb[i] = ldg<uint32_t>(blob + osb + (((size_t)rb * G + g) * 8 + r) * 4);
     }
     if (base == 0) {
-      if (A_FIRST) {
 #pragma unroll
-        for (int i = 0; i < kAPre; ++i) {
-          const int j = tid + kThreads * i;
-          if (j < NW) reinterpret_cast<v4u*>(lds_a)[a_slot(j, WPG)] = ar[i];
-        }
-        for (int j = tid + kThreads * kAPre; j < NW; j += kThreads)
-          reinterpret_cast<v4u*>(lds_a)[a_slot(j, WPG)] = ldg<v4u>(abuf_t + (size_t)j * 16);
-      } else {  // written by other workgroups of this launch: device-coherent loads
-        before_stage();
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(abuf_t);
-        uint64_t* dst = reinterpret_cast<uint64_t*>(lds_a);
-        constexpr int kAD = 8;  // device-scope loads in flight per thread
-        for (int j0 = 0; j0 < 2 * NW; j0 += kThreads * kAD) {
-          uint64_t v[kAD];
-#pragma unroll
-          for (int i = 0; i < kAD; ++i) v[i] = ld_dev(src + min(j0 + tid + kThreads * i, 2 * NW - 1));
-#pragma unroll
-          for (int i = 0; i < kAD; ++i) {
-            const int j = j0 + tid + kThreads * i;
-            if (j < 2 * NW) dst[a_slot(j >> 1, WPG) * 2 + (j & 1)] = v[i];
-          }
-        }
+      for (int i = 0; i < kAPre; ++i) {
+        const int j = tid + kThreads * i;
+        if (j < NW) reinterpret_cast<v4u*>(lds_a)[a_slot(j, WPG)] = ar[i];
       }
+      for (int j = tid + kThreads * kAPre; j < NW; j += kThreads)
+        reinterpret_cast<v4u*>(lds_a)[a_slot(j, WPG)] = ldg<v4u>(abuf_t + (size_t)j * 16);
       if (tid < K) wk[tid] = wk_src[tid];
       __syncthreads();
       group_sums<ACT>(lds_a, asum, NI);
@@ -783,39 +776,47 @@ template <int ACT, int MAXI>
 __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int t = blockIdx.y;
-  down_block<ACT, MAXI, true>(a, t, blockIdx.x, a.sel_addr + (size_t)t * a.K, a.wts + (size_t)t * a.K, smem,
-                              [] {});
+  down_block<ACT, MAXI>(a, t, blockIdx.x, a.sel_addr + (size_t)t * a.K, a.wts + (size_t)t * a.K, smem);
 }
 
 // ---------------------------------------------------------------- fused layer
 // One launch per batch-1 bf16 layer on resident experts.  Workgroups, in
-// block order: router rows | shared gate/up | routed gate/up | down+combine.
-// A workgroup only waits for results of lower-numbered workgroups, and
-// workgroups are dispatched in block order within each XCD, so the lowest
-// unfinished workgroup can always run: no deadlock even when the grid does
-// not fit the GPU at once.  Waits are bounded spins (a timeout raises an
-// error flag and the workgroup carries on).
+// block order: router rows | shared gate/up | routed gate/up | down+combine;
+// gate/up workgroups take 16 rows, so that the whole grid of the common
+// shapes (868 workgroups for d_model 2816, 128 experts, top-8, d_ff 704)
+// fits the GPU at once and the down workgroups fetch their weights while the
+// routed experts stream.  A workgroup only waits for results of lower-
+// numbered workgroups, and workgroups are dispatched in block order within
+// each XCD, so the lowest unfinished workgroup can always run: no deadlock
+// even when the grid does not fit.  Waits are bounded spins (a timeout
+// raises an error flag and the workgroup carries on).
 //
 // Hand-offs.  Each launch has a tag (launch count + 1, read from the
 // synchronisation area).  Router wavefronts store their logit with the tag
 // into 64 replicas of a logit table; a routed gate/up or down workgroup polls
 // its replica (workgroup index % 64) until every entry carries this launch's
-// tag, so the logits need no counter.  Gate/up workgroups count their
-// arrivals (8 sub-counters, then a top counter; counters only grow, and a
-// phase is complete when a counter reaches tag * members); the arrival that
-// completes the phase sets 64 ready flags to the tag, and down workgroups
-// poll one flag each.  The last workgroup to finish publishes the next tag.
-// Every polled or counted word has its own cache line, 4160 bytes from the
-// next, so the hundreds of pollers spread over memory channels instead of
-// queueing on one address.  Nothing is reset between launches, so graph
-// replays need no memset.
+// tag, so the logits need no counter.  The gate/up results are counted in
+// phases: phase 0 = the shared expert, phase 1 + q = the q-th group of P
+// consecutive chosen experts (P = as many as fill 32 groups of the down
+// projection).  Arrivals go to 8 sub-counters, then a top counter; counters
+// only grow, and a phase is complete when a counter reaches tag * members.
+// The arrival that completes a phase sets the phase's ready flags to the tag.
+// Down workgroups load all their weights as soon as the routing is known,
+// then take the phases in order: wait for the flag, stage that part of the
+// activation vector, accumulate its groups.  Only the last phase's part is
+// left when the last gate/up workgroup finishes.  The last workgroup to
+// finish publishes the next tag.  Every polled or counted word has its own
+// cache line, 4160 bytes from the next, so the hundreds of pollers spread over
+// memory channels instead of queueing on one address.  Nothing is reset
+// between launches, so graph replays need no memset.
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kSyncStride = 4160 / 4;  // words between slots
-constexpr int kSyncSubs = 8, kSyncFlags = 64, kLogitReplicas = 64;
-constexpr int kSlotGateUp = 0;                                // subs, top, flags
-constexpr int kSlotDone = kSlotGateUp + kSyncSubs + 1 + kSyncFlags;  // subs, top
-constexpr int kSlotEpoch = kSlotDone + kSyncSubs + 1;         // replicas of the launch count
-constexpr int kSyncSlots = kSlotEpoch + kSyncFlags;
+constexpr int kSyncSubs = 8, kPhaseFlags = 16, kEpochReplicas = 64, kLogitReplicas = 64;
+constexpr int kPhaseSlots = kSyncSubs + 1 + kPhaseFlags;  // subs, top, flags
+constexpr int kMaxPhases = 9;                              // shared + up to 8 expert groups
+constexpr int kSlotDone = kMaxPhases * kPhaseSlots;        // subs, top
+constexpr int kSlotEpoch = kSlotDone + kSyncSubs + 1;      // replicas of the launch count
+constexpr int kSyncSlots = kSlotEpoch + kEpochReplicas;
 
 __host__ __device__ inline size_t logit_rep_stride(int E) {  // uint64 entries between replicas
   return ((size_t)E * 8 + 4095) / 4096 * 512 + 8;
@@ -823,6 +824,21 @@ __host__ __device__ inline size_t logit_rep_stride(int E) {  // uint64 entries b
 __host__ __device__ inline size_t sync_area_bytes(int E) {
   return (size_t)kSyncSlots * kSyncStride * 4 + (size_t)kLogitReplicas * logit_rep_stride(E) * 8;
 }
+
+// Down-projection phases: groups of the activation vector in phase p.
+struct DownPhases {
+  int Gs, Gf, K, P, NQ;  // shared groups, groups per expert, experts, experts per phase, expert phases
+  __host__ __device__ DownPhases(int fs, int f, int K_) : Gs(fs / 64), Gf(f / 64), K(K_) {
+    P = Gf >= 32 ? 1 : 32 / Gf;
+    NQ = (K + P - 1) / P;
+  }
+  __host__ __device__ int first(int p) const { return p == 0 ? 0 : Gs + (p - 1) * P * Gf; }
+  __host__ __device__ int count(int p) const {
+    if (p == 0) return Gs;
+    const int e0 = (p - 1) * P;
+    return (min(K, e0 + P) - e0) * Gf;
+  }
+};
 
 __device__ __forceinline__ uint32_t* sync_slot(uint32_t* area, int slot) {
   return area + (size_t)slot * kSyncStride;
@@ -838,29 +854,33 @@ __device__ __forceinline__ bool phase_count(uint32_t* area, int base, int i, int
   return atomicAdd(sync_slot(area, base + kSyncSubs), 1u) == tag * groups - 1u;
 }
 
-// Gate/up member i of n arrives after its device-scope stores completed.
-__device__ __forceinline__ void gate_up_arrive(uint32_t* area, int i, int n, uint32_t tag) {
+// Gate/up member i of n arrives in phase p after its device-scope stores
+// completed.
+__device__ __forceinline__ void gate_up_arrive(uint32_t* area, int p, int i, int n, uint32_t tag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x < 64) {
-    const bool last = threadIdx.x == 0 && phase_count(area, kSlotGateUp, i, n, tag);
-    if (__ballot(last)) st_dev(sync_slot(area, kSlotGateUp + kSyncSubs + 1 + (int)threadIdx.x), tag);
+    const int base = p * kPhaseSlots;
+    const bool last = threadIdx.x == 0 && phase_count(area, base, i, n, tag);
+    if (__ballot(last) && threadIdx.x < kPhaseFlags)
+      st_dev(sync_slot(area, base + kSyncSubs + 1 + (int)threadIdx.x), tag);
   }
 }
 
-__device__ __forceinline__ void gate_up_wait(const LayerArgs& a, uint32_t* area, uint32_t tag) {
-  if (threadIdx.x == 0) {
-    const uint32_t* flag = sync_slot(area, kSlotGateUp + kSyncSubs + 1 + (int)(blockIdx.x % kSyncFlags));
-    uint32_t it = 0;
-    while (ld_dev(flag) != tag) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++it == kSpinLimit) {
-        atomicOr(a.err, kErrSyncTimeout);
-        break;
-      }
+// Poll *p until (value >> SHIFT) == tag, one load in flight and a pause of
+// about 64 * SLEEP cycles between loads: hundreds of workgroups poll at once,
+// and their loads share the memory system with the weight stream.
+template <class T, int SHIFT, int SLEEP>
+__device__ __forceinline__ T poll_tag(const LayerArgs& a, const T* p, uint32_t tag, T v) {
+  for (uint32_t it = 0; (uint32_t)(v >> SHIFT) != tag; ++it) {
+    if (it == kSpinLimit) {
+      atomicOr(a.err, kErrSyncTimeout);
+      break;
     }
+    __builtin_amdgcn_s_sleep(SLEEP);
+    v = ld_dev(p);
   }
-  __syncthreads();  // the activations are then read with device-scope loads
+  return v;
 }
 
 // Copy this launch's logits from replica `rep` into LDS, polling each entry
@@ -874,18 +894,7 @@ __device__ __forceinline__ void stage_tagged_logits(const LayerArgs& a, const ui
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int e = threadIdx.x + kThreads * i;
-    if (e < a.E) {
-      uint32_t it = 0;
-      while ((uint32_t)(v[i] >> 32) != tag) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++it == kSpinLimit) {
-          atomicOr(a.err, kErrSyncTimeout);
-          break;
-        }
-        v[i] = ld_dev(rep + e);
-      }
-      s_logits[e] = __uint_as_float((uint32_t)v[i]);
-    }
+    if (e < a.E) s_logits[e] = __uint_as_float((uint32_t)poll_tag<uint64_t, 32, 2>(a, rep + e, tag, v[i]));
   }
   __syncthreads();
 }
@@ -899,15 +908,161 @@ __device__ __forceinline__ void finish_launch(uint32_t* area, int total, uint32_
   }
 }
 
+constexpr int kFusedGuRows = 16;  // gate/up rows per workgroup of the fused kernel
+
 __host__ __device__ inline int fused_groups(int E, int K, int d, int f, int fs, int* NR, int* NS, int* NG, int* ND) {
   *NR = (E + kWaves - 1) / kWaves;
-  *NS = fs / 8;
-  *NG = K * (f / 8);
+  *NS = fs / kFusedGuRows;
+  *NG = K * (f / kFusedGuRows);
   *ND = d / 8;
   return *NR + *NS + *NG + *ND;
 }
 
-template <int MAXI, int NE, int MAXID>
+// Stage groups [g0, g1) of the activation vector into LDS with device-
+// coherent loads (other workgroups of this launch wrote them), then their
+// group sums; ends with a workgroup barrier.
+__device__ __forceinline__ void stage_a_coherent(const LayerArgs& a, char* lds_a, float* asum, int g0, int g1) {
+  constexpr int WPG = a_words(1);
+  const int tid = threadIdx.x;
+  const uint64_t* src = static_cast<const uint64_t*>(a.abuf) + (size_t)g0 * WPG * 2;
+  uint64_t* dst = reinterpret_cast<uint64_t*>(lds_a);
+  const int nw = (g1 - g0) * WPG * 2;  // 8-byte units
+  constexpr int kAD = 8;
+  for (int j0 = 0; j0 < nw; j0 += kThreads * kAD) {
+    uint64_t v[kAD];
+#pragma unroll
+    for (int i = 0; i < kAD; ++i) v[i] = ld_dev(src + min(j0 + tid + kThreads * i, nw - 1));
+#pragma unroll
+    for (int i = 0; i < kAD; ++i) {
+      const int j = j0 + tid + kThreads * i;
+      if (j < nw) dst[a_slot(g0 * WPG + (j >> 1), WPG) * 2 + (j & 1)] = v[i];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < (g1 - g0) * WPG; i += kThreads) {
+    const v4u x = reinterpret_cast<const v4u*>(lds_a)[a_slot(g0 * WPG + i, WPG)];
+    float h[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      h[2 * m] = f16_to_f32((uint16_t)(x[m] & 0xFFFFu));
+      h[2 * m + 1] = f16_to_f32((uint16_t)(x[m] >> 16));
+    }
+    float sum = ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
+    sum = xor_sum(sum, 1, WPG / 2);
+    if ((i & (WPG - 1)) == 0) asum[g0 + i / WPG] = sum;
+  }
+  __syncthreads();
+}
+
+// Down projection of output rows 8*rb..8*rb+7 (see above) in two parts: the
+// shared expert's groups [0, Gs) as soon as the shared gate/up is done, then
+// the chosen experts' groups [Gs, NI) once every expert phase is done.  Lane
+// (r = tid & 7, jj = tid >> 3) owns row r and the groups jj + 32 i of each
+// part; SS + SR weight slots, all loaded before the first wait.
+template <int SS, int SR>
+__device__ void down_two_part(const LayerArgs& a, int rb, const uint64_t* sel, const float* s_w, char* smem,
+                              uint32_t* area, uint32_t tag) {
+  const int tid = threadIdx.x, r = tid & 7, jj = tid >> 3;
+  const DownPhases ph(a.fs, a.f, a.K);
+  const int Gs = ph.Gs, Gf = ph.Gf;
+  const int NI = Gs + a.K * Gf, NR = NI - Gs;
+  constexpr int WPG = a_words(1);
+  char* lds_a = smem;
+  float* asum = reinterpret_cast<float*>(smem + (size_t)NI * (WPG + 1) * 16);
+  float* red = asum + NI;
+  v4u q0[SS + SR], q1[SS + SR];
+  uint32_t sb[SS + SR];
+#pragma unroll
+  for (int s = 0; s < SS + SR; ++s) {  // every weight load goes out now, before any wait
+    const bool shared = s < SS;
+    const int li = jj + 32 * (shared ? s : s - SS);
+    const uint8_t* blob;
+    int G, g;
+    uint32_t oq, osb;
+    if (shared) {
+      g = min(li, max(Gs, 1) - 1);
+      blob = Gs > 0 ? a.shared_blob : reinterpret_cast<const uint8_t*>(sel[0]);
+      G = Gs > 0 ? Gs : Gf;
+      oq = Gs > 0 ? a.so.dq : a.ro.dq;
+      osb = Gs > 0 ? a.so.dsb : a.ro.dsb;
+    } else {
+      const int c = min(li, NR - 1);
+      const int k = c / Gf;
+      g = c - k * Gf;
+      G = Gf;
+      blob = reinterpret_cast<const uint8_t*>(sel[k]);
+      oq = a.ro.dq;
+      osb = a.ro.dsb;
+    }
+    const size_t off = (((size_t)rb * G + g) * 2) * 128 + r * 16;
+    q0[s] = ldg<v4u>(blob + oq + off);
+    q1[s] = ldg<v4u>(blob + oq + off + 128);
+    sb[s] = ldg<uint32_t>(blob + osb + (((size_t)rb * G + g) * 8 + r) * 4);
+  }
+  float acc = 0.f;
+  auto accumulate = [&](int s, int it) {
+    float pp = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4u q = h ? q1[s] : q0[s];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t w = q[m];
+        const v4u av = reinterpret_cast<const v4u*>(lds_a)[it * (WPG + 1) + h * 4 + m];
+        pp = dot2_f16(nib_pair<kMagicF16>(w, 0), av[0], pp);
+        pp = dot2_f16(nib_pair<kMagicF16>(w, 1), av[1], pp);
+        pp = dot2_f16(nib_pair<kMagicF16>(w, 2), av[2], pp);
+        pp = dot2_f16(nib_pair<kMagicF16>(w, 3), av[3], pp);
+      }
+    }
+    const float term = group_term<1>(pp, sb[s], asum[it], 1024.f);
+    const float wgt = (it < Gs) ? 1.f : s_w[(it - Gs) / Gf];
+    acc = fmaf(wgt, term, acc);
+  };
+  const int fl = kSyncSubs + 1 + (int)(blockIdx.x % kPhaseFlags);
+  if (Gs > 0) {  // shared part
+    if (threadIdx.x == 0) {
+      const uint32_t* flag = sync_slot(area, fl);
+      poll_tag<uint32_t, 0, 8>(a, flag, tag, ld_dev(flag));
+    }
+    __syncthreads();
+    stage_a_coherent(a, lds_a, asum, 0, Gs);
+#pragma unroll
+    for (int s = 0; s < SS; ++s)
+      if (jj + 32 * s < Gs) accumulate(s, jj + 32 * s);
+  }
+  // Routed part.  The last expert phase (its workgroups are dispatched last)
+  // is polled gently, then lane p of wavefront 0 checks phase p, all in one
+  // round trip when they are done.
+  if (threadIdx.x < 64) {
+    if (threadIdx.x == 0) {
+      const uint32_t* last = sync_slot(area, ph.NQ * kPhaseSlots + fl);
+      poll_tag<uint32_t, 0, 8>(a, last, tag, ld_dev(last));
+    }
+    const int p = 1 + (int)threadIdx.x;
+    if (p < ph.NQ) {
+      const uint32_t* flag = sync_slot(area, p * kPhaseSlots + fl);
+      poll_tag<uint32_t, 0, 2>(a, flag, tag, ld_dev(flag));
+    }
+  }
+  __syncthreads();
+  stage_a_coherent(a, lds_a, asum, Gs, NI);
+#pragma unroll
+  for (int s = 0; s < SR; ++s)
+    if (jj + 32 * s < NR) accumulate(SS + s, Gs + jj + 32 * s);
+  acc = xor_sum(acc, 8, 32);
+  if ((tid & 63) < 8) red[(tid >> 6) * 8 + r] = acc;
+  __syncthreads();
+  if (tid < 8) {
+    const float y = (red[r] + red[8 + r]) + (red[16 + r] + red[24 + r]);
+    const int row = rb * 8 + r;
+    float v = y;
+    if (a.resid) v += bf16_to_f32(static_cast<const uint16_t*>(a.resid)[row]);
+    static_cast<uint16_t*>(a.out)[row] = f32_to_bf16(v);
+  }
+}
+
+template <int MAXI, int NE, int SS, int SR>
 __global__ __launch_bounds__(kThreads) void fused_layer_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   __shared__ uint32_t scratch[128];
@@ -918,31 +1073,38 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(LayerArgs a) {
   const int total = fused_groups(a.E, a.K, a.d, a.f, a.fs, &NR, &NS, &NG, &ND);
   const int b = blockIdx.x;
   uint32_t* area = a.counter;
-  const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kSyncFlags)) + 1u;
+  const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kEpochReplicas)) + 1u;
   uint64_t* lrep = reinterpret_cast<uint64_t*>(area + (size_t)kSyncSlots * kSyncStride);
   const size_t rstride = logit_rep_stride(a.E);
   const XStage S = carve_x(smem, a.d);
   if (b < NR) {
+    __builtin_amdgcn_s_setprio(2);  // on the critical path: ahead of the streaming wavefronts
     router_row<1>(a, 0, b * kWaves + (threadIdx.x >> 6), S, lrep, rstride, tag);
   } else if (b < NR + NS) {
     XRegs xr;
     x_issue<1>(a, 0, xr);
-    gate_up_block<1, MAXI>(a, 0, a.shared_blob, a.so, b - NR, 0, S, xr);
-    gate_up_arrive(area, b - NR, NS + NG, tag);
+    gate_up_block<1, MAXI, kFusedGuRows>(a, 0, a.shared_blob, a.so, b - NR, 0, S, xr);
+    gate_up_arrive(area, 0, b - NR, NS, tag);
   } else if (b < NR + NS + NG) {
-    const int g = b - NR - NS, RB = a.f >> 3;
+    const int g = b - NR - NS, RB = a.f / kFusedGuRows;
     const int k = g / RB, rb = g - k * RB;
+    const DownPhases ph(a.fs, a.f, a.K);
     XRegs xr;
     x_issue<1>(a, 0, xr);
+    __builtin_amdgcn_s_setprio(2);
     stage_tagged_logits(a, lrep + (size_t)(b % kLogitReplicas) * rstride, tag, s_logits);
     if (threadIdx.x < 64) {  // one wavefront finds the expert
       const int id = topk_kth<NE>(a, 0, s_logits, k);
       if (threadIdx.x == 0) scratch[0] = (uint32_t)id;
     }
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
     const int id = (int)scratch[0];
-    gate_up_block<1, MAXI>(a, 0, a.expert_base + (size_t)id * a.expert_stride, a.ro, rb, a.fs + k * a.f, S, xr);
-    gate_up_arrive(area, b - NR, NS + NG, tag);
+    gate_up_block<1, MAXI, kFusedGuRows>(a, 0, a.expert_base + (size_t)id * a.expert_stride, a.ro, rb,
+                                         a.fs + k * a.f, S, xr);
+    const int q = k / ph.P;  // expert phase
+    const int members = (min(a.K, (q + 1) * ph.P) - q * ph.P) * RB;
+    gate_up_arrive(area, 1 + q, (k - q * ph.P) * RB + rb, members, tag);
   } else {
     const int rb = b - NR - NS - NG;
     stage_tagged_logits(a, lrep + (size_t)(b % kLogitReplicas) * rstride, tag, s_logits);
@@ -957,8 +1119,10 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(LayerArgs a) {
       if (rb == 0) publish_routing(a, 0, threadIdx.x, id, w);
     }
     __syncthreads();
-    down_block<1, MAXID, false>(a, 0, rb, s_sel, s_w, smem, [&] { gate_up_wait(a, area, tag); });
+    __builtin_amdgcn_s_setprio(2);
+    down_two_part<SS, SR>(a, rb, s_sel, s_w, smem, area, tag);
   }
+  __builtin_amdgcn_s_setprio(0);
   finish_launch(area, total, tag);
 }
 
@@ -1023,22 +1187,35 @@ size_t fused_lds_bytes(const LayerArgs& a) {
   return std::max(x_stage_bytes(a.d), down_lds_bytes(F, NI, a.K, 1));
 }
 
-template <int NE, int MAXI>
-hipError_t launch_fused_mi(const LayerArgs& a, hipStream_t s) {
+template <int NE, int MAXI, int SS, int SR>
+hipError_t launch_fused_k(const LayerArgs& a, hipStream_t s) {
   int NR, NS, NG, ND;
   const int total = fused_groups(a.E, a.K, a.d, a.f, a.fs, &NR, &NS, &NG, &ND);
-  const int NI = a.fs / 64 + a.K * (a.f / 64);
-  const size_t lds = fused_lds_bytes(a);
-  if (NI <= 128)
-    launch_timed(a.prof, kKFusedLayer, fused_layer_kernel<MAXI, NE, 4>, dim3(total), dim3(kThreads), lds, s, a);
-  else
-    launch_timed(a.prof, kKFusedLayer, fused_layer_kernel<MAXI, NE, 8>, dim3(total), dim3(kThreads), lds, s, a);
+  launch_timed(a.prof, kKFusedLayer, fused_layer_kernel<MAXI, NE, SS, SR>, dim3(total), dim3(kThreads),
+               fused_lds_bytes(a), s, a);
   return hipGetLastError();
 }
 
+// Weight slots of a down workgroup: ceil(Gs / 32) for the shared part (0..2)
+// and ceil(K * Gf / 32) for the routed part (1..4).
+template <int NE, int MAXI>
+hipError_t launch_fused_mi(const LayerArgs& a, hipStream_t s) {
+  const int ss = (a.fs / 64 + 31) / 32, sr = (a.K * (a.f / 64) + 31) / 32;
+  const int code = (ss <= 1 ? ss : 2) * 8 + (sr <= 2 ? 2 : 4);
+  switch (code) {
+    case 2: return launch_fused_k<NE, MAXI, 0, 2>(a, s);
+    case 4: return launch_fused_k<NE, MAXI, 0, 4>(a, s);
+    case 10: return launch_fused_k<NE, MAXI, 1, 2>(a, s);
+    case 12: return launch_fused_k<NE, MAXI, 1, 4>(a, s);
+    case 18: return launch_fused_k<NE, MAXI, 2, 2>(a, s);
+    default: return launch_fused_k<NE, MAXI, 2, 4>(a, s);
+  }
+}
+
+// Gate/up weight slots per lane: ceil(G / 16) with 16 lanes per row (1..4).
 template <int NE>
 hipError_t launch_fused_ne(const LayerArgs& a, hipStream_t s) {
-  const int maxi = (a.d / 64 + 31) / 32;
+  const int maxi = (a.d / 64 + kThreads / kFusedGuRows - 1) / (kThreads / kFusedGuRows);
   if (maxi <= 1) return launch_fused_mi<NE, 1>(a, s);
   if (maxi == 2) return launch_fused_mi<NE, 2>(a, s);
   if (maxi == 3) return launch_fused_mi<NE, 3>(a, s);
@@ -1060,8 +1237,13 @@ size_t decode_lds_bytes_down(int F, int NI, int K, int act) { return down_lds_by
 
 // The fused layer kernel serves one bf16 token on resident experts, when its
 // LDS (dynamic part plus about 6 KB of static routing state) fits in 64 KB.
+// The down workgroups hold at most 2 shared and 4 routed weight slots (64 and
+// 128 groups), the gate/up workgroups at most 4 (d_model <= 4096), and the
+// expert phases fit the synchronisation area.
 bool decode_fused_ok(const LayerArgs& a) {
-  return a.T == 1 && a.act == 1 && a.E <= 1024 && fused_lds_bytes(a) + 6 * 1024 <= 64 * 1024;
+  const DownPhases ph(a.fs, a.f, a.K);
+  return a.T == 1 && a.act == 1 && a.E <= 1024 && a.d <= 4096 && fused_lds_bytes(a) + 6 * 1024 <= 64 * 1024 &&
+         ph.Gs <= 64 && a.K * ph.Gf <= 128 && ph.NQ + 1 <= kMaxPhases;
 }
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s) {

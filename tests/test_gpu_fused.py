@@ -1,7 +1,8 @@
-"""Single-launch decode kernel: parity with the fp64 oracle, bit identity with
-the three-kernel decode path (same arithmetic in the same order), repeated
-launches and graph replays (its cross-workgroup counters reset themselves),
-and the cases it must refuse."""
+"""Single-launch decode kernel: parity with the fp64 oracle, agreement with
+the three-kernel decode path (same routing bit for bit; outputs equal up to
+the fp32 summation order of the down projection, which the fused kernel
+takes phase by phase), repeated launches and graph replays (its
+cross-workgroup counters need no reset), and the cases it must refuse."""
 import numpy as np
 import pytest
 
@@ -22,9 +23,13 @@ def decode_layer():
     gl.close()
 
 
-def _same(a, b):
-    for u, v in zip(a, b):
-        assert np.array_equal(u, v)
+def _agree(fused, split):
+    """Identical expert sets and weights; outputs within a few bf16 ulps."""
+    assert np.array_equal(fused[1], split[1])
+    assert np.array_equal(fused[2], split[2])
+    yf, ys = O.tokens_to_f64(fused[0]), O.tokens_to_f64(split[0])
+    rms = np.sqrt(np.mean(ys * ys, axis=-1, keepdims=True))
+    assert np.all(np.abs(yf - ys) <= 2.0 ** -7 * np.abs(ys) + 1e-3 * rms), np.abs(yf - ys).max()
 
 
 def test_fused_decode_layer_tokens(decode_layer):
@@ -34,7 +39,7 @@ def test_fused_decode_layer_tokens(decode_layer):
     for t in range(16):
         got = gl.forward(x[t:t + 1], path=M.MOE_PATH_FUSED)
         worst = max(worst, check_layer(gl, OL, x[t:t + 1], *got))
-        _same(got, gl.forward(x[t:t + 1], path=M.MOE_PATH_DECODE))
+        _agree(got, gl.forward(x[t:t + 1], path=M.MOE_PATH_DECODE))
     print(f"fused: worst rel L2 over 16 tokens {worst:.3e}")
     assert M.moe_layer_check_errors(gl.handle) == 0
 
@@ -55,7 +60,7 @@ SHAPES = [  # (d, E, K, f, fs): one expert, no shared expert, K = E, E > 256, ra
     (1088, 17, 4, 192, 128),
     (512, 300, 9, 64, 0),
     (2048, 256, 8, 512, 512),
-    (4160, 8, 2, 128, 64),
+    (4096, 8, 2, 128, 64),
     (256, 64, 64, 64, 64),
 ]
 
@@ -71,7 +76,7 @@ def test_fused_shapes(shape):
     for t in range(4):
         got = gl.forward(x[t:t + 1], path=M.MOE_PATH_FUSED)
         check_layer(gl, OL, x[t:t + 1], *got)
-        _same(got, gl.forward(x[t:t + 1], path=M.MOE_PATH_DECODE))
+        _agree(got, gl.forward(x[t:t + 1], path=M.MOE_PATH_DECODE))
     assert M.moe_layer_check_errors(gl.handle) == 0
     gl.close()
 
@@ -120,7 +125,7 @@ def test_fused_forced_and_reused(decode_layer):
     check_layer(gl, OL, x[:1], *got, forced=forced)
     got2 = gl.forward(x[1:2], path=M.MOE_PATH_FUSED, reuse=True)
     check_layer(gl, OL, x[1:2], *got2, forced=forced)
-    _same(got2, gl.forward(x[1:2], path=M.MOE_PATH_DECODE, forced=forced))
+    _agree(got2, gl.forward(x[1:2], path=M.MOE_PATH_DECODE, forced=forced))
     assert M.moe_layer_check_errors(gl.handle) == 0
 
 
@@ -142,3 +147,9 @@ def test_fused_refuses_what_it_does_not_serve(decode_layer):
     with pytest.raises(M.MoeError):  # fp32 activations
         g32.forward(make_tokens(wf, 1), path=M.MOE_PATH_FUSED)
     g32.close()
+    wd = Workload(83, "wide", d=4160, E=8, K=2, f=128, fs=64, act="bf16", zipf=1.0, T=1)
+    gwide = GpuLayer(wd, make_layer(wd), 1)
+    with pytest.raises(M.MoeError):  # d_model above 4096
+        gwide.forward(make_tokens(wd, 1), path=M.MOE_PATH_FUSED)
+    gwide.forward(make_tokens(wd, 1))  # AUTO falls back to the three-kernel path
+    gwide.close()
