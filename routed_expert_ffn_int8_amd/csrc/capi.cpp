@@ -20,6 +20,7 @@
 
 namespace moe {
 size_t decode_lds_bytes_x(int d);
+size_t decode_abuf_bytes(int T, int F);
 size_t decode_lds_bytes_down(int F, int NI, int K, int act);
 size_t prefill_workspace_bytes(int T, int d, int E, int K, int f, int fs);
 void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, int fs);
@@ -300,7 +301,7 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
   const size_t F = L->fs + K * L->f;
   if (dalloc(&L->d_logits, T * E * 4) != hipSuccess || dalloc(&L->d_ids, T * K * 4) != hipSuccess ||
       dalloc(&L->d_wts, T * K * 4) != hipSuccess || dalloc(&L->d_sel, T * K * 8) != hipSuccess || dalloc(&L->d_counter, decode_sync_bytes(L->E)) != hipSuccess ||
-      dalloc(&L->d_abuf, T * F * 4) != hipSuccess ||
+      dalloc(&L->d_abuf, decode_abuf_bytes((int)T, (int)F)) != hipSuccess ||
       dalloc(&L->d_err, 64) != hipSuccess)
     return fail(MOE_ERR_NOMEM, "decode workspace alloc failed");
   HIP_OK(hipMemset(L->d_ids, 0, T * K * 4));

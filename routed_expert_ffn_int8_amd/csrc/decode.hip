@@ -58,6 +58,30 @@ template <class T>
 __device__ __forceinline__ T ld_dev(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The same coherence for 16-byte words: buffer loads/stores with the sc1
+// cache-policy bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ v4u ld_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+}
+__device__ __forceinline__ void st_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off, v4u v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSc1);
+}
+
+// The fused kernel keeps kAReps copies of the intermediate activation vector,
+// a_rep_stride(F) bytes apart, so that the hundreds of down workgroups
+// reading it spread over several copies and memory channels.  Each value is
+// one 32-bit word: fp16 bits << 16 | the low 16 bits of the launch tag, so a
+// reader can tell a value of this launch from a stale one.
+constexpr int kAReps = 8;
+__host__ __device__ inline size_t a_rep_stride(int F) { return ((size_t)F * 4 + 4095) / 4096 * 4096 + 512; }
+__device__ __forceinline__ bool fresh4(const v4u& w, uint32_t t16) {
+  return ((w[0] & 0xFFFFu) == t16) & ((w[1] & 0xFFFFu) == t16) & ((w[2] & 0xFFFFu) == t16) &
+         ((w[3] & 0xFFFFu) == t16);
+}
 
 struct XStage {
   float* xf;   // [d] input as fp32 (after rounding to the activation type)
@@ -244,10 +268,12 @@ __device__ __forceinline__ char* abuf_of(const LayerArgs& a, int t, int act) {
 // activation vector.  Lane (r = tid % ROWS, jj = tid / ROWS) reads row r for
 // the groups jj + JJ i (JJ = 256 / ROWS): each wavefront load covers eight
 // whole 128-byte runs.  `xr` holds the token loads, issued by the caller
-// before it waited on anything, so they overlap the weight fetch.
-template <int ACT, int MAXI, int ROWS = 8>
+// before it waited on anything, so they overlap the weight fetch.  REPS
+// (bf16 only): the ROWS results, tagged with `tag`, go to every copy of the
+// fused kernel's activation vector in 16-byte stores.
+template <int ACT, int MAXI, int ROWS = 8, bool REPS = false>
 __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, const BlobOffsets& o, int rb,
-                              int apos, const XStage& S, const XRegs& xr) {
+                              int apos, const XStage& S, const XRegs& xr, uint32_t tag = 0) {
   constexpr int JJ = kThreads / ROWS;
   const int tid = threadIdx.x, r = tid % ROWS, jj = tid / ROWS;
   const int G = a.d >> 6;
@@ -294,7 +320,21 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
     const float gsum = (S.red[r * 2] + S.red[W + r * 2]) + (S.red[2 * W + r * 2] + S.red[3 * W + r * 2]);
     const float usum =
         (S.red[r * 2 + 1] + S.red[W + r * 2 + 1]) + (S.red[2 * W + r * 2 + 1] + S.red[3 * W + r * 2 + 1]);
-    store_a<ACT>(abuf_of(a, t, ACT), apos + row, silu(gsum) * usum);
+    const float v = silu(gsum) * usum;
+    if (REPS) {  // S.xf is free: the bf16 products read S.xp
+      reinterpret_cast<uint32_t*>(S.xf)[r] = ((uint32_t)f32_to_f16(v) << 16) | (tag & 0xFFFFu);
+    } else {
+      store_a<ACT>(abuf_of(a, t, ACT), apos + row, v);
+    }
+  }
+  if (REPS) {
+    __syncthreads();
+    constexpr int CH = ROWS / 4;  // 16-byte words of this row block
+    if (tid < CH * kAReps) {
+      const int c = tid % CH, q = tid / CH;
+      const size_t off = (size_t)q * a_rep_stride(a.fs + a.K * a.f) + (size_t)(apos + rb * ROWS) * 4 + c * 16;
+      st_dev16(buf_rsrc(a.abuf), (uint32_t)off, reinterpret_cast<const v4u*>(S.xf)[c]);
+    }
   }
 }
 
@@ -505,13 +545,11 @@ __device__ __forceinline__ void publish_routing(const LayerArgs& a, int t, int l
 constexpr int kRouterPre = 8;  // 16-byte router chunks per lane issued up front (d <= 8192)
 constexpr int kWaves = kThreads / 64;
 
-// Logit of router row e for token t by one wavefront (e >= E: no store).
-// rep == nullptr: store to the logits array.  Otherwise lane j stores the
-// logit, tagged with `tag` in the high word, to entry e of replica j of the
-// tagged table (replicas `rstride` entries apart).
+// Logit of router row e for token t by one wavefront (rows e >= E repeat
+// row E-1); every lane returns it.  The row's scale and bias are loaded with
+// the weights, before the token is waited for.
 template <int ACT>
-__device__ void router_row(const LayerArgs& a, int t, int e, const XStage& S, uint64_t* rep = nullptr,
-                           size_t rstride = 0, uint32_t tag = 0) {
+__device__ float router_row(const LayerArgs& a, int t, int e, const XStage& S) {
   const int lane = threadIdx.x & 63;
   const int ec = min(e, a.E - 1);
   const int NC = a.d >> 4;  // 16-byte chunks per router row
@@ -521,6 +559,8 @@ __device__ void router_row(const LayerArgs& a, int t, int e, const XStage& S, ui
   v4u wr[kRouterPre];
 #pragma unroll
   for (int i = 0; i < kRouterPre; ++i) wr[i] = ldg<v4u>(wrow + (size_t)min(lane + 64 * i, NC - 1) * 16);
+  const float s = f16_to_f32(ldg<uint16_t>(a.router_scale + ec));
+  const float b = a.router_bias ? ldg<float>(a.router_bias + ec) : 0.f;
   x_commit<ACT>(a, t, xr, S);
   float acc = 0.f;
 #pragma unroll
@@ -540,15 +580,7 @@ __device__ void router_row(const LayerArgs& a, int t, int e, const XStage& S, ui
     }
   }
   acc = xor_sum(acc, 1, 32);  // every lane holds the same sum
-  if (e < a.E) {
-    const float s = f16_to_f32(a.router_scale[e]);
-    const float b = a.router_bias ? a.router_bias[e] : 0.f;
-    const float v = fmaf(s, acc, b);
-    if (rep)
-      st_dev(rep + (size_t)lane * rstride + e, ((uint64_t)tag << 32) | __float_as_uint(v));
-    else if (lane == 0)
-      a.logits[(size_t)t * a.E + e] = v;
-  }
+  return fmaf(s, acc, b);
 }
 
 template <int ACT, int MAXI>
@@ -563,7 +595,9 @@ __global__ __launch_bounds__(kThreads) void route_shared_kernel(LayerArgs a) {
     gate_up_block<ACT, MAXI>(a, t, a.shared_blob, a.so, blockIdx.x - NR, 0, S, xr);
     return;
   }
-  router_row<ACT>(a, t, blockIdx.x * kWaves + (threadIdx.x >> 6), S);
+  const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const float v = router_row<ACT>(a, t, e, S);
+  if (e < a.E && (threadIdx.x & 63) == 0) a.logits[(size_t)t * a.E + e] = v;
 }
 
 // Stand-alone top-K (one wavefront per token), used when the routing must be
@@ -782,133 +816,141 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
 // ---------------------------------------------------------------- fused layer
 // One launch per batch-1 bf16 layer on resident experts.  Workgroups, in
 // block order: router rows | shared gate/up | routed gate/up | down+combine;
-// gate/up workgroups take 16 rows, so that the whole grid of the common
-// shapes (868 workgroups for d_model 2816, 128 experts, top-8, d_ff 704)
-// fits the GPU at once and the down workgroups fetch their weights while the
-// routed experts stream.  A workgroup only waits for results of lower-
-// numbered workgroups, and workgroups are dispatched in block order within
-// each XCD, so the lowest unfinished workgroup can always run: no deadlock
-// even when the grid does not fit.  Waits are bounded spins (a timeout
+// gate/up workgroups take 16 rows.  A workgroup only waits for results of
+// lower-numbered workgroups, and workgroups are dispatched in block order, so
+// the lowest unfinished workgroup can always run: no deadlock even when the
+// grid does not fit the GPU at once.  Waits are bounded spins (a timeout
 // raises an error flag and the workgroup carries on).
 //
-// Hand-offs.  Each launch has a tag (launch count + 1, read from the
-// synchronisation area).  Router wavefronts store their logit with the tag
-// into 64 replicas of a logit table; a routed gate/up or down workgroup polls
-// its replica (workgroup index % 64) until every entry carries this launch's
-// tag, so the logits need no counter.  The gate/up results are counted in
-// phases: phase 0 = the shared expert, phase 1 + q = the q-th group of P
-// consecutive chosen experts (P = as many as fill 32 groups of the down
-// projection).  Arrivals go to 8 sub-counters, then a top counter; counters
-// only grow, and a phase is complete when a counter reaches tag * members.
-// The arrival that completes a phase sets the phase's ready flags to the tag.
-// Down workgroups load all their weights as soon as the routing is known,
-// then take the phases in order: wait for the flag, stage that part of the
-// activation vector, accumulate its groups.  Only the last phase's part is
-// left when the last gate/up workgroup finishes.  The last workgroup to
-// finish publishes the next tag.  Every polled or counted word has its own
-// cache line, 4160 bytes from the next, so the hundreds of pollers spread over
-// memory channels instead of queueing on one address.  Nothing is reset
-// between launches, so graph replays need no memset.
+// Hand-offs go through counters that only grow.  Each launch has a tag (the
+// launch count + 1, read from an epoch word); a stage is complete when its
+// counter has grown by its number of producer workgroups to tag * members.
+// A producer stores its results with device-scope stores, waits until they
+// are done, then adds one to each of the counter's 8 replicas; a consumer
+// polls the replica of its own index with a single lane, so a few hundred
+// pollers spread over 8 addresses instead of flooding one.
+//   router rows    -> logits (64 replicas of the table)     + router counter
+//   shared gate/up -> shared part of the activation vector  + shared counter
+//   routed gate/up -> routed part of the activation vector  + routed counter
+// Routed gate/up and down workgroups run the top-K themselves on the staged
+// logits.  Down workgroups fetch the shared expert's down weights at once and
+// the chosen experts' as soon as the routing is known.  They are also the
+// last to need the tag: each counts itself once it has seen the routed
+// counter complete, and the last one publishes the tag as the new epoch while
+// the others still compute, so the next launch needs no reset and the end of
+// this one waits for nothing.  Every counter word has its own cache lines
+// (4160 bytes apart).
 constexpr uint32_t kSpinLimit = 1u << 22;
-constexpr int kSyncStride = 4160 / 4;  // words between slots
-constexpr int kSyncSubs = 8, kPhaseFlags = 16, kEpochReplicas = 64, kLogitReplicas = 64;
-constexpr int kPhaseSlots = kSyncSubs + 1 + kPhaseFlags;  // subs, top, flags
-constexpr int kMaxPhases = 9;                              // shared + up to 8 expert groups
-constexpr int kSlotDone = kMaxPhases * kPhaseSlots;        // subs, top
-constexpr int kSlotEpoch = kSlotDone + kSyncSubs + 1;      // replicas of the launch count
-constexpr int kSyncSlots = kSlotEpoch + kEpochReplicas;
+constexpr int kSyncStride = 4160 / 4;  // words between counter words
+constexpr int kReps = 8;               // replicas of each polled counter
+constexpr int kEpochReps = 64, kLogitReplicas = 64;
+enum : int { kCntRouter = 0, kCntShared = 1, kCntRouted = 2, kCntDoneSub = 3, kCntDoneTop = 4, kNumCnt = 5 };
+constexpr int kSlotEpoch = kNumCnt * kReps;  // kEpochReps words
+constexpr int kSyncSlots = kSlotEpoch + kEpochReps;
 
-__host__ __device__ inline size_t logit_rep_stride(int E) {  // uint64 entries between replicas
-  return ((size_t)E * 8 + 4095) / 4096 * 512 + 8;
-}
+// Logit table entries: tag << 32 | fp32 bits.  Entries between replicas (the
+// table rounded up to 4 KB, so 4-entry runs of the last router rows fit, plus
+// 64 bytes to spread the replicas over channels).
+__host__ __device__ inline size_t logit_rep_stride(int E) { return ((size_t)E * 8 + 4095) / 4096 * 512 + 8; }
 __host__ __device__ inline size_t sync_area_bytes(int E) {
   return (size_t)kSyncSlots * kSyncStride * 4 + (size_t)kLogitReplicas * logit_rep_stride(E) * 8;
 }
 
-// Down-projection phases: groups of the activation vector in phase p.
-struct DownPhases {
-  int Gs, Gf, K, P, NQ;  // shared groups, groups per expert, experts, experts per phase, expert phases
-  __host__ __device__ DownPhases(int fs, int f, int K_) : Gs(fs / 64), Gf(f / 64), K(K_) {
-    P = Gf >= 32 ? 1 : 32 / Gf;
-    NQ = (K + P - 1) / P;
-  }
-  __host__ __device__ int first(int p) const { return p == 0 ? 0 : Gs + (p - 1) * P * Gf; }
-  __host__ __device__ int count(int p) const {
-    if (p == 0) return Gs;
-    const int e0 = (p - 1) * P;
-    return (min(K, e0 + P) - e0) * Gf;
-  }
-};
-
 __device__ __forceinline__ uint32_t* sync_slot(uint32_t* area, int slot) {
   return area + (size_t)slot * kSyncStride;
 }
-
-// Member i of n arrives in the phase whose slots start at `base`; true (in
-// the calling lane) for the arrival that completes the phase.
-__device__ __forceinline__ bool phase_count(uint32_t* area, int base, int i, int n, uint32_t tag) {
-  const int j = i % kSyncSubs;
-  const uint32_t need = (uint32_t)((n - j + kSyncSubs - 1) / kSyncSubs);
-  if (atomicAdd(sync_slot(area, base + j), 1u) != tag * need - 1u) return false;
-  const uint32_t groups = (uint32_t)min(n, kSyncSubs);
-  return atomicAdd(sync_slot(area, base + kSyncSubs), 1u) == tag * groups - 1u;
+__device__ __forceinline__ uint32_t* counter_rep(uint32_t* area, int c, int r) {
+  return sync_slot(area, c * kReps + r);
 }
 
-// Gate/up member i of n arrives in phase p after its device-scope stores
-// completed.
-__device__ __forceinline__ void gate_up_arrive(uint32_t* area, int p, int i, int n, uint32_t tag) {
-  __builtin_amdgcn_s_waitcnt(0);
+// Called by every thread once the workgroup's tagged device-scope stores have
+// been issued: adds one to every replica of counter c (lanes 0..7, no return
+// value).  The stores are not waited for: a consumer that sees the counter
+// complete reads the data and re-reads any word whose tag is not yet this
+// launch's.
+__device__ __forceinline__ void arrive(uint32_t* area, int c) {
   __syncthreads();
-  if (threadIdx.x < 64) {
-    const int base = p * kPhaseSlots;
-    const bool last = threadIdx.x == 0 && phase_count(area, base, i, n, tag);
-    if (__ballot(last) && threadIdx.x < kPhaseFlags)
-      st_dev(sync_slot(area, base + kSyncSubs + 1 + (int)threadIdx.x), tag);
-  }
+  if (threadIdx.x < kReps)
+    __hip_atomic_fetch_add(counter_rep(area, c, threadIdx.x), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Poll *p until (value >> SHIFT) == tag, one load in flight and a pause of
-// about 64 * SLEEP cycles between loads: hundreds of workgroups poll at once,
-// and their loads share the memory system with the weight stream.
-template <class T, int SHIFT, int SLEEP>
-__device__ __forceinline__ T poll_tag(const LayerArgs& a, const T* p, uint32_t tag, T v) {
-  for (uint32_t it = 0; (uint32_t)(v >> SHIFT) != tag; ++it) {
-    if (it == kSpinLimit) {
-      atomicOr(a.err, kErrSyncTimeout);
-      break;
+// Lane 0 polls replica (workgroup % 8) of counter c until it reaches
+// `target` (wrap-safe), pausing about 64 * SLEEP cycles between loads; ends
+// with a workgroup barrier.
+template <int SLEEP>
+__device__ __forceinline__ void wait_count(const LayerArgs& a, uint32_t* area, int c, uint32_t target) {
+  if (threadIdx.x == 0) {
+    const uint32_t* p = counter_rep(area, c, blockIdx.x % kReps);
+    uint32_t v = ld_dev(p);
+    for (uint32_t it = 0; (int32_t)(v - target) < 0; ++it) {
+      if (it == kSpinLimit) {
+        atomicOr(a.err, kErrSyncTimeout);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(SLEEP);
+      v = ld_dev(p);
     }
-    __builtin_amdgcn_s_sleep(SLEEP);
-    v = ld_dev(p);
   }
-  return v;
+  __syncthreads();
 }
 
-// Copy this launch's logits from replica `rep` into LDS, polling each entry
-// until it carries `tag`; ends with a workgroup barrier.
-__device__ __forceinline__ void stage_tagged_logits(const LayerArgs& a, const uint64_t* rep, uint32_t tag,
-                                                    float* s_logits) {
-  constexpr int N = (1024 + kThreads - 1) / kThreads;
+// Copy the logits of this launch from replica `rep` (the router counter was
+// seen complete) into LDS with device-coherent loads, re-reading entries
+// whose tag is still a previous launch's; ends with a workgroup barrier.
+template <int NE>
+__device__ __forceinline__ void stage_logits_dev(const LayerArgs& a, const uint64_t* rep, uint32_t tag,
+                                                 float* s_logits) {
+  constexpr int N = (64 * NE + kThreads - 1) / kThreads;
   uint64_t v[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = ld_dev(rep + min((int)threadIdx.x + kThreads * i, a.E - 1));
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int e = threadIdx.x + kThreads * i;
-    if (e < a.E) s_logits[e] = __uint_as_float((uint32_t)poll_tag<uint64_t, 32, 2>(a, rep + e, tag, v[i]));
+    if (e < a.E) {
+      for (uint32_t it = 0; (uint32_t)(v[i] >> 32) != tag; ++it) {
+        if (it == kSpinLimit) {
+          atomicOr(a.err, kErrSyncTimeout);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v[i] = ld_dev(rep + e);
+      }
+      s_logits[e] = __uint_as_float((uint32_t)v[i]);
+    }
   }
   __syncthreads();
 }
 
-// Every workgroup arrives here last; the final one publishes the next tag.
-__device__ __forceinline__ void finish_launch(uint32_t* area, int total, uint32_t tag) {
-  __syncthreads();
+// Down workgroup i of n has passed its last wait of this launch; the last of
+// them publishes `tag` as the epoch the next launch starts from.  Wavefront 0.
+__device__ __forceinline__ void done_with_tag(uint32_t* area, int i, int n, uint32_t tag) {
   if (threadIdx.x < 64) {
-    const bool last = threadIdx.x == 0 && phase_count(area, kSlotDone, blockIdx.x, total, tag);
+    bool last = false;
+    if (threadIdx.x == 0) {
+      const int j = i % kReps;
+      const uint32_t need = (uint32_t)((n - j + kReps - 1) / kReps);
+      if (atomicAdd(counter_rep(area, kCntDoneSub, j), 1u) == tag * need - 1u) {
+        const uint32_t groups = (uint32_t)min(n, kReps);
+        last = atomicAdd(counter_rep(area, kCntDoneTop, 0), 1u) == tag * groups - 1u;
+      }
+    }
     if (__ballot(last)) st_dev(sync_slot(area, kSlotEpoch + (int)threadIdx.x), tag);
   }
 }
 
 constexpr int kFusedGuRows = 16;  // gate/up rows per workgroup of the fused kernel
+
+// Workgroups whose weight fetch does not wait for the routing (shared gate/up,
+// the shared part of the down projection) hold it back for a moment, so that
+// the router's loads, on the critical path, do not queue behind megabytes of
+// weights in the memory controllers.
+#ifndef MOE_FUSED_BULK_DELAY
+#define MOE_FUSED_BULK_DELAY 4
+#endif
+__device__ __forceinline__ void bulk_delay() {
+  for (int i = 0; i < MOE_FUSED_BULK_DELAY; ++i) __builtin_amdgcn_s_sleep(8);  // 512 cycles each
+}
 
 __host__ __device__ inline int fused_groups(int E, int K, int d, int f, int fs, int* NR, int* NS, int* NG, int* ND) {
   *NR = (E + kWaves - 1) / kWaves;
@@ -918,24 +960,46 @@ __host__ __device__ inline int fused_groups(int E, int K, int d, int f, int fs, 
   return *NR + *NS + *NG + *ND;
 }
 
-// Stage groups [g0, g1) of the activation vector into LDS with device-
-// coherent loads (other workgroups of this launch wrote them), then their
-// group sums; ends with a workgroup barrier.
-__device__ __forceinline__ void stage_a_coherent(const LayerArgs& a, char* lds_a, float* asum, int g0, int g1) {
+// Stage groups [g0, g1) of the activation vector (tagged words, written by
+// other workgroups of this launch) into LDS as fp16 pairs from this
+// workgroup's copy with device-coherent loads, re-reading words that still
+// carry an old tag; then their group sums.  Ends with a workgroup barrier.
+__device__ __forceinline__ void stage_a_coherent(const LayerArgs& a, char* lds_a, float* asum, int g0, int g1,
+                                                 uint32_t tag) {
   constexpr int WPG = a_words(1);
   const int tid = threadIdx.x;
-  const uint64_t* src = static_cast<const uint64_t*>(a.abuf) + (size_t)g0 * WPG * 2;
-  uint64_t* dst = reinterpret_cast<uint64_t*>(lds_a);
-  const int nw = (g1 - g0) * WPG * 2;  // 8-byte units
-  constexpr int kAD = 8;
+  const uint32_t t16 = tag & 0xFFFFu;
+  const auto rs = buf_rsrc(a.abuf);
+  const uint32_t base = (uint32_t)((blockIdx.x % kAReps) * a_rep_stride(a.fs + a.K * a.f) + (size_t)g0 * 64 * 4);
+  const int nw = (g1 - g0) * WPG;  // LDS words: 8 values = 32 bytes of tagged words each
+  constexpr int kAD = 3;
   for (int j0 = 0; j0 < nw; j0 += kThreads * kAD) {
-    uint64_t v[kAD];
+    v4u lo[kAD], hi[kAD];
 #pragma unroll
-    for (int i = 0; i < kAD; ++i) v[i] = ld_dev(src + min(j0 + tid + kThreads * i, nw - 1));
+    for (int i = 0; i < kAD; ++i) {
+      const uint32_t off = base + (uint32_t)min(j0 + tid + kThreads * i, nw - 1) * 32;
+      lo[i] = ld_dev16(rs, off);
+      hi[i] = ld_dev16(rs, off + 16);
+    }
 #pragma unroll
     for (int i = 0; i < kAD; ++i) {
       const int j = j0 + tid + kThreads * i;
-      if (j < nw) dst[a_slot(g0 * WPG + (j >> 1), WPG) * 2 + (j & 1)] = v[i];
+      if (j < nw) {
+        const uint32_t off = base + (uint32_t)j * 32;
+        for (uint32_t it = 0; !(fresh4(lo[i], t16) && fresh4(hi[i], t16)); ++it) {
+          if (it == kSpinLimit) {
+            atomicOr(a.err, kErrSyncTimeout);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          lo[i] = ld_dev16(rs, off);
+          hi[i] = ld_dev16(rs, off + 16);
+        }
+        v4u p;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) p[m] = (lo[i][m] >> 16) | (hi[i][m] & 0xFFFF0000u);
+        reinterpret_cast<v4u*>(lds_a)[a_slot(g0 * WPG + j, WPG)] = p;
+      }
     }
   }
   __syncthreads();
@@ -954,50 +1018,55 @@ __device__ __forceinline__ void stage_a_coherent(const LayerArgs& a, char* lds_a
   __syncthreads();
 }
 
-// Down projection of output rows 8*rb..8*rb+7 (see above) in two parts: the
-// shared expert's groups [0, Gs) as soon as the shared gate/up is done, then
-// the chosen experts' groups [Gs, NI) once every expert phase is done.  Lane
+// Down workgroup of output rows 8*rb..8*rb+7 of the fused kernel: the shared
+// expert's groups [0, Gs) as soon as the shared gate/up is done, then the
+// chosen experts' groups [Gs, NI) once the routed gate/up is done.  Lane
 // (r = tid & 7, jj = tid >> 3) owns row r and the groups jj + 32 i of each
-// part; SS + SR weight slots, all loaded before the first wait.
-template <int SS, int SR>
-__device__ void down_two_part(const LayerArgs& a, int rb, const uint64_t* sel, const float* s_w, char* smem,
-                              uint32_t* area, uint32_t tag) {
+// part; SS shared and SR routed weight slots.  The shared slots are loaded at
+// once, the routed ones as soon as the routing is known.
+template <int SS, int SR, int NE>
+__device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_router, uint32_t members_shared,
+                           uint32_t members_routed, const uint64_t* lrep, char* smem, float* s_logits,
+                           uint32_t* scratch, uint64_t* s_sel, float* s_w) {
   const int tid = threadIdx.x, r = tid & 7, jj = tid >> 3;
-  const DownPhases ph(a.fs, a.f, a.K);
-  const int Gs = ph.Gs, Gf = ph.Gf;
-  const int NI = Gs + a.K * Gf, NR = NI - Gs;
+  uint32_t* area = a.counter;
+  const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + blockIdx.x % kEpochReps)) + 1u;
+  const int Gs = a.fs >> 6, Gf = a.f >> 6;
+  const int NI = Gs + a.K * Gf, NRG = NI - Gs;
   constexpr int WPG = a_words(1);
   char* lds_a = smem;
   float* asum = reinterpret_cast<float*>(smem + (size_t)NI * (WPG + 1) * 16);
   float* red = asum + NI;
   v4u q0[SS + SR], q1[SS + SR];
   uint32_t sb[SS + SR];
-#pragma unroll
-  for (int s = 0; s < SS + SR; ++s) {  // every weight load goes out now, before any wait
-    const bool shared = s < SS;
-    const int li = jj + 32 * (shared ? s : s - SS);
-    const uint8_t* blob;
-    int G, g;
-    uint32_t oq, osb;
-    if (shared) {
-      g = min(li, max(Gs, 1) - 1);
-      blob = Gs > 0 ? a.shared_blob : reinterpret_cast<const uint8_t*>(sel[0]);
-      G = Gs > 0 ? Gs : Gf;
-      oq = Gs > 0 ? a.so.dq : a.ro.dq;
-      osb = Gs > 0 ? a.so.dsb : a.ro.dsb;
-    } else {
-      const int c = min(li, NR - 1);
-      const int k = c / Gf;
-      g = c - k * Gf;
-      G = Gf;
-      blob = reinterpret_cast<const uint8_t*>(sel[k]);
-      oq = a.ro.dq;
-      osb = a.ro.dsb;
-    }
+  auto load_slot = [&](int s, const uint8_t* blob, int G, int g, uint32_t oq, uint32_t osb) {
     const size_t off = (((size_t)rb * G + g) * 2) * 128 + r * 16;
     q0[s] = ldg<v4u>(blob + oq + off);
     q1[s] = ldg<v4u>(blob + oq + off + 128);
     sb[s] = ldg<uint32_t>(blob + osb + (((size_t)rb * G + g) * 8 + r) * 4);
+  };
+  bulk_delay();
+#pragma unroll
+  for (int s = 0; s < SS; ++s) load_slot(s, a.shared_blob, Gs, min(jj + 32 * s, Gs - 1), a.so.dq, a.so.dsb);
+  // routing
+  wait_count<1>(a, area, kCntRouter, tag * members_router);
+  stage_logits_dev<NE>(a, lrep, tag, s_logits);
+  if (threadIdx.x < 64) {
+    int id;
+    float w;
+    topk_wave<NE>(a, 0, s_logits, &id, &w, scratch);
+    if (threadIdx.x < a.K) {
+      s_sel[threadIdx.x] = reinterpret_cast<uint64_t>(a.expert_base + (size_t)id * a.expert_stride);
+      s_w[threadIdx.x] = w;
+    }
+    if (rb == 0) publish_routing(a, 0, threadIdx.x, id, w);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < SR; ++s) {
+    const int c = min(jj + 32 * s, NRG - 1);
+    const int k = c / Gf;
+    load_slot(SS + s, reinterpret_cast<const uint8_t*>(s_sel[k]), Gf, c - k * Gf, a.ro.dq, a.ro.dsb);
   }
   float acc = 0.f;
   auto accumulate = [&](int s, int it) {
@@ -1019,37 +1088,19 @@ __device__ void down_two_part(const LayerArgs& a, int rb, const uint64_t* sel, c
     const float wgt = (it < Gs) ? 1.f : s_w[(it - Gs) / Gf];
     acc = fmaf(wgt, term, acc);
   };
-  const int fl = kSyncSubs + 1 + (int)(blockIdx.x % kPhaseFlags);
-  if (Gs > 0) {  // shared part
-    if (threadIdx.x == 0) {
-      const uint32_t* flag = sync_slot(area, fl);
-      poll_tag<uint32_t, 0, 8>(a, flag, tag, ld_dev(flag));
-    }
-    __syncthreads();
-    stage_a_coherent(a, lds_a, asum, 0, Gs);
+  if (SS > 0) {  // shared part
+    wait_count<4>(a, area, kCntShared, tag * members_shared);
+    stage_a_coherent(a, lds_a, asum, 0, Gs, tag);
 #pragma unroll
     for (int s = 0; s < SS; ++s)
       if (jj + 32 * s < Gs) accumulate(s, jj + 32 * s);
   }
-  // Routed part.  The last expert phase (its workgroups are dispatched last)
-  // is polled gently, then lane p of wavefront 0 checks phase p, all in one
-  // round trip when they are done.
-  if (threadIdx.x < 64) {
-    if (threadIdx.x == 0) {
-      const uint32_t* last = sync_slot(area, ph.NQ * kPhaseSlots + fl);
-      poll_tag<uint32_t, 0, 8>(a, last, tag, ld_dev(last));
-    }
-    const int p = 1 + (int)threadIdx.x;
-    if (p < ph.NQ) {
-      const uint32_t* flag = sync_slot(area, p * kPhaseSlots + fl);
-      poll_tag<uint32_t, 0, 2>(a, flag, tag, ld_dev(flag));
-    }
-  }
-  __syncthreads();
-  stage_a_coherent(a, lds_a, asum, Gs, NI);
+  wait_count<2>(a, area, kCntRouted, tag * members_routed);
+  done_with_tag(area, rb, nd, tag);
+  stage_a_coherent(a, lds_a, asum, Gs, NI, tag);
 #pragma unroll
   for (int s = 0; s < SR; ++s)
-    if (jj + 32 * s < NR) accumulate(SS + s, Gs + jj + 32 * s);
+    if (jj + 32 * s < NRG) accumulate(SS + s, Gs + jj + 32 * s);
   acc = xor_sum(acc, 8, 32);
   if ((tid & 63) < 8) red[(tid >> 6) * 8 + r] = acc;
   __syncthreads();
@@ -1063,36 +1114,49 @@ __device__ void down_two_part(const LayerArgs& a, int rb, const uint64_t* sel, c
 }
 
 template <int MAXI, int NE, int SS, int SR>
-__global__ __launch_bounds__(kThreads) void fused_layer_kernel(LayerArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   __shared__ uint32_t scratch[128];
-  __shared__ float s_logits[1024];
+  __shared__ float s_logits[64 * NE];
   __shared__ uint64_t s_sel[64];
   __shared__ float s_w[64];
   int NR, NS, NG, ND;
-  const int total = fused_groups(a.E, a.K, a.d, a.f, a.fs, &NR, &NS, &NG, &ND);
+  fused_groups(a.E, a.K, a.d, a.f, a.fs, &NR, &NS, &NG, &ND);
   const int b = blockIdx.x;
   uint32_t* area = a.counter;
-  const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kEpochReplicas)) + 1u;
   uint64_t* lrep = reinterpret_cast<uint64_t*>(area + (size_t)kSyncSlots * kSyncStride);
   const size_t rstride = logit_rep_stride(a.E);
+  const uint64_t* my_rep = lrep + (size_t)(b % kLogitReplicas) * rstride;
   const XStage S = carve_x(smem, a.d);
   if (b < NR) {
     __builtin_amdgcn_s_setprio(2);  // on the critical path: ahead of the streaming wavefronts
-    router_row<1>(a, 0, b * kWaves + (threadIdx.x >> 6), S, lrep, rstride, tag);
+    const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kEpochReps)) + 1u;
+    const float v = router_row<1>(a, 0, b * kWaves + (threadIdx.x >> 6), S);
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x < kLogitReplicas) {  // lane j: the 4 tagged logits of this workgroup into replica j
+      const size_t off = ((size_t)threadIdx.x * rstride + (size_t)b * kWaves) * 8;
+      const auto rs = buf_rsrc(lrep);
+      st_dev16(rs, (uint32_t)off, v4u{__float_as_uint(s_w[0]), tag, __float_as_uint(s_w[1]), tag});
+      st_dev16(rs, (uint32_t)off + 16, v4u{__float_as_uint(s_w[2]), tag, __float_as_uint(s_w[3]), tag});
+    }
+    arrive(area, kCntRouter);
   } else if (b < NR + NS) {
+    const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kEpochReps)) + 1u;
     XRegs xr;
     x_issue<1>(a, 0, xr);
-    gate_up_block<1, MAXI, kFusedGuRows>(a, 0, a.shared_blob, a.so, b - NR, 0, S, xr);
-    gate_up_arrive(area, 0, b - NR, NS, tag);
+    bulk_delay();
+    gate_up_block<1, MAXI, kFusedGuRows, true>(a, 0, a.shared_blob, a.so, b - NR, 0, S, xr, tag);
+    arrive(area, kCntShared);
   } else if (b < NR + NS + NG) {
     const int g = b - NR - NS, RB = a.f / kFusedGuRows;
     const int k = g / RB, rb = g - k * RB;
-    const DownPhases ph(a.fs, a.f, a.K);
+    const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kEpochReps)) + 1u;
     XRegs xr;
     x_issue<1>(a, 0, xr);
     __builtin_amdgcn_s_setprio(2);
-    stage_tagged_logits(a, lrep + (size_t)(b % kLogitReplicas) * rstride, tag, s_logits);
+    wait_count<1>(a, area, kCntRouter, tag * (uint32_t)NR);
+    stage_logits_dev<NE>(a, my_rep, tag, s_logits);
     if (threadIdx.x < 64) {  // one wavefront finds the expert
       const int id = topk_kth<NE>(a, 0, s_logits, k);
       if (threadIdx.x == 0) scratch[0] = (uint32_t)id;
@@ -1100,30 +1164,13 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(LayerArgs a) {
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
     const int id = (int)scratch[0];
-    gate_up_block<1, MAXI, kFusedGuRows>(a, 0, a.expert_base + (size_t)id * a.expert_stride, a.ro, rb,
-                                         a.fs + k * a.f, S, xr);
-    const int q = k / ph.P;  // expert phase
-    const int members = (min(a.K, (q + 1) * ph.P) - q * ph.P) * RB;
-    gate_up_arrive(area, 1 + q, (k - q * ph.P) * RB + rb, members, tag);
+    gate_up_block<1, MAXI, kFusedGuRows, true>(a, 0, a.expert_base + (size_t)id * a.expert_stride, a.ro, rb,
+                                               a.fs + k * a.f, S, xr, tag);
+    arrive(area, kCntRouted);
   } else {
-    const int rb = b - NR - NS - NG;
-    stage_tagged_logits(a, lrep + (size_t)(b % kLogitReplicas) * rstride, tag, s_logits);
-    if (threadIdx.x < 64) {
-      int id;
-      float w;
-      topk_wave<NE>(a, 0, s_logits, &id, &w, scratch);
-      if (threadIdx.x < a.K) {
-        s_sel[threadIdx.x] = reinterpret_cast<uint64_t>(a.expert_base + (size_t)id * a.expert_stride);
-        s_w[threadIdx.x] = w;
-      }
-      if (rb == 0) publish_routing(a, 0, threadIdx.x, id, w);
-    }
-    __syncthreads();
-    __builtin_amdgcn_s_setprio(2);
-    down_two_part<SS, SR>(a, rb, s_sel, s_w, smem, area, tag);
+    down_fused<SS, SR, NE>(a, b - NR - NS - NG, ND, (uint32_t)NR, (uint32_t)NS, (uint32_t)NG, my_rep, smem,
+                           s_logits, scratch, s_sel, s_w);
   }
-  __builtin_amdgcn_s_setprio(0);
-  finish_launch(area, total, tag);
 }
 
 template <int ACT, int MAXI, int NE>
@@ -1233,17 +1280,16 @@ hipError_t launch_fused(const LayerArgs& a, hipStream_t s) {
 
 size_t decode_lds_bytes_x(int d) { return x_stage_bytes(d); }
 size_t decode_sync_bytes(int E) { return sync_area_bytes(E); }
+size_t decode_abuf_bytes(int T, int F) { return std::max((size_t)T * F * 4, kAReps * a_rep_stride(F)); }
 size_t decode_lds_bytes_down(int F, int NI, int K, int act) { return down_lds_bytes(F, NI, K, act); }
 
 // The fused layer kernel serves one bf16 token on resident experts, when its
 // LDS (dynamic part plus about 6 KB of static routing state) fits in 64 KB.
 // The down workgroups hold at most 2 shared and 4 routed weight slots (64 and
-// 128 groups), the gate/up workgroups at most 4 (d_model <= 4096), and the
-// expert phases fit the synchronisation area.
+// 128 groups), the gate/up workgroups at most 4 (d_model <= 4096).
 bool decode_fused_ok(const LayerArgs& a) {
-  const DownPhases ph(a.fs, a.f, a.K);
   return a.T == 1 && a.act == 1 && a.E <= 1024 && a.d <= 4096 && fused_lds_bytes(a) + 6 * 1024 <= 64 * 1024 &&
-         ph.Gs <= 64 && a.K * ph.Gf <= 128 && ph.NQ + 1 <= kMaxPhases;
+         a.fs / 64 <= 64 && a.K * (a.f / 64) <= 128;
 }
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s) {
