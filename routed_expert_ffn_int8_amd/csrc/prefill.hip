@@ -3,7 +3,8 @@
 // Rockchip-NPU MoE streaming plan, §2.5 and §8.4: prompts are processed in
 // 128-token chunks so that one fetched expert serves every row of the chunk
 // that chose it.  Per chunk:
-//   1. router GEMV + softmax top-K per token (the decode kernels, T rows);
+//   1. router logits on bf16 MFMA (int8 weights are exact in bf16) and the
+//      softmax top-K of every token, in one kernel;
 //   2. token->expert grouping: counting sort, stable in token order, plus a
 //      list of 16-token tiles per expert (and per shared-expert row block);
 //   3. grouped gate/up GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16): the
@@ -19,6 +20,7 @@
 // chunk is routed on its own, and the union of chosen experts can be large.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -27,6 +29,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 template <class T>
 __device__ __forceinline__ T ldg(const void* p) {
@@ -39,19 +42,48 @@ constexpr int kPThreads = 64 * kPWaves;
 constexpr int kRowsPerWG = 16 * kPWaves;  // weight rows per workgroup
 
 // ------------------------------------------------------------ sort + tiles
+// Exclusive prefix sum of one int per thread over the workgroup (up to 1024
+// threads); *total receives the sum.  sh: 16 ints of LDS.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int t = lane < nw ? sh[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int y = __shfl_up(t, o, 64);
+      if (lane >= o) t += y;
+    }
+    if (lane < nw) sh[lane] = t;
+  }
+  __syncthreads();
+  const int base = w > 0 ? sh[w - 1] : 0;
+  *total = sh[nw - 1];
+  __syncthreads();  // sh may be reused by the caller
+  return base + x - v;
+}
+
 // Deterministic token->expert grouping by one workgroup of 1024 threads.
 // Each expert gets a bitmask over the chunk's tokens (set with LDS atomic-or,
 // whose result does not depend on order); its count is the mask's popcount,
 // offsets are the exclusive scan, and a pair (t, k) choosing expert e lands at
 // offsets[e] + popcount of e's mask below bit t, i.e. the pairs of an expert
 // are in ascending token order.  With a tile list it also emits (expert, tile)
-// entries: ceil(n_e/16) per chosen expert, then ceil(T/16) for the shared
-// expert (expert id E).  Needs E * ceil(T/32) words of LDS; repeated ids in
-// one token's set are counted once.
+// entries: ceil(n_e/16) per chosen expert in expert order, then ceil(T/16) for
+// the shared expert (expert id E).  Needs E * ceil(T/32) words of LDS;
+// repeated ids in one token's set are counted once.  E <= 1024.
 __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ ids, int T, int K, int E,
                                                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                                                    int32_t* tiles, int with_shared) {
   extern __shared__ uint32_t sh[];  // off[E+1], mask[E][NW]
+  __shared__ int scan_sh[16];
   const int NW = (T + 31) >> 5;
   int32_t* off = reinterpret_cast<int32_t*>(sh);
   uint32_t* mask = sh + E + 1;
@@ -63,38 +95,34 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
     if (e >= 0 && e < E) atomicOr(&mask[e * NW + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int w = 0; w < NW; ++w) c += __popc(mask[e * NW + w]);
-    off[e] = c;  // count for now, turned into the offset below
+  int c = 0;
+  if (tid < E)
+    for (int w = 0; w < NW; ++w) c += __popc(mask[tid * NW + w]);
+  int total = 0, ntile_total = 0;
+  const int o = block_excl_scan(c, scan_sh, &total);
+  const int nt_e = (c + kTile - 1) / kTile;
+  const int to = block_excl_scan(nt_e, scan_sh, &ntile_total);
+  if (tid < E) {
+    off[tid] = o;
+    counts[tid] = c;
+    offsets[tid] = o;
+    if (tiles)
+      for (int tt = 0; tt < nt_e; ++tt) {
+        tiles[1 + 2 * (to + tt)] = tid;
+        tiles[2 + 2 * (to + tt)] = tt;
+      }
   }
-  __syncthreads();
-  if (tid == 0) {  // E <= 1024: a serial scan is cheaper than its barriers
-    int run = 0, nt = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = off[e];
-      counts[e] = c;
-      off[e] = run;
-      offsets[e] = run;
-      run += c;
-      if (tiles)
-        for (int tt = 0; tt * kTile < c; ++tt) {
-          tiles[1 + 2 * nt] = e;
-          tiles[2 + 2 * nt] = tt;
-          ++nt;
-        }
+  if (tid == 0) {
+    off[E] = total;
+    offsets[E] = total;
+  }
+  if (tiles) {
+    const int ns = with_shared ? (T + kTile - 1) / kTile : 0;
+    for (int tt = tid; tt < ns; tt += blockDim.x) {
+      tiles[1 + 2 * (ntile_total + tt)] = E;
+      tiles[2 + 2 * (ntile_total + tt)] = tt;
     }
-    off[E] = run;
-    offsets[E] = run;
-    if (tiles) {
-      if (with_shared)
-        for (int tt = 0; tt * kTile < T; ++tt) {
-          tiles[1 + 2 * nt] = E;
-          tiles[2 + 2 * nt] = tt;
-          ++nt;
-        }
-      tiles[0] = nt;
-    }
+    if (tid == 0) tiles[0] = ntile_total + ns;
   }
   __syncthreads();
   for (int i = tid; i < n; i += blockDim.x) {
@@ -107,6 +135,105 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
     perm[pos] = i;
     inv[i] = pos;
   }
+}
+
+// ------------------------------------------------------------ router + top-K
+// Workgroup (16-token tile, 16 experts) of 16 wavefronts: they split d in
+// sixteen and each runs v_mfma_f32_16x16x32_bf16 over its share, A = the
+// token rows (bf16, straight from memory), B = the int8 router rows
+// converted exactly to bf16; the 16 partial 16x16 blocks are summed in a fixed
+// order in LDS and scaled: logit = scale_e * acc + bias_e.  Logits go to the
+// layer's logit array with device-scope stores.  The workgroup that completes
+// a token tile (an arrival counter, which that workgroup resets for the next
+// call) runs the softmax top-K of the tile's tokens, one wavefront per token.
+constexpr int kRouteWaves = 16;
+constexpr int kRoutePre = 4;  // k-blocks of router weights in flight per lane
+
+__device__ __forceinline__ uint32_t int8x2_to_bf16x2(uint32_t w, int j) {  // bytes 2j, 2j+1 of w
+  const float lo = (float)(((int)(w << (24 - 16 * j))) >> 24);
+  const float hi = (float)(((int)(w << (16 - 16 * j))) >> 24);
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);  // exact: |q| <= 128
+}
+
+size_t route_lds_bytes(int E) { return (size_t)kTile * E * 4; }
+
+template <int NE>
+__global__ __launch_bounds__(64 * kRouteWaves) void pf_route_kernel(PrefillArgs p) {
+  extern __shared__ __align__(16) char smem[];  // [16][E] logits of the tile (last workgroup)
+  __shared__ float part[kRouteWaves][64][4];
+  __shared__ uint32_t scratch[kRouteWaves][2 * 64];
+  __shared__ uint32_t last_sh;
+  const LayerArgs& a = p.L;
+  const int d = a.d, E = a.E, T = a.T;
+  const int t0 = blockIdx.x * kTile;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kb = lane >> 4;
+  const int e = 16 * blockIdx.y + n, ec = min(e, E - 1);
+  const int KB = d / 32;
+  const int k_lo = (KB * wave) / kRouteWaves, k_hi = (KB * (wave + 1)) / kRouteWaves;
+  const int8_t* wrow = a.router_w + (size_t)ec * d + 8 * kb;
+  const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + (size_t)min(t0 + n, T - 1) * d + 8 * kb;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = k_lo; k0 < k_hi; k0 += kRoutePre) {
+    v2u wq[kRoutePre];
+    v4u xv[kRoutePre];
+#pragma unroll
+    for (int i = 0; i < kRoutePre; ++i) {
+      const int k = min(k0 + i, k_hi - 1);
+      wq[i] = ldg<v2u>(wrow + (size_t)k * 32);
+      xv[i] = ldg<v4u>(xrow + (size_t)k * 32);
+    }
+#pragma unroll
+    for (int i = 0; i < kRoutePre; ++i) {
+      if (k0 + i < k_hi) {
+        v4u bv;
+        bv[0] = int8x2_to_bf16x2(wq[i][0], 0);
+        bv[1] = int8x2_to_bf16x2(wq[i][0], 1);
+        bv[2] = int8x2_to_bf16x2(wq[i][1], 0);
+        bv[3] = int8x2_to_bf16x2(wq[i][1], 1);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[i]), __builtin_bit_cast(bf16x8, bv),
+                                                      acc, 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[wave][lane][i] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+    const float sc = f16_to_f32(ldg<uint16_t>(a.router_scale + ec));
+    const float bi = a.router_bias ? ldg<float>(a.router_bias + ec) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // C row m = 4 kb + i (token), column n (expert)
+      float v = 0.f;
+      for (int w = 0; w < kRouteWaves; ++w) v += part[w][lane][i];
+      const int t = t0 + 4 * kb + i;
+      if (t < T && e < E)
+        __hip_atomic_store(a.logits + (size_t)t * E + e, fmaf(sc, v, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // logit stores done before the arrival
+    if (lane == 0) {
+      const uint32_t old = atomicAdd(p.route_cnt + blockIdx.x, 1u);
+      last_sh = old == gridDim.y - 1 ? 1u : 0u;
+      if (last_sh) __hip_atomic_store(p.route_cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  if (!last_sh) return;
+  const int t = t0 + wave;
+  if (t >= T) return;
+  float* s_log = reinterpret_cast<float*>(smem) + (size_t)wave * E;
+  const float* lt = a.logits + (size_t)t * E;
+  float v[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) v[i] = __hip_atomic_load(lt + min(lane + 64 * i, E - 1), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int i = 0; i < NE; ++i)
+    if (lane + 64 * i < E) s_log[lane + 64 * i] = v[i];
+  int id;
+  float w;
+  topk_wave<NE>(a, t, s_log, &id, &w, scratch[wave]);
+  publish_routing(a, t, lane, id, w);
 }
 
 // ------------------------------------------------------------ tile staging
@@ -412,6 +539,7 @@ size_t prefill_workspace_bytes(int T, int d, int E, int K, int f, int fs) {
   const int C = T < kChunkTokens ? T : kChunkTokens;
   size_t b = 0;
   b += align_up((size_t)E * 4) + align_up((size_t)(E + 1) * 4);  // counts, offsets
+  b += align_up((size_t)((C + kTile - 1) / kTile) * 4);            // router arrival counters
   b += 2 * align_up((size_t)C * K * 4);                            // perm, inv
   b += align_up((1 + 2 * max_tiles(C, K, E)) * 4);                 // tiles
   b += align_up((size_t)C * K * f * 2) + align_up((size_t)C * (fs > 0 ? fs : 64) * 2);  // A, As
@@ -429,6 +557,7 @@ void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, 
   };
   p.counts = reinterpret_cast<int32_t*>(take((size_t)E * 4));
   p.offsets = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  p.route_cnt = reinterpret_cast<uint32_t*>(take((size_t)((C + kTile - 1) / kTile) * 4));
   p.perm = reinterpret_cast<int32_t*>(take((size_t)C * K * 4));
   p.inv = reinterpret_cast<int32_t*>(take((size_t)C * K * 4));
   p.tiles = reinterpret_cast<int32_t*>(take((1 + 2 * max_tiles(C, K, E)) * 4));
@@ -437,8 +566,6 @@ void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, 
   p.Y = reinterpret_cast<float*>(take((size_t)C * K * d * 4));
   p.Ys = reinterpret_cast<float*>(take((size_t)C * d * 4));
 }
-
-hipError_t launch_decode(const LayerArgs& a, hipStream_t s);
 
 // Staging words per thread for 16 rows of `width` bf16 values, rounded up to a power of two.
 static int stage_words(int width) {
@@ -469,6 +596,10 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
       if (e != hipSuccess) return e;
     }
+    // the router's tile of logits for up to 1024 experts (64 KB) next to its 24 KB of static LDS
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(pf_route_kernel<16>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds_bytes(1024));
+    if (e != hipSuccess) return e;
     lds_raised = true;
   }
   for (int c0 = 0; c0 < a0.T; c0 += kChunkTokens) {
@@ -484,12 +615,21 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
     if (a0.ids_out) a.ids_out = a0.ids_out + (size_t)c0 * a.K;
     if (a0.w_out) a.w_out = a0.w_out + (size_t)c0 * a.K;
     p.xact = const_cast<void*>(a.x);
-    // 1. router + top-K (decode kernels over the chunk's tokens)
-    LayerArgs r = a;
-    r.stages = kStageRouter;
-    r.topk_in_gate_up = 0;
-    hipError_t e = launch_decode(r, s);
-    if (e != hipSuccess) return e;
+    // 1. router + top-K
+    {
+      const dim3 g_rt((unsigned)((C + kTile - 1) / kTile), (unsigned)((a.E + 15) / 16));
+      const dim3 b_rt(64 * kRouteWaves);
+      const size_t l_rt = route_lds_bytes(a.E);
+      if (a.E <= 64)
+        launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<1>, g_rt, b_rt, l_rt, s, p);
+      else if (a.E <= 128)
+        launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<2>, g_rt, b_rt, l_rt, s, p);
+      else if (a.E <= 256)
+        launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<4>, g_rt, b_rt, l_rt, s, p);
+      else
+        launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<16>, g_rt, b_rt, l_rt, s, p);
+    }
+    hipError_t e;
     // 2. grouping + tiles
     launch_timed(a.prof, kKSort, sort_kernel, dim3(1), dim3(1024), sort_lds_bytes(C, a.E), s, (const int32_t*)a.ids,
                  C, a.K, a.E, p.counts, p.offsets, p.perm, p.inv, p.tiles, a.fs > 0 ? 1 : 0);

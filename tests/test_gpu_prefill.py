@@ -74,10 +74,14 @@ def test_prefill_shapes(shape):
 
 
 def test_prefill_and_decode_paths_agree(prefill_layer):
+    """Same expert sets; coefficients equal up to the fp32 summation order of
+    the router (matrix-core tiles in prefill, one wavefront per row in
+    decode), which moves logits by ~1e-6."""
     w, gl, OL = prefill_layer
     x = make_tokens(w, 16, stream=35)
     yp, idp, wp = gl.forward(x, path=M.MOE_PATH_PREFILL)
     yd, idd, wd = gl.forward(x, path=M.MOE_PATH_DECODE)
-    assert np.array_equal(idp, idd) and np.array_equal(wp, wd)
+    assert np.array_equal(idp, idd)
+    assert np.max(np.abs(wp - wd)) < 1e-5
     a, b = O.tokens_to_f64(yp), O.tokens_to_f64(yd)
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 5e-3
