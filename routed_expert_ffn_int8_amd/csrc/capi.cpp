@@ -20,7 +20,7 @@
 
 namespace moe {
 size_t decode_lds_bytes_x(int d);
-size_t decode_abuf_bytes(int T, int F);
+size_t decode_arep_bytes(int F);
 size_t decode_lds_bytes_down(int F, int NI, int K, int act);
 size_t prefill_workspace_bytes(int T, int d, int E, int K, int f, int fs);
 void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, int fs);
@@ -110,6 +110,7 @@ struct moe_layer {
   float* d_wts = nullptr;
   uint32_t* d_counter = nullptr;
   void* d_abuf = nullptr;
+  void* d_arep = nullptr;  // the fused kernel's activation copies
   int32_t* d_err = nullptr;
   // prefill workspace
   char* d_prefill = nullptr;
@@ -220,6 +221,7 @@ void free_layer(moe_layer* L) {
   (void)hipFree(L->d_wts);
   (void)hipFree(L->d_counter);
   (void)hipFree(L->d_abuf);
+  (void)hipFree(L->d_arep);
   (void)hipFree(L->d_err);
   (void)hipFree(L->d_prefill);
   (void)hipFree(L->d_slots);
@@ -301,7 +303,7 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
   const size_t F = L->fs + K * L->f;
   if (dalloc(&L->d_logits, T * E * 4) != hipSuccess || dalloc(&L->d_ids, T * K * 4) != hipSuccess ||
       dalloc(&L->d_wts, T * K * 4) != hipSuccess || dalloc(&L->d_sel, T * K * 8) != hipSuccess || dalloc(&L->d_counter, decode_sync_bytes(L->E)) != hipSuccess ||
-      dalloc(&L->d_abuf, decode_abuf_bytes((int)T, (int)F)) != hipSuccess ||
+      dalloc(&L->d_abuf, T * F * 4) != hipSuccess || dalloc(&L->d_arep, decode_arep_bytes((int)F)) != hipSuccess ||
       dalloc(&L->d_err, 64) != hipSuccess)
     return fail(MOE_ERR_NOMEM, "decode workspace alloc failed");
   HIP_OK(hipMemset(L->d_ids, 0, T * K * 4));
@@ -312,6 +314,7 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
   }
   HIP_OK(hipMemset(L->d_counter, 0, decode_sync_bytes(L->E)));
   HIP_OK(hipMemset(L->d_err, 0, 64));
+  HIP_OK(hipMemset(L->d_arep, 0, decode_arep_bytes((int)F)));  // parity 0: older than any launch
   // prefill workspace (bf16 only)
   if (L->act == MOE_ACT_BF16 && L->max_tokens > 1) {
     L->prefill_bytes = prefill_workspace_bytes((int)T, L->d, L->E, L->K, L->f, L->fs);
@@ -346,6 +349,7 @@ LayerArgs base_args(moe_layer* L, const void* x, void* out, int T) {
   a.wts = L->d_wts;
   a.counter = L->d_counter;
   a.abuf = L->d_abuf;
+  a.arep = L->d_arep;
   a.err = L->d_err;
   a.out = out;
   a.prof = L->prof.get();

@@ -74,14 +74,21 @@ __device__ __forceinline__ void st_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off,
 
 // The fused kernel keeps kAReps copies of the intermediate activation vector,
 // a_rep_stride(F) bytes apart, so that the hundreds of down workgroups
-// reading it spread over several copies and memory channels.  Each value is
-// one 32-bit word: fp16 bits << 16 | the low 16 bits of the launch tag, so a
-// reader can tell a value of this launch from a stale one.
-constexpr int kAReps = 8;
-__host__ __device__ inline size_t a_rep_stride(int F) { return ((size_t)F * 4 + 4095) / 4096 * 4096 + 512; }
-__device__ __forceinline__ bool fresh4(const v4u& w, uint32_t t16) {
-  return ((w[0] & 0xFFFFu) == t16) & ((w[1] & 0xFFFFu) == t16) & ((w[2] & 0xFFFFu) == t16) &
-         ((w[3] & 0xFFFFu) == t16);
+// reading it spread over several copies and memory channels.  Values are fp16
+// in the pair order of the down projection, rounded to 9 mantissa bits; the
+// freed last bit holds the parity of the launch tag, so a reader can tell a
+// value of this launch from the previous launch's and clears the bit before
+// use (the value is then the same whatever the parity).
+constexpr int kAReps = 32;
+__host__ __device__ inline size_t a_rep_stride(int F) { return ((size_t)F * 2 + 4095) / 4096 * 4096 + 512; }
+__device__ __forceinline__ uint16_t f32_to_f16_tagged(float v, uint32_t tag) {
+  uint32_t u = __float_as_uint(v);
+  u = (u + 0x1FFFu + ((u >> 14) & 1u)) & ~0x3FFFu;  // round to nearest even at 9 mantissa bits
+  return (uint16_t)((f32_to_f16(__uint_as_float(u)) & 0xFFFEu) | (tag & 1u));  // fp16 subnormals may round odd
+}
+__device__ __forceinline__ bool fresh4(const v4u& w, uint32_t par) {  // par: 0 or 0x00010001
+  return ((w[0] & 0x00010001u) == par) & ((w[1] & 0x00010001u) == par) & ((w[2] & 0x00010001u) == par) &
+         ((w[3] & 0x00010001u) == par);
 }
 
 struct XStage {
@@ -271,7 +278,10 @@ __device__ __forceinline__ char* abuf_of(const LayerArgs& a, int t, int act) {
 // whole 128-byte runs.  `xr` holds the token loads, issued by the caller
 // before it waited on anything, so they overlap the weight fetch.  REPS
 // (bf16 only): the ROWS results, tagged with `tag`, go to every copy of the
-// fused kernel's activation vector in 16-byte stores.
+// fused kernel's activation vector in 16-byte stores, and the token is
+// staged before the weights are requested (its loads went out long before):
+// staging it after them would make the first product wait for every weight,
+// as the wait for the token loads cannot be told apart from theirs.
 template <int ACT, int MAXI, int ROWS = 8, bool REPS = false>
 __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, const BlobOffsets& o, int rb,
                               int apos, const XStage& S, const XRegs& xr, uint32_t tag = 0) {
@@ -285,6 +295,7 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
   const uint8_t* gsb = blob + o.gsb + ((size_t)rb8 * G * 8 + r8) * 4;  // + g * 32
   const uint8_t* usb = blob + o.usb + ((size_t)rb8 * G * 8 + r8) * 4;
   float accg = 0.f, accu = 0.f;
+  if (REPS) x_commit<ACT>(a, t, xr, S);
   for (int base = 0; base < G; base += JJ * MAXI) {
     v4u qg0[MAXI], qg1[MAXI], qu0[MAXI], qu1[MAXI];
     uint32_t sg[MAXI], su[MAXI];
@@ -299,7 +310,7 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
       sg[i] = ldg<uint32_t>(gsb + g * 32);
       su[i] = ldg<uint32_t>(usb + g * 32);
     }
-    if (base == 0) x_commit<ACT>(a, t, xr, S);
+    if (!REPS && base == 0) x_commit<ACT>(a, t, xr, S);
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
       const int g = base + jj + JJ * i;
@@ -323,19 +334,21 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
         (S.red[r * 2 + 1] + S.red[W + r * 2 + 1]) + (S.red[2 * W + r * 2 + 1] + S.red[3 * W + r * 2 + 1]);
     const float v = silu(gsum) * usum;
     if (REPS) {  // S.xf is free: the bf16 products read S.xp
-      reinterpret_cast<uint32_t*>(S.xf)[r] = ((uint32_t)f32_to_f16(v) << 16) | (tag & 0xFFFFu);
+      const int m = r & 7;
+      reinterpret_cast<uint16_t*>(S.xf)[(r & ~7) + (m & 3) * 2 + (m >> 2)] = f32_to_f16_tagged(v, tag);
     } else {
       store_a<ACT>(abuf_of(a, t, ACT), apos + row, v);
     }
   }
   if (REPS) {
     __syncthreads();
-    constexpr int CH = ROWS / 4;  // 16-byte words of this row block
+    constexpr int CH = ROWS / 8;  // 16-byte words of this row block
     if (tid < CH * kAReps) {
       const int c = tid % CH, q = tid / CH;
-      const size_t off = (size_t)q * a_rep_stride(a.fs + a.K * a.f) + (size_t)(apos + rb * ROWS) * 4 + c * 16;
-      st_dev16(buf_rsrc(a.abuf), (uint32_t)off, reinterpret_cast<const v4u*>(S.xf)[c]);
+      const size_t off = (size_t)q * a_rep_stride(a.fs + a.K * a.f) + (size_t)(apos + rb * ROWS) * 2 + c * 16;
+      st_dev16(buf_rsrc(a.arep), (uint32_t)off, reinterpret_cast<const v4u*>(S.xf)[c]);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the copies land before the arrival: consumers then read them once
   }
 }
 
@@ -640,10 +653,11 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
 // Hand-offs go through counters that only grow.  Each launch has a tag (the
 // launch count + 1, read from an epoch word); a stage is complete when its
 // counter has grown by its number of producer workgroups to tag * members.
-// A producer stores its results with device-scope stores, waits until they
-// are done, then adds one to each of the counter's 8 replicas; a consumer
-// polls the replica of its own index with a single lane, so a few hundred
-// pollers spread over 8 addresses instead of flooding one.
+// A producer issues its results as tagged device-scope stores and, without
+// waiting for them, adds one to part (its index mod 8) of the counter, in all
+// 8 replicas of that part; a consumer polls the 8 parts of its replica with 8
+// lanes of one wavefront, then reads the data, re-reading any word that still
+// carries an old tag.
 //   router rows    -> logits (64 replicas of the table)     + router counter
 //   shared gate/up -> shared part of the activation vector  + shared counter
 //   routed gate/up -> routed part of the activation vector  + routed counter
@@ -651,17 +665,17 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
 // logits.  Down workgroups fetch the shared expert's down weights at once and
 // the chosen experts' as soon as the routing is known.  They are also the
 // last to need the tag: each counts itself once it has seen the routed
-// counter complete, and the last one publishes the tag as the new epoch while
-// the others still compute, so the next launch needs no reset and the end of
-// this one waits for nothing.  Every counter word has its own cache lines
-// (4160 bytes apart).
+// counter complete, and that count is where every workgroup of the next
+// launch reads its tag from (launch_tag), so nothing is reset between
+// launches and nothing waits for an atomic's result.  Every counter word has
+// its own cache lines (4160 bytes apart).
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kSyncStride = 4160 / 4;  // words between counter words
-constexpr int kReps = 8;               // replicas of each polled counter
-constexpr int kEpochReps = 64, kLogitReplicas = 64;
-enum : int { kCntRouter = 0, kCntShared = 1, kCntRouted = 2, kCntDoneSub = 3, kCntDoneTop = 4, kNumCnt = 5 };
-constexpr int kSlotEpoch = kNumCnt * kReps;  // kEpochReps words
-constexpr int kSyncSlots = kSlotEpoch + kEpochReps;
+constexpr int kParts = 8;  // a stage counter is split in parts: producer i adds to part i % kParts
+constexpr int kReps = 8;   // each part is kept in replicas: a consumer polls replica (workgroup % kReps)
+constexpr int kLogitReplicas = 64;
+enum : int { kCntRouter = 0, kCntShared = 1, kCntRouted = 2, kCntDone = 3, kNumCnt = 4 };
+constexpr int kSyncSlots = kNumCnt * kParts * kReps;
 
 // Logit table entries: tag << 32 | fp32 bits.  Entries between replicas (the
 // table rounded up to 4 KB, so 4-entry runs of the last router rows fit, plus
@@ -674,36 +688,43 @@ __host__ __device__ inline size_t sync_area_bytes(int E) {
 __device__ __forceinline__ uint32_t* sync_slot(uint32_t* area, int slot) {
   return area + (size_t)slot * kSyncStride;
 }
-__device__ __forceinline__ uint32_t* counter_rep(uint32_t* area, int c, int r) {
-  return sync_slot(area, c * kReps + r);
+__device__ __forceinline__ uint32_t* counter_rep(uint32_t* area, int c, int part, int r) {
+  return sync_slot(area, (c * kParts + part) * kReps + r);
 }
 
 // Called by every thread once the workgroup's tagged device-scope stores have
-// been issued: adds one to every replica of counter c (lanes 0..7, no return
-// value).  The stores are not waited for: a consumer that sees the counter
-// complete reads the data and re-reads any word whose tag is not yet this
-// launch's.
-__device__ __forceinline__ void arrive(uint32_t* area, int c) {
+// been issued: producer i of a stage adds one to every replica of part
+// i % kParts of the stage's counter (lanes 0..kReps-1, no return value).
+// Atomics and polls on one address queue where they are performed, so each
+// address sees 1/kParts of the arrivals and 1/kReps of the pollers.  The
+// stores are not waited for: a consumer that sees the counter complete reads
+// the data and re-reads any word whose tag is not yet this launch's.
+__device__ __forceinline__ void arrive(uint32_t* area, int c, int i) {
   __syncthreads();
   if (threadIdx.x < kReps)
-    __hip_atomic_fetch_add(counter_rep(area, c, threadIdx.x), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(counter_rep(area, c, i % kParts, threadIdx.x), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Lane 0 polls replica (workgroup % 8) of counter c until it reaches
-// `target` (wrap-safe), pausing about 64 * SLEEP cycles between loads; ends
-// with a workgroup barrier.
+// Lanes 0..kParts-1 poll the parts of counter c of a stage with n producers
+// (replica workgroup % kReps) until each part has grown to tag * (its number
+// of producers) (wrap-safe), pausing about 64 * SLEEP cycles between rounds;
+// ends with a workgroup barrier.
 template <int SLEEP>
-__device__ __forceinline__ void wait_count(const LayerArgs& a, uint32_t* area, int c, uint32_t target) {
-  if (threadIdx.x == 0) {
-    const uint32_t* p = counter_rep(area, c, blockIdx.x % kReps);
-    uint32_t v = ld_dev(p);
-    for (uint32_t it = 0; (int32_t)(v - target) < 0; ++it) {
+__device__ __forceinline__ void wait_count(const LayerArgs& a, uint32_t* area, int c, uint32_t tag, int n) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    bool pending = lane < kParts && lane < n;
+    const uint32_t target = tag * (uint32_t)((n - lane + kParts - 1) / kParts);
+    const uint32_t* p = counter_rep(area, c, min(lane, kParts - 1), blockIdx.x % kReps);
+    if (pending) pending = (int32_t)(ld_dev(p) - target) < 0;
+    for (uint32_t it = 0; __ballot(pending) != 0; ++it) {
       if (it == kSpinLimit) {
-        atomicOr(a.err, kErrSyncTimeout);
+        if (lane == 0) atomicOr(a.err, kErrSyncTimeout);
         break;
       }
       __builtin_amdgcn_s_sleep(SLEEP);
-      v = ld_dev(p);
+      if (pending) pending = (int32_t)(ld_dev(p) - target) < 0;
     }
   }
   __syncthreads();
@@ -737,31 +758,47 @@ __device__ __forceinline__ void stage_logits_dev(const LayerArgs& a, const uint6
   __syncthreads();
 }
 
-// Down workgroup i of n has passed its last wait of this launch; the last of
-// them publishes `tag` as the epoch the next launch starts from.  Wavefront 0.
-__device__ __forceinline__ void done_with_tag(uint32_t* area, int i, int n, uint32_t tag) {
-  if (threadIdx.x < 64) {
-    bool last = false;
-    if (threadIdx.x == 0) {
-      const int j = i % kReps;
-      const uint32_t need = (uint32_t)((n - j + kReps - 1) / kReps);
-      if (atomicAdd(counter_rep(area, kCntDoneSub, j), 1u) == tag * need - 1u) {
-        const uint32_t groups = (uint32_t)min(n, kReps);
-        last = atomicAdd(counter_rep(area, kCntDoneTop, 0), 1u) == tag * groups - 1u;
-      }
-    }
-    if (__ballot(last)) st_dev(sync_slot(area, kSlotEpoch + (int)threadIdx.x), tag);
+// The launch tag comes from a 64-bit count of down workgroups that have
+// passed their last wait (8 parts, replica 0; part i % 8 for down workgroup
+// i).  A down workgroup passes it only after every other workgroup of the
+// launch has arrived somewhere, i.e. started and read the count, and the count
+// cannot reach the next multiple of nd before every down workgroup, the
+// reader included, has passed.  So every workgroup of launch n reads a total
+// in [(n-1) nd, n nd) and takes tag = total / nd + 1 = n, with no reset
+// between launches and no atomic whose result anyone waits for.  Called by
+// whole wavefronts (lanes 0..7 load the parts).
+__device__ __forceinline__ uint32_t launch_tag(uint32_t* area, int nd) {
+  const int lane = threadIdx.x & 63;
+  uint64_t v = lane < kParts
+                   ? ld_dev(reinterpret_cast<const uint64_t*>(counter_rep(area, kCntDone, lane, 0)))
+                   : 0ull;
+#pragma unroll
+  for (int m = 1; m < kParts; m <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+    v += ((uint64_t)hi << 32) | lo;
   }
+  const uint64_t total = ((uint64_t)__shfl((uint32_t)(v >> 32), 0, 64) << 32) | __shfl((uint32_t)v, 0, 64);
+  return (uint32_t)(total / (uint64_t)nd) + 1u;
+}
+// Down workgroup i has passed its last wait of this launch (one atomic, no
+// return value).
+__device__ __forceinline__ void count_done(uint32_t* area, int i) {
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(counter_rep(area, kCntDone, i % kParts, 0)), 1ull,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kFusedGuRows = 16;  // gate/up rows per workgroup of the fused kernel
 
 // Workgroups whose weight fetch does not wait for the routing (shared gate/up,
-// the shared part of the down projection) hold it back for a moment, so that
-// the router's loads, on the critical path, do not queue behind megabytes of
-// weights in the memory controllers.
+// the shared part of the down projection) hold it back for about 3 us (the
+// router's time), so that the router's loads, on the critical path, do not
+// queue behind megabytes of weights in the memory controllers; the shared
+// weights then stream while the routing is handed off.  Measured on the
+// d_model 2816 / 128-expert layer: 0 -> 18.8 us per token, 3 us -> 18.3 us,
+// 4 us or more -> slower again.
 #ifndef MOE_FUSED_BULK_DELAY
-#define MOE_FUSED_BULK_DELAY 4
+#define MOE_FUSED_BULK_DELAY 14
 #endif
 __device__ __forceinline__ void bulk_delay() {
   for (int i = 0; i < MOE_FUSED_BULK_DELAY; ++i) __builtin_amdgcn_s_sleep(8);  // 512 cycles each
@@ -775,44 +812,39 @@ __host__ __device__ inline int fused_groups(int E, int K, int d, int f, int fs, 
   return *NR + *NS + *NG + *ND;
 }
 
-// Stage groups [g0, g1) of the activation vector (tagged words, written by
-// other workgroups of this launch) into LDS as fp16 pairs from this
-// workgroup's copy with device-coherent loads, re-reading words that still
-// carry an old tag; then their group sums.  Ends with a workgroup barrier.
+// Stage groups [g0, g1) of the activation vector (written by other
+// workgroups of this launch, parity-tagged) into LDS from this workgroup's
+// copy with device-coherent loads, re-reading words that still carry the
+// previous launch's parity and clearing the parity bits; then their group
+// sums.  Ends with a workgroup barrier.
 __device__ __forceinline__ void stage_a_coherent(const LayerArgs& a, char* lds_a, float* asum, int g0, int g1,
                                                  uint32_t tag) {
   constexpr int WPG = a_words(1);
   const int tid = threadIdx.x;
-  const uint32_t t16 = tag & 0xFFFFu;
-  const auto rs = buf_rsrc(a.abuf);
-  const uint32_t base = (uint32_t)((blockIdx.x % kAReps) * a_rep_stride(a.fs + a.K * a.f) + (size_t)g0 * 64 * 4);
-  const int nw = (g1 - g0) * WPG;  // LDS words: 8 values = 32 bytes of tagged words each
-  constexpr int kAD = 3;
+  const uint32_t par = (tag & 1u) * 0x00010001u;
+  const auto rs = buf_rsrc(a.arep);
+  const uint32_t base = (uint32_t)((blockIdx.x % kAReps) * a_rep_stride(a.fs + a.K * a.f) + (size_t)g0 * 64 * 2);
+  const int nw = (g1 - g0) * WPG;  // 16-byte words
+  constexpr int kAD = 4;
   for (int j0 = 0; j0 < nw; j0 += kThreads * kAD) {
-    v4u lo[kAD], hi[kAD];
+    v4u v[kAD];
 #pragma unroll
-    for (int i = 0; i < kAD; ++i) {
-      const uint32_t off = base + (uint32_t)min(j0 + tid + kThreads * i, nw - 1) * 32;
-      lo[i] = ld_dev16(rs, off);
-      hi[i] = ld_dev16(rs, off + 16);
-    }
+    for (int i = 0; i < kAD; ++i) v[i] = ld_dev16(rs, base + (uint32_t)min(j0 + tid + kThreads * i, nw - 1) * 16);
 #pragma unroll
     for (int i = 0; i < kAD; ++i) {
       const int j = j0 + tid + kThreads * i;
       if (j < nw) {
-        const uint32_t off = base + (uint32_t)j * 32;
-        for (uint32_t it = 0; !(fresh4(lo[i], t16) && fresh4(hi[i], t16)); ++it) {
+        for (uint32_t it = 0; !fresh4(v[i], par); ++it) {
           if (it == kSpinLimit) {
             atomicOr(a.err, kErrSyncTimeout);
             break;
           }
           __builtin_amdgcn_s_sleep(1);
-          lo[i] = ld_dev16(rs, off);
-          hi[i] = ld_dev16(rs, off + 16);
+          v[i] = ld_dev16(rs, base + (uint32_t)j * 16);
         }
         v4u p;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) p[m] = (lo[i][m] >> 16) | (hi[i][m] & 0xFFFF0000u);
+        for (int m = 0; m < 4; ++m) p[m] = v[i][m] & 0xFFFEFFFEu;
         reinterpret_cast<v4u*>(lds_a)[a_slot(g0 * WPG + j, WPG)] = p;
       }
     }
@@ -845,7 +877,7 @@ __device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_
                            uint32_t* scratch, uint64_t* s_sel, float* s_w) {
   const int tid = threadIdx.x, r = tid & 7, jj = tid >> 3;
   uint32_t* area = a.counter;
-  const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + blockIdx.x % kEpochReps)) + 1u;
+  const uint32_t tag = launch_tag(area, nd);
   const int Gs = a.fs >> 6, Gf = a.f >> 6;
   const int NI = Gs + a.K * Gf, NRG = NI - Gs;
   constexpr int WPG = a_words(1);
@@ -864,7 +896,7 @@ __device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_
 #pragma unroll
   for (int s = 0; s < SS; ++s) load_slot(s, a.shared_blob, Gs, min(jj + 32 * s, Gs - 1), a.so.dq, a.so.dsb);
   // routing
-  wait_count<1>(a, area, kCntRouter, tag * members_router);
+  wait_count<1>(a, area, kCntRouter, tag, (int)members_router);
   stage_logits_dev<NE>(a, lrep, tag, s_logits);
   if (threadIdx.x < 64) {
     int id;
@@ -904,15 +936,15 @@ __device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_
     acc = fmaf(wgt, term, acc);
   };
   if (SS > 0) {  // shared part
-    wait_count<4>(a, area, kCntShared, tag * members_shared);
+    wait_count<4>(a, area, kCntShared, tag, (int)members_shared);
     stage_a_coherent(a, lds_a, asum, 0, Gs, tag);
 #pragma unroll
     for (int s = 0; s < SS; ++s)
       if (jj + 32 * s < Gs) accumulate(s, jj + 32 * s);
   }
-  wait_count<2>(a, area, kCntRouted, tag * members_routed);
-  done_with_tag(area, rb, nd, tag);
+  wait_count<2>(a, area, kCntRouted, tag, (int)members_routed);
   stage_a_coherent(a, lds_a, asum, Gs, NI, tag);
+  count_done(area, rb);  // after the staging: its loads would otherwise also wait for this atomic
 #pragma unroll
   for (int s = 0; s < SR; ++s)
     if (jj + 32 * s < NRG) accumulate(SS + s, Gs + jj + 32 * s);
@@ -945,7 +977,7 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
   const XStage S = carve_x(smem, a.d);
   if (b < NR) {
     __builtin_amdgcn_s_setprio(2);  // on the critical path: ahead of the streaming wavefronts
-    const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kEpochReps)) + 1u;
+    const uint32_t tag = launch_tag(area, ND);
     const float v = router_row<1>(a, 0, b * kWaves + (threadIdx.x >> 6), S);
     if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -955,22 +987,22 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
       st_dev16(rs, (uint32_t)off, v4u{__float_as_uint(s_w[0]), tag, __float_as_uint(s_w[1]), tag});
       st_dev16(rs, (uint32_t)off + 16, v4u{__float_as_uint(s_w[2]), tag, __float_as_uint(s_w[3]), tag});
     }
-    arrive(area, kCntRouter);
+    arrive(area, kCntRouter, b);
   } else if (b < NR + NS) {
-    const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kEpochReps)) + 1u;
+    const uint32_t tag = launch_tag(area, ND);
     XRegs xr;
     x_issue<1>(a, 0, xr);
     bulk_delay();
     gate_up_block<1, MAXI, kFusedGuRows, true>(a, 0, a.shared_blob, a.so, b - NR, 0, S, xr, tag);
-    arrive(area, kCntShared);
+    arrive(area, kCntShared, b - NR);
   } else if (b < NR + NS + NG) {
     const int g = b - NR - NS, RB = a.f / kFusedGuRows;
     const int k = g / RB, rb = g - k * RB;
-    const uint32_t tag = ld_dev(sync_slot(area, kSlotEpoch + b % kEpochReps)) + 1u;
+    const uint32_t tag = launch_tag(area, ND);
     XRegs xr;
     x_issue<1>(a, 0, xr);
     __builtin_amdgcn_s_setprio(2);
-    wait_count<1>(a, area, kCntRouter, tag * (uint32_t)NR);
+    wait_count<1>(a, area, kCntRouter, tag, NR);
     stage_logits_dev<NE>(a, my_rep, tag, s_logits);
     if (threadIdx.x < 64) {  // one wavefront finds the expert
       const int id = topk_kth<NE>(a, 0, s_logits, k);
@@ -981,7 +1013,7 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
     const int id = (int)scratch[0];
     gate_up_block<1, MAXI, kFusedGuRows, true>(a, 0, a.expert_base + (size_t)id * a.expert_stride, a.ro, rb,
                                                a.fs + k * a.f, S, xr, tag);
-    arrive(area, kCntRouted);
+    arrive(area, kCntRouted, g);
   } else {
     down_fused<SS, SR, NE>(a, b - NR - NS - NG, ND, (uint32_t)NR, (uint32_t)NS, (uint32_t)NG, my_rep, smem,
                            s_logits, scratch, s_sel, s_w);
@@ -1095,7 +1127,7 @@ hipError_t launch_fused(const LayerArgs& a, hipStream_t s) {
 
 size_t decode_lds_bytes_x(int d) { return x_stage_bytes(d); }
 size_t decode_sync_bytes(int E) { return sync_area_bytes(E); }
-size_t decode_abuf_bytes(int T, int F) { return std::max((size_t)T * F * 4, kAReps * a_rep_stride(F)); }
+size_t decode_arep_bytes(int F) { return kAReps * a_rep_stride(F); }
 size_t decode_lds_bytes_down(int F, int NI, int K, int act) { return down_lds_bytes(F, NI, K, act); }
 
 // The fused layer kernel serves one bf16 token on resident experts, when its

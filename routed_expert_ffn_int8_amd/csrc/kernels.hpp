@@ -62,6 +62,7 @@ struct LayerArgs {
   float* wts;          // [T][K]
   uint32_t* counter;   // synchronisation area of the fused kernel (decode_sync_bytes(E)), zeroed at creation
   void* abuf;          // [T][F] F = fs + K*f: fp16 pair-permuted (bf16 mode) or fp32
+  void* arep;          // fused kernel: its own parity-tagged copies of the activation vector
   int32_t* err;        // sticky error flags
   // options
   const int32_t* forced;  // [T][K] or null
