@@ -42,7 +42,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "prefill.hip", "device.hpp", "kernels.hpp", "layout.hpp"):
+    for name in ("decode.hip", "prefill.hip", "device.hpp", "kernels.hpp", "layout.hpp", "topk.hpp"):
         with open(os.path.join(ROOT, "routed_expert_ffn_int8_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -244,6 +244,11 @@ def run_prefill(args, M, torch, np, chunks=None, summary=False):
     out = torch.empty_like(x)
     ids = torch.empty((C * nch, w.K), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
 
     def call(i, s):
         o = M.fwd_opts(topk_ids=ids[i * C:(i + 1) * C], path=M.MOE_PATH_PREFILL)
