@@ -222,10 +222,12 @@ __device__ __forceinline__ float group_dot(const v4u& q0, const v4u& q1, const X
       const int word = g * 8 + h * 4 + m;
       if (ACT == 1) {
         const v4u xw = S.xp[g * 9 + h * 4 + m];
-        p = dot2_bf16(nib_pair<kMagicBf16>(w, 0), xw[0], p);
-        p = dot2_bf16(nib_pair<kMagicBf16>(w, 1), xw[1], p);
-        p = dot2_bf16(nib_pair<kMagicBf16>(w, 2), xw[2], p);
-        p = dot2_bf16(nib_pair<kMagicBf16>(w, 3), xw[3], p);
+        uint32_t np[4];
+        nib_pairs<kExpBf16>(w, np);
+        p = dot2_bf16(np[0], xw[0], p);
+        p = dot2_bf16(np[1], xw[1], p);
+        p = dot2_bf16(np[2], xw[2], p);
+        p = dot2_bf16(np[3], xw[3], p);
       } else {
         const float4 x0 = reinterpret_cast<const float4*>(S.xf)[word * 2];
         const float4 x1 = reinterpret_cast<const float4*>(S.xf)[word * 2 + 1];
@@ -591,10 +593,12 @@ __device__ void down_block(const LayerArgs& a, int t, int rb, const uint64_t* se
             const uint32_t w = q[m];
             if (ACT == 1) {
               const v4u av = reinterpret_cast<const v4u*>(lds_a)[it * 9 + h * 4 + m];
-              p = dot2_f16(nib_pair<kMagicF16>(w, 0), av[0], p);
-              p = dot2_f16(nib_pair<kMagicF16>(w, 1), av[1], p);
-              p = dot2_f16(nib_pair<kMagicF16>(w, 2), av[2], p);
-              p = dot2_f16(nib_pair<kMagicF16>(w, 3), av[3], p);
+              uint32_t np[4];
+              nib_pairs<kExpF16>(w, np);
+              p = dot2_f16(np[0], av[0], p);
+              p = dot2_f16(np[1], av[1], p);
+              p = dot2_f16(np[2], av[2], p);
+              p = dot2_f16(np[3], av[3], p);
             } else {
               const float4 x0 = reinterpret_cast<const float4*>(lds_a)[it * 17 + (h * 4 + m) * 2];
               const float4 x1 = reinterpret_cast<const float4*>(lds_a)[it * 17 + (h * 4 + m) * 2 + 1];
@@ -925,10 +929,12 @@ __device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_
       for (int m = 0; m < 4; ++m) {
         const uint32_t w = q[m];
         const v4u av = reinterpret_cast<const v4u*>(lds_a)[it * (WPG + 1) + h * 4 + m];
-        pp = dot2_f16(nib_pair<kMagicF16>(w, 0), av[0], pp);
-        pp = dot2_f16(nib_pair<kMagicF16>(w, 1), av[1], pp);
-        pp = dot2_f16(nib_pair<kMagicF16>(w, 2), av[2], pp);
-        pp = dot2_f16(nib_pair<kMagicF16>(w, 3), av[3], pp);
+        uint32_t np[4];
+        nib_pairs<kExpF16>(w, np);
+        pp = dot2_f16(np[0], av[0], pp);
+        pp = dot2_f16(np[1], av[1], pp);
+        pp = dot2_f16(np[2], av[2], pp);
+        pp = dot2_f16(np[3], av[3], pp);
       }
     }
     const float term = group_term<1>(pp, sb[s], asum[it], 1024.f);

@@ -18,15 +18,21 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
 }
 
-// Nibbles m and m+4 of a packed word as a pair of 16-bit floats whose value
-// is OFFSET + q: 0x4300|q is the bf16 128+q, 0x6400|q is the fp16 1024+q
-// (the nibble lands in the low mantissa bits, whose weight is exactly 1).
-template <uint32_t MAGIC>
-__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int m) {
-  return ((w >> (4 * m)) & 0x000F000Fu) | MAGIC;
+// The 8 nibbles of a packed word as 4 pairs of 16-bit floats whose values
+// are OFFSET + q: pair m holds nibbles m and m+4 (low, high half).  The high
+// byte of each half is the exponent byte E (0x43: bf16 128 + q; 0x64: fp16
+// 1024 + q), the nibble lands in the low mantissa bits, whose weight is
+// exactly 1.  One shift and one and-or per pair (the first needs no shift).
+template <uint32_t E>
+__device__ __forceinline__ void nib_pairs(uint32_t w, uint32_t (&p)[4]) {
+  constexpr uint32_t M = (E << 8) * 0x00010001u;
+  p[0] = (w & 0x000F000Fu) | M;
+  p[1] = ((w >> 4) & 0x000F000Fu) | M;
+  p[2] = ((w >> 8) & 0x000F000Fu) | M;
+  p[3] = ((w >> 12) & 0x000F000Fu) | M;
 }
-constexpr uint32_t kMagicBf16 = 0x43004300u;  // 128 + q
-constexpr uint32_t kMagicF16 = 0x64006400u;   // 1024 + q
+constexpr uint32_t kExpBf16 = 0x43u;  // bf16 128 + q
+constexpr uint32_t kExpF16 = 0x64u;   // fp16 1024 + q
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {  // round to nearest even (finite inputs)

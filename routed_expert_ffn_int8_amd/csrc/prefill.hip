@@ -39,7 +39,6 @@ __device__ __forceinline__ T ldg(const void* p) {
 constexpr int kTile = 16;      // tokens per MFMA tile
 constexpr int kPWaves = 8;     // wavefronts per prefill GEMM workgroup
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kRowsPerWG = 16 * kPWaves;  // weight rows per workgroup
 
 // ------------------------------------------------------------ sort + tiles
 // Exclusive prefix sum of one int per thread over the workgroup (up to 1024
@@ -311,10 +310,12 @@ __device__ void stage_rows(int width, const uint16_t* const* rows, v4u* lds, flo
 
 __device__ __forceinline__ bf16x8 b_operand(uint32_t w) {
   v4u v;
-  v[0] = nib_pair<kMagicBf16>(w, 0);
-  v[1] = nib_pair<kMagicBf16>(w, 1);
-  v[2] = nib_pair<kMagicBf16>(w, 2);
-  v[3] = nib_pair<kMagicBf16>(w, 3);
+  uint32_t np[4];
+  nib_pairs<kExpBf16>(w, np);
+  v[0] = np[0];
+  v[1] = np[1];
+  v[2] = np[2];
+  v[3] = np[3];
   return __builtin_bit_cast(bf16x8, v);
 }
 
@@ -325,49 +326,66 @@ __device__ __forceinline__ void group_epilogue(f32x4& acc, const f32x4& t, uint3
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, t[i], fmaf(bb, xs4[i], acc[i]));
 }
 
-constexpr int kPre = 6;  // groups of weights in flight per lane
+#ifndef MOE_PF_PRE
+#define MOE_PF_PRE 2
+#endif
+constexpr int kPre = MOE_PF_PRE;  // groups of weights in flight per lane (gate/up)
+
+// Raw buffer resource over an expert blob (no range check: every offset is
+// inside the blob by construction) and a 4-byte load at voffset + soffset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t* blob) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ uint32_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
 
 // ------------------------------------------------------------ gate/up GEMM
-// One workgroup: one (expert, 16-token tile) x 128 rows of gate and up.
-// Lane (n = lane & 15, kb = lane >> 4) of wavefront w owns weight row
-// n0 + n; for MFMA j of a group it feeds word 4j + kb of the row (B operand)
-// and of the tile rows (A operand, from LDS), so both operands share one
-// order of the 64 k values.
+// One workgroup: one (expert, 16-token tile) x 256 rows of gate and up, two
+// 16-row tiles per wavefront sharing each A operand read, so that the chunk's
+// (expert, tile) pairs fit the GPU in one round of workgroups.  Lane
+// (n = lane & 15, kb = lane >> 4) of wavefront w owns weight row n0 + 16 t + n
+// of tile t; for MFMA j of a group it feeds word 4j + kb of the row (B
+// operand) and of the tile rows (A operand, from LDS), so both operands share
+// one order of the 64 k values.
+#ifndef MOE_GU_TILES
+#define MOE_GU_TILES 1
+#endif
+constexpr int kGuTiles = MOE_GU_TILES;
+constexpr int kGuRowsPerWG = 16 * kGuTiles * kPWaves;
+
 template <int STG>
 __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
   extern __shared__ __align__(16) char smem[];
   const LayerArgs& a = p.L;
-  const int nch = (max(a.f, a.fs) + kRowsPerWG - 1) / kRowsPerWG;
+  const int nch = (max(a.f, a.fs) + kGuRowsPerWG - 1) / kGuRowsPerWG;
   const int tile = blockIdx.x / nch, ch = blockIdx.x - tile * nch;
   const TileInfo ti = tile_info(p, tile);
   if (!ti.valid) return;
   const int fdim = ti.shared ? a.fs : a.f;
-  if (ch * kRowsPerWG >= fdim) return;
+  if (ch * kGuRowsPerWG >= fdim) return;
   const int d = a.d, G = d >> 6, W = d >> 3;
   v4u* xs_lds = reinterpret_cast<v4u*>(smem);
   float* gsum = reinterpret_cast<float*>(smem + (size_t)kTile * (W + 1) * 16);
   const BlobOffsets& o = ti.shared ? a.so : a.ro;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kb = lane >> 4;
-  const int n0 = ch * kRowsPerWG + wave * 16;
-  const bool wave_on = n0 < fdim;
-  const int row = min(n0, fdim - 16) + n;
-  const int rb = row >> 3, r = row & 7;
-  const uint8_t* gq = ti.blob + o.gq + (size_t)rb * G * 256 + r * 16 + kb * 4;
-  const uint8_t* uq = ti.blob + o.uq + (size_t)rb * G * 256 + r * 16 + kb * 4;
-  const uint32_t* gsb = reinterpret_cast<const uint32_t*>(ti.blob + o.gsb) + (size_t)rb * G * 8 + r;  // + g * 8
-  const uint32_t* usb = reinterpret_cast<const uint32_t*>(ti.blob + o.usb) + (size_t)rb * G * 8 + r;
-  // weights of the first kPre groups go out before the activations are staged
-  uint32_t wg0[kPre], wg1[kPre], wu0[kPre], wu1[kPre], sg[kPre], su[kPre];
+  const int n0 = ch * kGuRowsPerWG + wave * 16 * kGuTiles;
+  // Buffer loads: the blob is the resource, a per-lane offset is computed
+  // once and the group's offset is a uniform (scalar) operand, so a load
+  // costs no vector address arithmetic.
+  const auto rs = blob_rsrc(ti.blob);
+  uint32_t vgq[kGuTiles], vuq[kGuTiles], vgs[kGuTiles], vus[kGuTiles];
 #pragma unroll
-  for (int i = 0; i < kPre; ++i) {
-    const int g = min(i, G - 1);
-    wg0[i] = ldg<uint32_t>(gq + (size_t)g * 256);
-    wg1[i] = ldg<uint32_t>(gq + (size_t)g * 256 + 128);
-    wu0[i] = ldg<uint32_t>(uq + (size_t)g * 256);
-    wu1[i] = ldg<uint32_t>(uq + (size_t)g * 256 + 128);
-    sg[i] = ldg<uint32_t>(gsb + g * 8);
-    su[i] = ldg<uint32_t>(usb + g * 8);
+  for (int t = 0; t < kGuTiles; ++t) {
+    const int row = min(n0 + 16 * t, fdim - 16) + n;
+    const int rb = row >> 3, r = row & 7;
+    const uint32_t vq = (uint32_t)rb * G * 256 + r * 16 + kb * 4;  // + g * 256
+    const uint32_t vsb = ((uint32_t)rb * G * 8 + r) * 4;           // + g * 32
+    vgq[t] = o.gq + vq;
+    vuq[t] = o.uq + vq;
+    vgs[t] = o.gsb + vsb;
+    vus[t] = o.usb + vsb;
   }
   __shared__ const uint16_t* rows[kTile];
   if (threadIdx.x < kTile) {
@@ -376,9 +394,29 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
     rows[m] = tok < 0 ? nullptr : static_cast<const uint16_t*>(p.xact) + (size_t)tok * d;
   }
   __syncthreads();
+  // The token rows are staged before any weight is requested: a wavefront's
+  // loads complete in order, so staging behind a first batch of weight loads
+  // would wait for them, and the grid's first batch is tens of megabytes.
   stage_rows<true, STG>(d, rows, xs_lds, gsum);
-  if (!wave_on) return;  // no barrier follows
-  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  if (n0 >= fdim) return;  // no barrier follows
+  uint32_t wg0[kPre][kGuTiles], wg1[kPre][kGuTiles], wu0[kPre][kGuTiles], wu1[kPre][kGuTiles];
+  uint32_t sg[kPre][kGuTiles], su[kPre][kGuTiles];
+  auto fetch = [&](int i, uint32_t g) {
+#pragma unroll
+    for (int t = 0; t < kGuTiles; ++t) {
+      wg0[i][t] = bload(rs, vgq[t], g * 256);
+      wg1[i][t] = bload(rs, vgq[t] + 128, g * 256);
+      wu0[i][t] = bload(rs, vuq[t], g * 256);
+      wu1[i][t] = bload(rs, vuq[t] + 128, g * 256);
+      sg[i][t] = bload(rs, vgs[t], g * 32);
+      su[i][t] = bload(rs, vus[t], g * 32);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) fetch(i, (uint32_t)min(i, G - 1));
+  f32x4 accg[kGuTiles], accu[kGuTiles];
+#pragma unroll
+  for (int t = 0; t < kGuTiles; ++t) accg[t] = accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const v4u* arow = xs_lds + n * (W + 1);  // A operand: tile row m = lane & 15
   // Branch-free body (clamped group index, zero factor past the end) so the
@@ -391,45 +429,51 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
       const float on = g < G ? 1.f : 0.f;
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + kb]);
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 4 + kb]);
-      f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg0[i]), zero, 0, 0, 0);
-      tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg1[i]), tg, 0, 0, 0);
-      f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu0[i]), zero, 0, 0, 0);
-      tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu1[i]), tu, 0, 0, 0);
       const float* xs4 = gsum + gc * kTile + 4 * kb;
-      group_epilogue(accg, tg, sg[i], xs4, on);
-      group_epilogue(accu, tu, su[i], xs4, on);
-      // refill this slot with group g + kPre
-      const int gn = min(g + kPre, G - 1);
-      wg0[i] = ldg<uint32_t>(gq + (size_t)gn * 256);
-      wg1[i] = ldg<uint32_t>(gq + (size_t)gn * 256 + 128);
-      wu0[i] = ldg<uint32_t>(uq + (size_t)gn * 256);
-      wu1[i] = ldg<uint32_t>(uq + (size_t)gn * 256 + 128);
-      sg[i] = ldg<uint32_t>(gsb + gn * 8);
-      su[i] = ldg<uint32_t>(usb + gn * 8);
+#pragma unroll
+      for (int t = 0; t < kGuTiles; ++t) {
+        f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg0[i][t]), zero, 0, 0, 0);
+        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg1[i][t]), tg, 0, 0, 0);
+        f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu0[i][t]), zero, 0, 0, 0);
+        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu1[i][t]), tu, 0, 0, 0);
+        group_epilogue(accg[t], tg, sg[i][t], xs4, on);
+        group_epilogue(accu[t], tu, su[i][t], xs4, on);
+      }
+      fetch(i, (uint32_t)min(g + kPre, G - 1));  // refill this slot with group g + kPre
     }
   }
   // D layout: lane holds column n (weight row) for tile rows 4*kb + i
   uint16_t* dst = ti.shared ? p.As : p.A;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * kb + i;
-    if (m < ti.m_valid) {
-      const float v = silu(accg[i]) * accu[i];
-      const size_t grow = (size_t)(ti.base + ti.tt * kTile + m);
-      const int c = n0 + n, j = c >> 3, q = c & 7;
-      dst[grow * fdim + j * 8 + (q & 3) * 2 + (q >> 2)] = f32_to_bf16(v);
+  for (int t = 0; t < kGuTiles; ++t) {
+    const int c = n0 + 16 * t + n;
+    if (n0 + 16 * t >= fdim) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * kb + i;
+      if (m < ti.m_valid) {
+        const float v = silu(accg[t][i]) * accu[t][i];
+        const size_t grow = (size_t)(ti.base + ti.tt * kTile + m);
+        const int j = c >> 3, q = c & 7;
+        dst[grow * fdim + j * 8 + (q & 3) * 2 + (q >> 2)] = f32_to_bf16(v);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------ down GEMM
-// One workgroup: one (expert, 16-token tile) x 128 rows of the down
-// projection; outputs fp32 rows in grouped order (shared: token order).
+// One workgroup: one (expert, 16-token tile) x 256 rows of the down
+// projection, two 16-row tiles per wavefront sharing each A operand read;
+// outputs fp32 rows in grouped order (shared: token order).
+constexpr int kDnTiles = 2;                              // 16-row tiles per wavefront
+constexpr int kDnRowsPerWG = 16 * kDnTiles * kPWaves;    // 256
+constexpr int kDnPre = 4;                                // groups in flight per lane
+
 template <int STG>
 __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   extern __shared__ __align__(16) char smem[];
   const LayerArgs& a = p.L;
-  const int nch = (a.d + kRowsPerWG - 1) / kRowsPerWG;
+  const int nch = (a.d + kDnRowsPerWG - 1) / kDnRowsPerWG;
   const int tile = blockIdx.x / nch, ch = blockIdx.x - tile * nch;
   const TileInfo ti = tile_info(p, tile);
   if (!ti.valid) return;
@@ -440,19 +484,15 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   const BlobOffsets& o = ti.shared ? a.so : a.ro;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kb = lane >> 4;
-  const int n0 = ch * kRowsPerWG + wave * 16;
-  const bool wave_on = n0 < a.d;
-  const int row = min(n0, a.d - 16) + n;
-  const int rb = row >> 3, r = row & 7;
-  const uint8_t* dq = ti.blob + o.dq + (size_t)rb * G * 256 + r * 16 + kb * 4;
-  const uint32_t* dsb = reinterpret_cast<const uint32_t*>(ti.blob + o.dsb) + (size_t)rb * G * 8 + r;  // + g * 8
-  uint32_t w0[kPre], w1[kPre], sb[kPre];
+  const int n0 = ch * kDnRowsPerWG + wave * 16 * kDnTiles;  // tile t covers rows n0 + 16 t ..
+  const auto rs = blob_rsrc(ti.blob);
+  uint32_t vq[kDnTiles], vs[kDnTiles];
 #pragma unroll
-  for (int i = 0; i < kPre; ++i) {
-    const int g = min(i, G - 1);
-    w0[i] = ldg<uint32_t>(dq + (size_t)g * 256);
-    w1[i] = ldg<uint32_t>(dq + (size_t)g * 256 + 128);
-    sb[i] = ldg<uint32_t>(dsb + g * 8);
+  for (int t = 0; t < kDnTiles; ++t) {
+    const int row = min(n0 + 16 * t, a.d - 16) + n;
+    const int rb = row >> 3, r = row & 7;
+    vq[t] = o.dq + (uint32_t)rb * G * 256 + r * 16 + kb * 4;  // + g * 256
+    vs[t] = o.dsb + ((uint32_t)rb * G * 8 + r) * 4;           // + g * 32
   }
   __shared__ const uint16_t* rows[kTile];
   if (threadIdx.x < kTile) {
@@ -461,33 +501,58 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
     rows[m] = (m >= ti.m_valid) ? nullptr : src + (size_t)(ti.base + ti.tt * kTile + m) * fdim;
   }
   __syncthreads();
-  stage_rows<false, STG>(fdim, rows, as_lds, gsum);
-  if (!wave_on) return;  // no barrier follows
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  stage_rows<false, STG>(fdim, rows, as_lds, gsum);  // before any weight request, as in gate/up
+  if (n0 >= a.d) return;  // no barrier follows
+  uint32_t w0[kDnPre][kDnTiles], w1[kDnPre][kDnTiles], sb[kDnPre][kDnTiles];
+#pragma unroll
+  for (int i = 0; i < kDnPre; ++i) {
+    const uint32_t g = (uint32_t)min(i, G - 1);
+#pragma unroll
+    for (int t = 0; t < kDnTiles; ++t) {
+      w0[i][t] = bload(rs, vq[t], g * 256);
+      w1[i][t] = bload(rs, vq[t] + 128, g * 256);
+      sb[i][t] = bload(rs, vs[t], g * 32);
+    }
+  }
+  f32x4 acc[kDnTiles];
+#pragma unroll
+  for (int t = 0; t < kDnTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const v4u* arow = as_lds + n * (W + 1);
-  for (int g0 = 0; g0 < G; g0 += kPre) {
+  for (int g0 = 0; g0 < G; g0 += kDnPre) {
 #pragma unroll
-    for (int i = 0; i < kPre; ++i) {
+    for (int i = 0; i < kDnPre; ++i) {
       const int g = g0 + i;
       const int gc = min(g, G - 1);
       const float on = g < G ? 1.f : 0.f;
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + kb]);
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 4 + kb]);
-      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w0[i]), zero, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w1[i]), t, 0, 0, 0);
-      group_epilogue(acc, t, sb[i], gsum + gc * kTile + 4 * kb, on);
-      const int gn = min(g + kPre, G - 1);
-      w0[i] = ldg<uint32_t>(dq + (size_t)gn * 256);
-      w1[i] = ldg<uint32_t>(dq + (size_t)gn * 256 + 128);
-      sb[i] = ldg<uint32_t>(dsb + gn * 8);
+      const float* xs4 = gsum + gc * kTile + 4 * kb;
+#pragma unroll
+      for (int t = 0; t < kDnTiles; ++t) {
+        f32x4 m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w0[i][t]), zero, 0, 0, 0);
+        m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w1[i][t]), m, 0, 0, 0);
+        group_epilogue(acc[t], m, sb[i][t], xs4, on);
+      }
+      const uint32_t gn = (uint32_t)min(g + kDnPre, G - 1);
+#pragma unroll
+      for (int t = 0; t < kDnTiles; ++t) {
+        w0[i][t] = bload(rs, vq[t], gn * 256);
+        w1[i][t] = bload(rs, vq[t] + 128, gn * 256);
+        sb[i][t] = bload(rs, vs[t], gn * 32);
+      }
     }
   }
   float* dst = ti.shared ? p.Ys : p.Y;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * kb + i;
-    if (m < ti.m_valid) dst[(size_t)(ti.base + ti.tt * kTile + m) * a.d + n0 + n] = acc[i];
+  for (int t = 0; t < kDnTiles; ++t) {
+    const int c0 = n0 + 16 * t;
+    if (c0 >= a.d) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * kb + i;
+      if (m < ti.m_valid) dst[(size_t)(ti.base + ti.tt * kTile + m) * a.d + c0 + n] = acc[t][i];
+    }
   }
 }
 
@@ -635,7 +700,7 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
                  C, a.K, a.E, p.counts, p.offsets, p.perm, p.inv, p.tiles, a.fs > 0 ? 1 : 0);
     // 3. gate/up, 4. down, 5. combine
     const size_t mt = max_tiles(C, a.K, a.E);
-    const int nch_gu = (((a.f > a.fs) ? a.f : a.fs) + kRowsPerWG - 1) / kRowsPerWG;
+    const int nch_gu = (((a.f > a.fs) ? a.f : a.fs) + kGuRowsPerWG - 1) / kGuRowsPerWG;
     const size_t lds_gu = prefill_lds_gate_up(a.d);
     const dim3 g_gu((unsigned)(mt * nch_gu)), blk(kPThreads);
     switch (stage_words(a.d)) {
@@ -646,7 +711,7 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
       default: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<16>, g_gu, blk, lds_gu, s, p); break;
     }
     const int fmax = (a.f > a.fs) ? a.f : a.fs;
-    const int nch_dn = (a.d + kRowsPerWG - 1) / kRowsPerWG;
+    const int nch_dn = (a.d + kDnRowsPerWG - 1) / kDnRowsPerWG;
     const size_t lds_dn = (size_t)kTile * (fmax / 8 + 1) * 16 + (size_t)(fmax / 64) * kTile * 4;
     const dim3 g_dn((unsigned)(mt * nch_dn));
     switch (stage_words(fmax)) {
