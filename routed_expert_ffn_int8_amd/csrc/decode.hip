@@ -40,6 +40,12 @@ namespace {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
+// Bound of every wait loop for another workgroup's results (each round
+// sleeps and reloads, so this is well above 100 ms; the waits that occur
+// take microseconds): past it the workgroup sets an error flag and goes on,
+// so a broken hand-off ends the kernel instead of hanging it.
+constexpr uint32_t kSpinLimit = 1u << 18;
+
 // Load through the global address space (the pointers come from tables, so
 // the compiler cannot infer it and would emit flat loads).
 template <class T>
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
 __host__ __device__ constexpr int a_words(int act) { return act == 1 ? 8 : 16; }
 __host__ __device__ inline size_t down_lds_bytes(int F, int NI, int K, int act) {
   (void)F;
-  return (size_t)NI * (a_words(act) + 1) * 16 + (size_t)NI * 4 + (size_t)K * 4 + 32 * 4;
+  return (size_t)NI * (a_words(act) + 1) * 16 + (size_t)NI * 4 + (size_t)K * 4 + 40 * 4;
 }
 __device__ __forceinline__ int a_slot(int j, int wpg) { return (j / wpg) * (wpg + 1) + j % wpg; }
 
@@ -673,7 +679,6 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
 // launch reads its tag from (launch_tag), so nothing is reset between
 // launches and nothing waits for an atomic's result.  Every counter word has
 // its own cache lines (4160 bytes apart).
-constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kSyncStride = 4160 / 4;  // words between counter words
 constexpr int kParts = 8;  // a stage counter is split in parts: producer i adds to part i % kParts
 constexpr int kReps = 8;   // each part is kept in replicas: a consumer polls replica (workgroup % kReps)
@@ -949,7 +954,12 @@ __device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_
       if (jj + 32 * s < Gs) accumulate(s, jj + 32 * s);
   }
   wait_count<2>(a, area, kCntRouted, tag, (int)members_routed);
+  // the residual row, loaded with the activations and parked in LDS (in
+  // place of a load whose latency would come at the very end)
+  uint32_t hres = 0;
+  if (tid < 8 && a.resid) hres = (uint32_t)ldg<uint16_t>(static_cast<const uint16_t*>(a.resid) + rb * 8 + r) << 16;
   stage_a_coherent(a, lds_a, asum, Gs, NI, tag);
+  if (tid < 8) red[32 + r] = __uint_as_float(hres);
   count_done(area, rb);  // after the staging: its loads would otherwise also wait for this atomic
 #pragma unroll
   for (int s = 0; s < SR; ++s)
@@ -961,7 +971,7 @@ __device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_
     const float y = (red[r] + red[8 + r]) + (red[16 + r] + red[24 + r]);
     const int row = rb * 8 + r;
     float v = y;
-    if (a.resid) v += bf16_to_f32(static_cast<const uint16_t*>(a.resid)[row]);
+    if (a.resid) v += red[32 + r];
     static_cast<uint16_t*>(a.out)[row] = f32_to_bf16(v);
   }
 }

@@ -37,7 +37,10 @@ __device__ __forceinline__ T ldg(const void* p) {
 }
 
 constexpr int kTile = 16;      // tokens per MFMA tile
-constexpr int kPWaves = 8;     // wavefronts per prefill GEMM workgroup
+#ifndef MOE_PF_WAVES
+#define MOE_PF_WAVES 8
+#endif
+constexpr int kPWaves = MOE_PF_WAVES;  // wavefronts per prefill GEMM workgroup
 constexpr int kPThreads = 64 * kPWaves;
 
 // ------------------------------------------------------------ sort + tiles
@@ -327,7 +330,7 @@ __device__ __forceinline__ void group_epilogue(f32x4& acc, const f32x4& t, uint3
 }
 
 #ifndef MOE_PF_PRE
-#define MOE_PF_PRE 2
+#define MOE_PF_PRE 4
 #endif
 constexpr int kPre = MOE_PF_PRE;  // groups of weights in flight per lane (gate/up)
 
@@ -339,15 +342,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t* blob)
 __device__ __forceinline__ uint32_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
+__device__ __forceinline__ v2u bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+}
 
 // ------------------------------------------------------------ gate/up GEMM
 // One workgroup: one (expert, 16-token tile) x 256 rows of gate and up, two
 // 16-row tiles per wavefront sharing each A operand read, so that the chunk's
 // (expert, tile) pairs fit the GPU in one round of workgroups.  Lane
 // (n = lane & 15, kb = lane >> 4) of wavefront w owns weight row n0 + 16 t + n
-// of tile t; for MFMA j of a group it feeds word 4j + kb of the row (B
+// of tile t; for MFMA j of a group it feeds word 2 kb + j of the row (B
 // operand) and of the tile rows (A operand, from LDS), so both operands share
-// one order of the 64 k values.
+// one order of the 64 k values, and a lane's two words of a group are
+// adjacent in the packed layout: one 8-byte load.
 #ifndef MOE_GU_TILES
 #define MOE_GU_TILES 1
 #endif
@@ -380,7 +387,7 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
   for (int t = 0; t < kGuTiles; ++t) {
     const int row = min(n0 + 16 * t, fdim - 16) + n;
     const int rb = row >> 3, r = row & 7;
-    const uint32_t vq = (uint32_t)rb * G * 256 + r * 16 + kb * 4;  // + g * 256
+    const uint32_t vq = (uint32_t)rb * G * 256 + (kb >> 1) * 128 + r * 16 + (kb & 1) * 8;  // + g * 256
     const uint32_t vsb = ((uint32_t)rb * G * 8 + r) * 4;           // + g * 32
     vgq[t] = o.gq + vq;
     vuq[t] = o.uq + vq;
@@ -399,21 +406,23 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
   // would wait for them, and the grid's first batch is tens of megabytes.
   stage_rows<true, STG>(d, rows, xs_lds, gsum);
   if (n0 >= fdim) return;  // no barrier follows
-  uint32_t wg0[kPre][kGuTiles], wg1[kPre][kGuTiles], wu0[kPre][kGuTiles], wu1[kPre][kGuTiles];
+  v2u wg[kPre][kGuTiles], wu[kPre][kGuTiles];
   uint32_t sg[kPre][kGuTiles], su[kPre][kGuTiles];
   auto fetch = [&](int i, uint32_t g) {
 #pragma unroll
     for (int t = 0; t < kGuTiles; ++t) {
-      wg0[i][t] = bload(rs, vgq[t], g * 256);
-      wg1[i][t] = bload(rs, vgq[t] + 128, g * 256);
-      wu0[i][t] = bload(rs, vuq[t], g * 256);
-      wu1[i][t] = bload(rs, vuq[t] + 128, g * 256);
+      wg[i][t] = bload2(rs, vgq[t], g * 256);
+      wu[i][t] = bload2(rs, vuq[t], g * 256);
       sg[i][t] = bload(rs, vgs[t], g * 32);
       su[i][t] = bload(rs, vus[t], g * 32);
     }
   };
 #pragma unroll
-  for (int i = 0; i < kPre; ++i) fetch(i, (uint32_t)min(i, G - 1));
+  for (int i = 0; i < kPre; ++i) {  // in slot order (see the refill below)
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(i, (uint32_t)min(i, G - 1));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 accg[kGuTiles], accu[kGuTiles];
 #pragma unroll
   for (int t = 0; t < kGuTiles; ++t) accg[t] = accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -427,19 +436,24 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
       const int g = g0 + i;
       const int gc = min(g, G - 1);
       const float on = g < G ? 1.f : 0.f;
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + kb]);
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 4 + kb]);
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 2 * kb]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 2 * kb + 1]);
       const float* xs4 = gsum + gc * kTile + 4 * kb;
 #pragma unroll
       for (int t = 0; t < kGuTiles; ++t) {
-        f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg0[i][t]), zero, 0, 0, 0);
-        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg1[i][t]), tg, 0, 0, 0);
-        f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu0[i][t]), zero, 0, 0, 0);
-        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu1[i][t]), tu, 0, 0, 0);
+        f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg[i][t].x), zero, 0, 0, 0);
+        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg[i][t].y), tg, 0, 0, 0);
+        f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu[i][t].x), zero, 0, 0, 0);
+        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu[i][t].y), tu, 0, 0, 0);
         group_epilogue(accg[t], tg, sg[i][t], xs4, on);
         group_epilogue(accu[t], tu, su[i][t], xs4, on);
       }
-      fetch(i, (uint32_t)min(g + kPre, G - 1));  // refill this slot with group g + kPre
+      // refill this slot with group g + kPre, as one batch after this
+      // group's products: slots then complete in order, so the next
+      // group's wait leaves the other slots' loads in flight
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(i, (uint32_t)min(g + kPre, G - 1));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // D layout: lane holds column n (weight row) for tile rows 4*kb + i
@@ -491,7 +505,7 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   for (int t = 0; t < kDnTiles; ++t) {
     const int row = min(n0 + 16 * t, a.d - 16) + n;
     const int rb = row >> 3, r = row & 7;
-    vq[t] = o.dq + (uint32_t)rb * G * 256 + r * 16 + kb * 4;  // + g * 256
+    vq[t] = o.dq + (uint32_t)rb * G * 256 + (kb >> 1) * 128 + r * 16 + (kb & 1) * 8;  // + g * 256 (as gate/up)
     vs[t] = o.dsb + ((uint32_t)rb * G * 8 + r) * 4;           // + g * 32
   }
   __shared__ const uint16_t* rows[kTile];
@@ -503,17 +517,21 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   __syncthreads();
   stage_rows<false, STG>(fdim, rows, as_lds, gsum);  // before any weight request, as in gate/up
   if (n0 >= a.d) return;  // no barrier follows
-  uint32_t w0[kDnPre][kDnTiles], w1[kDnPre][kDnTiles], sb[kDnPre][kDnTiles];
-#pragma unroll
-  for (int i = 0; i < kDnPre; ++i) {
-    const uint32_t g = (uint32_t)min(i, G - 1);
+  v2u w[kDnPre][kDnTiles];
+  uint32_t sb[kDnPre][kDnTiles];
+  // slot i's loads go out as one batch, slots in order (scheduling
+  // barriers), so each group waits only for its own slot
+  auto fetch = [&](int i, uint32_t g) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kDnTiles; ++t) {
-      w0[i][t] = bload(rs, vq[t], g * 256);
-      w1[i][t] = bload(rs, vq[t] + 128, g * 256);
+      w[i][t] = bload2(rs, vq[t], g * 256);
       sb[i][t] = bload(rs, vs[t], g * 32);
     }
-  }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int i = 0; i < kDnPre; ++i) fetch(i, (uint32_t)min(i, G - 1));
   f32x4 acc[kDnTiles];
 #pragma unroll
   for (int t = 0; t < kDnTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -525,22 +543,16 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
       const int g = g0 + i;
       const int gc = min(g, G - 1);
       const float on = g < G ? 1.f : 0.f;
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + kb]);
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 4 + kb]);
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 2 * kb]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 2 * kb + 1]);
       const float* xs4 = gsum + gc * kTile + 4 * kb;
 #pragma unroll
       for (int t = 0; t < kDnTiles; ++t) {
-        f32x4 m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w0[i][t]), zero, 0, 0, 0);
-        m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w1[i][t]), m, 0, 0, 0);
+        f32x4 m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w[i][t].x), zero, 0, 0, 0);
+        m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w[i][t].y), m, 0, 0, 0);
         group_epilogue(acc[t], m, sb[i][t], xs4, on);
       }
-      const uint32_t gn = (uint32_t)min(g + kDnPre, G - 1);
-#pragma unroll
-      for (int t = 0; t < kDnTiles; ++t) {
-        w0[i][t] = bload(rs, vq[t], gn * 256);
-        w1[i][t] = bload(rs, vq[t] + 128, gn * 256);
-        sb[i][t] = bload(rs, vs[t], gn * 32);
-      }
+      fetch(i, (uint32_t)min(g + kDnPre, G - 1));
     }
   }
   float* dst = ti.shared ? p.Ys : p.Y;
