@@ -175,6 +175,17 @@ moe_status moe_layer_bytes(const moe_layer* layer, uint64_t* device_bytes, uint6
  * (bounded wait; that call's output is not valid). */
 moe_status moe_layer_check_errors(moe_layer* layer, int32_t* flags);
 
+/* The path run by calls that pass MOE_PATH_AUTO (moe_layer_forward, a NULL
+ * opts, and every layer call of moe_stack_forward); MOE_PATH_AUTO (the
+ * default) picks per call as described at moe_fwd_opts.path.  The paths differ
+ * in rounding: the fused kernel hands its intermediate activations between
+ * workgroups as fp16 with 9 mantissa bits, the others as full fp16.  So a
+ * streamed layer (always MOE_PATH_DECODE) is bit-identical to a resident one
+ * set to MOE_PATH_DECODE.  A call the chosen path cannot serve fails with
+ * MOE_ERR_INVALID, as with an explicit path.  MOE_ERR_INVALID for unknown
+ * values. */
+moe_status moe_layer_set_default_path(moe_layer* layer, int32_t path);
+
 /* Per-kernel timing.  enable != 0 brackets every kernel the layer launches
  * with HIP events on the launch stream; 0 stops and discards the record.
  * moe_layer_profile_read waits for the device, then fills HOST arrays

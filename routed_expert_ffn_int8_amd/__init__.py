@@ -66,6 +66,7 @@ _SIGS = {
     "moe_layer_sort": [_P, _P, C.c_int32, _P, _P, _P, _P, _P],
     "moe_layer_bytes": [_P, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)],
     "moe_layer_check_errors": [_P, C.POINTER(C.c_int32)],
+    "moe_layer_set_default_path": [_P, C.c_int32],
     "moe_layer_profile": [_P, C.c_int32],
     "moe_layer_profile_read": [_P, _P, _P],
     "moe_cache_attach": [_P, C.c_int32, _P],
@@ -193,6 +194,10 @@ def moe_layer_bytes(layer: int):
     db, eb = C.c_uint64(), C.c_uint64()
     _check(load().moe_layer_bytes(layer, C.byref(db), C.byref(eb)))
     return db.value, eb.value
+
+
+def moe_layer_set_default_path(layer: int, path: int):
+    _check(load().moe_layer_set_default_path(layer, path))
 
 
 def moe_layer_check_errors(layer: int) -> int:

@@ -117,6 +117,7 @@ struct moe_layer {
   size_t prefill_bytes = 0;
   // previous call (for reuse_previous)
   int prev_T = -1;
+  int default_path = MOE_PATH_AUTO;  // what a call passing MOE_PATH_AUTO runs
   int fused_ok = -1;  // whether the single-launch decode kernel serves this layer here (-1: not yet known)
   // streamed experts
   uint8_t* h_store = nullptr;  // pinned, E blobs
@@ -429,6 +430,7 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
     }
   }
   int path = o ? o->path : MOE_PATH_AUTO;
+  if (path == MOE_PATH_AUTO) path = L->default_path;
   const bool resident = L->residency == MOE_RESIDENT;
   if (L->fused_ok < 0) {  // shape, LDS and residency check, once per layer
     LayerArgs one = a;
@@ -567,6 +569,13 @@ moe_status moe_layer_bytes(const moe_layer* L, uint64_t* device_bytes, uint64_t*
   if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
   if (device_bytes) *device_bytes = L->device_bytes;
   if (expert_bytes) *expert_bytes = L->rl.stride;
+  return MOE_OK;
+}
+
+moe_status moe_layer_set_default_path(moe_layer* L, int32_t path) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_FUSED) return fail(MOE_ERR_INVALID, "unknown path %d", path);
+  L->default_path = path;
   return MOE_OK;
 }
 

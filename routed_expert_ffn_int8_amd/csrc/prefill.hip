@@ -479,9 +479,15 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
 // One workgroup: one (expert, 16-token tile) x 256 rows of the down
 // projection, two 16-row tiles per wavefront sharing each A operand read;
 // outputs fp32 rows in grouped order (shared: token order).
-constexpr int kDnTiles = 2;                              // 16-row tiles per wavefront
-constexpr int kDnRowsPerWG = 16 * kDnTiles * kPWaves;    // 256
-constexpr int kDnPre = 4;                                // groups in flight per lane
+#ifndef MOE_DN_TILES
+#define MOE_DN_TILES 2
+#endif
+#ifndef MOE_DN_PRE
+#define MOE_DN_PRE 4
+#endif
+constexpr int kDnTiles = MOE_DN_TILES;                   // 16-row tiles per wavefront
+constexpr int kDnRowsPerWG = 16 * kDnTiles * kPWaves;
+constexpr int kDnPre = MOE_DN_PRE;                       // groups in flight per lane
 
 template <int STG>
 __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {

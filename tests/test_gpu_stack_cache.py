@@ -117,6 +117,38 @@ def test_streamed_layer_bit_identical_and_counters_replay(w):
     st.close()
 
 
+def test_streamed_stack_equals_resident_stack_on_the_same_path():
+    """A stack of streamed layers (16-slot LFU caches, fills on a side stream)
+    ends in exactly the state of the same stack with every expert resident,
+    both on the split kernels, over steps with forced reuse."""
+    torch = torch_mod()
+    w = Workload(91, "stream-stack-small", d=512, E=64, K=8, f=128, fs=128, act="bf16", zipf=1.1, T=1,
+                 layers=3, steps=12, reuse_p=0.6, slots=16, noise_sd=0.1)
+    arrays = [make_layer(w, layer=l, seed=7) for l in range(w.layers)]
+    res = [GpuLayer(w, a, 1) for a in arrays]
+    st = [GpuLayer(w, a, 1, residency=M.MOE_STREAMED) for a in arrays]
+    for g in res:
+        M.moe_layer_set_default_path(g.handle, M.MOE_PATH_DECODE)
+    for g in st:
+        M.moe_cache_attach(g.handle, w.slots)
+    coins = make_reuse_coins(w, w.steps).astype(np.uint8)
+    finals = []
+    for layers in (res, st):
+        stack = M.moe_stack_create([g.handle for g in layers], 1e-6)
+        h = to_device(make_tokens(w, 1, stream=26))
+        for t in range(w.steps):
+            M.moe_stack_forward(h, stack, 1, reuse_mask=coins[t])
+        torch.cuda.synchronize()
+        finals.append(to_host(h))
+        M.moe_stack_destroy(stack)
+    assert np.array_equal(finals[0], finals[1]), "streamed stack differs from the resident stack"
+    assert sum(M.moe_cache_stats_get(g.handle)["misses"] for g in st) > 0, "no fills happened"
+    with pytest.raises(M.MoeError):
+        M.moe_layer_set_default_path(res[0].handle, 7)
+    for g in res + st:
+        g.close()
+
+
 def test_streamed_fault_injection_leaves_state_unchanged():
     w = CACHE_W
     arrays = make_layer(w)
