@@ -383,14 +383,34 @@ def run_stream(args, M, torch, np):
     h0 = torch.from_numpy(make_tokens(w, 1, stream=6).view(np.int16)).view(torch.bfloat16).cuda()
     out = {}
     finals = {}
+    _, eb = M.moe_layer_bytes(st_layers[0])
+    pool = None
+
+    def to_pool():  # the same layers, one LRU cache of the same total bytes
+        nonlocal pool
+        for L in st_layers:
+            M.moe_cache_detach(L)
+        pool = M.moe_cache_pool_create(w.layers * w.slots * eb, eb)
+        for L in st_layers:
+            M.moe_cache_attach_pool(L, pool)
+
     # resident on its fastest path; then resident on the streamed layers' path
-    # (the split kernels), which the streamed run must match bit for bit
+    # (the split kernels), which the streamed runs must match bit for bit;
+    # then streamed with 16 LFU slots per layer, then with one shared LRU pool
     for name, layers, path in (("resident", res_layers, M.MOE_PATH_AUTO),
                                ("resident_split", res_layers, M.MOE_PATH_DECODE),
-                               ("streamed", st_layers, M.MOE_PATH_AUTO)):
+                               ("streamed", st_layers, M.MOE_PATH_AUTO),
+                               ("streamed_lru", st_layers, M.MOE_PATH_AUTO)):
+        if name == "streamed_lru":
+            lfu_stats = [M.moe_cache_stats_get(L) for L in st_layers]
+            to_pool()
         for L in layers:
             M.moe_layer_set_default_path(L, path)
         stack = M.moe_stack_create(layers, 1e-6)
+        if layers is res_layers:  # untimed warm-up (the streamed runs start from empty caches on purpose)
+            hw = h0.clone()
+            for t in range(8):
+                M.moe_stack_forward(hw, stack, 1, reuse_mask=coins[t])
         h = h0.clone()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -402,8 +422,41 @@ def run_stream(args, M, torch, np):
         print(f"[bench] {name}: {out[name]:.1f} tok/s", file=sys.stderr, flush=True)
         finals[name] = h.clone()
         M.moe_stack_destroy(stack)
-    stats = [M.moe_cache_stats_get(L) for L in st_layers]
-    tot = {k: sum(s[k] for s in stats) for k in stats[0]}
+    tot = {k: sum(s[k] for s in lfu_stats) for k in lfu_stats[0]}
+    lru = M.moe_cache_pool_stats(pool)
+    # A harder trace for the two policies: a fresh N(0, 1) token every step
+    # (no recurrence), same reuse coins, both caches starting empty.
+    xs = torch.from_numpy(make_tokens(w, steps, stream=7).view(np.int16)).view(torch.bfloat16).cuda()
+    hard = {}
+    for name in ("lfu", "lru"):
+        for L in st_layers:
+            M.moe_cache_detach(L)
+        if name == "lfu":
+            for L in st_layers:
+                M.moe_cache_attach(L, w.slots)
+        else:
+            M.moe_cache_pool_destroy(pool)
+            pool = M.moe_cache_pool_create(w.layers * w.slots * eb, eb)
+            for L in st_layers:
+                M.moe_cache_attach_pool(L, pool)
+        stack = M.moe_stack_create(st_layers, 1e-6)
+        h = xs[0:1].clone()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(steps):
+            h.copy_(xs[t:t + 1])
+            M.moe_stack_forward(h, stack, 1, reuse_mask=coins[t])
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        M.moe_stack_destroy(stack)
+        if name == "lfu":
+            ss = [M.moe_cache_stats_get(L) for L in st_layers]
+            st = {k: sum(s[k] for s in ss) for k in ss[0]}
+        else:
+            st = M.moe_cache_pool_stats(pool)
+        hard[name] = {"tok_s": round(steps / dt, 2), "hit_rate": round(st["hits"] / max(1, st["accesses"]), 4),
+                      "misses_per_token": st["misses"] / steps}
+        print(f"[bench] independent tokens, {name}: {hard[name]}", file=sys.stderr, flush=True)
     res = {
         "metric": "MoE FFN expert-streaming stack tok/s (decode b=1, 40 layers, 16-slot LFU per layer)",
         "value": round(out["streamed"], 2), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": 0,
@@ -417,7 +470,17 @@ def run_stream(args, M, torch, np):
         "h2d_gbps_during_fills": round(tot["h2d_bytes"] / max(1, tot["h2d_ns"]), 2),
         "misses_per_token": tot["misses"] / steps,
         "streamed_equals_resident_same_path": bool(torch.equal(finals["resident_split"], finals["streamed"])),
+        "lru_shared_pool": {
+            "policy": "one LRU cache over (layer, expert), budget = 40 x 16 expert slots",
+            "tok_s": round(out["streamed_lru"], 2),
+            "hit_rate": round(lru["hits"] / max(1, lru["accesses"]), 4),
+            "misses_per_token": lru["misses"] / steps,
+            "h2d_bytes_per_token": lru["h2d_bytes"] / steps,
+            "equals_resident_same_path": bool(torch.equal(finals["resident_split"], finals["streamed_lru"])),
+        },
+        "independent_tokens_lfu_vs_lru": hard,
     }
+    M.moe_cache_pool_destroy(pool)
     for L in res_layers + st_layers:
         M.moe_layer_destroy(L)
     return res

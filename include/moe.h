@@ -61,6 +61,8 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, MOE_PATH_FU
 typedef struct moe_layer moe_layer; /* opaque, owned by the library */
 typedef struct moe_stack moe_stack; /* opaque, owned by the library */
 typedef struct moe_lfu moe_lfu;     /* opaque host-only cache policy object */
+typedef struct moe_lru moe_lru;     /* opaque host-only policy of a shared pool */
+typedef struct moe_cache_pool moe_cache_pool; /* opaque expert cache shared by layers */
 
 /*
  * Layer descriptor.  All weight pointers are HOST pointers in the canonical
@@ -242,6 +244,40 @@ moe_status moe_cache_contents(const moe_layer* layer, int32_t* expert_of_slot, u
  * expert compute and leaves the slot table unchanged. */
 moe_status moe_cache_fail_expert(moe_layer* layer, int32_t expert, int32_t fail);
 
+/* ---- shared expert cache under a byte budget (LRU) ---------------------
+ * BigMoeOnEdge, "the cache manages the expert working set": one cache keyed
+ * by (layer, expert) for all layers, a byte budget for expert weights only,
+ * least recently used entries evicted first, the working set in use
+ * protected.  Here: budget_bytes / expert_bytes slots of one expert blob each
+ * (moe_layer_bytes gives expert_bytes; every layer attached must have that
+ * size).  Policy: a call's hits are touched first; each miss takes the
+ * lowest empty slot, else evicts the entry (of any layer) with the oldest
+ * last use, lower slot first on ties, never an entry chosen by the same
+ * call; misses are placed in ascending expert order.  Fills are
+ * hipMemcpyAsync from the layer's pinned store on the pool's side stream,
+ * ordered before the expert kernels by events, as for per-layer caches.
+ * Layers sharing a pool must be called from one stream (or calls ordered),
+ * since a call may refill a slot another layer used last.  side_stream may
+ * be NULL (the pool creates one). */
+moe_status moe_cache_pool_create(uint64_t budget_bytes, uint64_t expert_bytes, void* side_stream,
+                                 moe_cache_pool** out);
+/* The layers that use it keep running only after another cache is
+ * attached. */
+moe_status moe_cache_pool_destroy(moe_cache_pool* pool);
+/* In place of moe_cache_attach.  The layer's key in the pool is the number
+ * of layers attached before it.  MOE_ERR_STATE if the layer is not
+ * MOE_STREAMED or has a cache; MOE_ERR_INVALID if its expert size or device
+ * differs from the pool's or the pool cannot hold one call's experts. */
+moe_status moe_cache_attach_pool(moe_layer* layer, moe_cache_pool* pool);
+/* Drop the layer's cache (its own slots, or its entries in a pool) and its
+ * counters; another cache may then be attached. */
+moe_status moe_cache_detach(moe_layer* layer);
+/* Totals over the pool (per-layer shares: moe_cache_stats_get). */
+moe_status moe_cache_pool_stats(const moe_cache_pool* pool, moe_cache_stats* out);
+/* HOST outputs [budget_bytes / expert_bytes]: key of the layer and expert
+ * held by each slot (-1 = empty). */
+moe_status moe_cache_pool_contents(const moe_cache_pool* pool, int32_t* layer_of_slot, int32_t* expert_of_slot);
+
 /* ---- stack of layers (decode through many MoE layers) ------------------
  * h <- act(h + MoE_l(act(rmsnorm(h)))) for each layer l in order, where
  * rmsnorm(h) = h / sqrt(mean(h^2) + eps) with unit gain. */
@@ -262,6 +298,13 @@ moe_status moe_lfu_create(int32_t n_slots, moe_lfu** out);
 moe_status moe_lfu_step(moe_lfu* lfu, const int32_t* chosen, int32_t n, int32_t* slot_out, int32_t* miss_out);
 moe_status moe_lfu_stats(const moe_lfu* lfu, moe_cache_stats* out);
 moe_status moe_lfu_destroy(moe_lfu* lfu);
+/* The shared pool's LRU policy: one call of the layer with key `layer`
+ * (>= 0); arguments as moe_lfu_step. */
+moe_status moe_lru_create(int32_t n_slots, moe_lru** out);
+moe_status moe_lru_step(moe_lru* lru, int32_t layer, const int32_t* chosen, int32_t n, int32_t* slot_out,
+                        int32_t* miss_out);
+moe_status moe_lru_stats(const moe_lru* lru, moe_cache_stats* out);
+moe_status moe_lru_destroy(moe_lru* lru);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* moe_last_error(void);

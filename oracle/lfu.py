@@ -57,3 +57,51 @@ class LfuReplay:
             pinned.add(s)
             slot_of[e], miss_of[e] = s, True
         return [slot_of[e] for e in chosen], [miss_of[e] for e in chosen]
+
+
+class LruPoolReplay:
+    """Replay of the shared expert cache under a byte budget (BigMoeOnEdge,
+    "the cache manages the expert working set": one LRU cache keyed by
+    (layer, expert) for all layers, its budget counting expert weights only,
+    the working set in use protected).  n_slots = budget // expert bytes.
+    Readings where the page is silent: a call's hits are touched first; each
+    miss, in ascending expert order, takes the lowest empty slot, else evicts
+    the entry with the oldest last use (lower slot on ties) among the slots
+    the same call has not chosen."""
+
+    def __init__(self, n_slots: int):
+        self.n_slots = n_slots
+        self.key = [None] * n_slots      # (layer, expert) or None
+        self.last = [0] * n_slots
+        self.now = 0
+        self.accesses = self.hits = self.misses = self.evictions = 0
+
+    def step(self, layer: int, chosen):
+        """Returns (slot per chosen id in the given order, miss flags)."""
+        chosen = list(chosen)
+        assert len(set(chosen)) == len(chosen) and len(chosen) <= self.n_slots
+        self.now += 1
+        where = {k: s for s, k in enumerate(self.key) if k is not None}
+        used = set()
+        slot_of, miss_of = {}, {}
+        for e in chosen:
+            self.accesses += 1
+            if (layer, e) in where:
+                s = where[(layer, e)]
+                self.last[s] = self.now
+                self.hits += 1
+                used.add(s)
+                slot_of[e], miss_of[e] = s, False
+        for e in sorted(x for x in chosen if (layer, x) not in where):
+            empty = [s for s in range(self.n_slots) if self.key[s] is None]
+            if empty:
+                s = empty[0]
+            else:
+                s = min((s for s in range(self.n_slots) if s not in used), key=lambda s: (self.last[s], s))
+                self.evictions += 1
+            self.key[s] = (layer, e)
+            self.last[s] = self.now
+            self.misses += 1
+            used.add(s)
+            slot_of[e], miss_of[e] = s, True
+        return [slot_of[e] for e in chosen], [miss_of[e] for e in chosen]

@@ -81,6 +81,16 @@ _SIGS = {
     "moe_lfu_step": [_P, _P, C.c_int32, _P, _P],
     "moe_lfu_stats": [_P, C.POINTER(moe_cache_stats)],
     "moe_lfu_destroy": [_P],
+    "moe_lru_create": [C.c_int32, C.POINTER(_P)],
+    "moe_lru_step": [_P, C.c_int32, _P, C.c_int32, _P, _P],
+    "moe_lru_stats": [_P, C.POINTER(moe_cache_stats)],
+    "moe_lru_destroy": [_P],
+    "moe_cache_pool_create": [C.c_uint64, C.c_uint64, _P, C.POINTER(_P)],
+    "moe_cache_pool_destroy": [_P],
+    "moe_cache_attach_pool": [_P, _P],
+    "moe_cache_detach": [_P],
+    "moe_cache_pool_stats": [_P, C.POINTER(moe_cache_stats)],
+    "moe_cache_pool_contents": [_P, _P, _P],
 }
 
 _lib = None
@@ -289,3 +299,59 @@ def moe_lfu_stats(lfu: int) -> dict:
 
 def moe_lfu_destroy(lfu: int):
     _check(load().moe_lfu_destroy(lfu))
+
+
+def moe_lru_create(n_slots: int) -> int:
+    out = _P()
+    _check(load().moe_lru_create(n_slots, C.byref(out)))
+    return out.value
+
+
+def moe_lru_step(lru: int, layer: int, chosen):
+    c = np.ascontiguousarray(chosen, dtype=np.int32)
+    slot = np.empty(len(c), np.int32)
+    miss = np.empty(len(c), np.int32)
+    _check(load().moe_lru_step(lru, layer, c.ctypes.data, len(c), slot.ctypes.data, miss.ctypes.data))
+    return slot, miss
+
+
+def moe_lru_stats(lru: int) -> dict:
+    s = moe_cache_stats()
+    _check(load().moe_lru_stats(lru, C.byref(s)))
+    return s.as_dict()
+
+
+def moe_lru_destroy(lru: int):
+    _check(load().moe_lru_destroy(lru))
+
+
+# ------------------------------------------------------- shared cache pool
+def moe_cache_pool_create(budget_bytes: int, expert_bytes: int, side_stream=None) -> int:
+    out = _P()
+    _check(load().moe_cache_pool_create(budget_bytes, expert_bytes, _stream(side_stream), C.byref(out)))
+    return out.value
+
+
+def moe_cache_pool_destroy(pool: int):
+    _check(load().moe_cache_pool_destroy(pool))
+
+
+def moe_cache_attach_pool(layer: int, pool: int):
+    _check(load().moe_cache_attach_pool(layer, pool))
+
+
+def moe_cache_detach(layer: int):
+    _check(load().moe_cache_detach(layer))
+
+
+def moe_cache_pool_stats(pool: int) -> dict:
+    s = moe_cache_stats()
+    _check(load().moe_cache_pool_stats(pool, C.byref(s)))
+    return s.as_dict()
+
+
+def moe_cache_pool_contents(pool: int, n_slots: int):
+    lay = np.empty(n_slots, np.int32)
+    exp = np.empty(n_slots, np.int32)
+    _check(load().moe_cache_pool_contents(pool, lay.ctypes.data, exp.ctypes.data))
+    return lay, exp

@@ -124,6 +124,8 @@ struct moe_layer {
   uint8_t* d_slots = nullptr;
   int n_slots = 0;
   std::unique_ptr<LfuPolicy> lfu;
+  moe_cache_pool* pool = nullptr;  // or a cache shared with other layers
+  int pool_id = -1;                // this layer's key in it
   hipStream_t side = nullptr;
   bool own_side = false;
   hipEvent_t ev_fill = nullptr, ev_fill_start = nullptr;
@@ -141,11 +143,37 @@ moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_o
 struct moe_stack {
   std::vector<moe_layer*> layers;
   float eps = 1e-6f;
+  // One synchronisation area and one set of activation copies for every
+  // layer's fused launches.  The layers run one after another, so a single
+  // area's launch count serves them all (its tag just keeps counting), and
+  // the area stays in cache instead of each layer touching its own cold one.
+  int dev = 0;
+  uint32_t* d_counter = nullptr;
+  void* d_arep = nullptr;
 };
 
 struct moe_lfu {
   LfuPolicy policy;
   explicit moe_lfu(int n) : policy(n) {}
+};
+
+struct moe_lru {
+  LruPool policy;
+  explicit moe_lru(int n) : policy(n) {}
+};
+
+// One expert cache for many streamed layers: slots of one expert blob each,
+// as many as the byte budget holds, LRU over (layer, expert).
+struct moe_cache_pool {
+  int dev = 0;
+  uint64_t expert_bytes = 0;
+  int n_slots = 0;
+  uint8_t* d_slots = nullptr;
+  hipStream_t side = nullptr;
+  bool own_side = false;
+  std::unique_ptr<LruPool> policy;
+  std::vector<moe_layer*> members;  // by key; null once a layer has left
+  moe_cache_stats stats{};
 };
 
 namespace {
@@ -206,9 +234,19 @@ void pack_parallel(const moe_layer_desc* D, const BlobLayout& L, uint8_t* dst) {
   for (auto& t : th) t.join();
 }
 
+// Take a layer out of its shared cache: its entries become empty slots.
+void leave_pool(moe_layer* L) {
+  if (!L->pool) return;
+  L->pool->policy->drop_layer(L->pool_id);
+  L->pool->members[L->pool_id] = nullptr;
+  L->pool = nullptr;
+  L->pool_id = -1;
+}
+
 void free_layer(moe_layer* L) {
   if (!L) return;
   (void)hipDeviceSynchronize();
+  leave_pool(L);
   (void)hipFree(L->d_experts);
   (void)hipFree(L->d_shared);
   (void)hipFree(L->d_zero);
@@ -357,10 +395,14 @@ LayerArgs base_args(moe_layer* L, const void* x, void* out, int T) {
   return a;
 }
 
-// Make every expert chosen by the routing in L->d_ids resident in a slot,
-// after the router has run on `stream`.  Blocks on the routing copy.
+// Make every expert chosen by the routing in L->d_ids resident in a slot of
+// the layer's cache (its own LFU slots or a shared LRU pool), after the
+// router has run on `stream`.  Blocks on the routing copy: once it is back,
+// everything queued earlier on `stream` is done, so no slot about to be
+// refilled is still being read.
 moe_status stream_in(moe_layer* L, int T, hipStream_t stream) {
-  if (!L->lfu) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
+  moe_cache_pool* P = L->pool;
+  if (!L->lfu && !P) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
   const size_t n = (size_t)T * L->K;
   HIP_OK(hipMemcpyAsync(L->h_ids, L->d_ids, n * 4, hipMemcpyDeviceToHost, stream));
   HIP_OK(hipStreamSynchronize(stream));
@@ -374,32 +416,59 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream) {
   chosen.erase(std::unique(chosen.begin(), chosen.end()), chosen.end());
   for (int32_t e : chosen) {
     if (e < 0 || e >= L->E) return fail(MOE_ERR_STATE, "routing produced expert id %d outside 0..%d", e, L->E - 1);
-    if (L->lfu->find(e) < 0 && L->fail_expert[e])
-      return fail(MOE_ERR_IO, "expert %d could not be read into a cache slot", e);
+    const bool cached = P ? P->policy->find(L->pool_id, e) >= 0 : L->lfu->find(e) >= 0;
+    if (!cached && L->fail_expert[e]) return fail(MOE_ERR_IO, "expert %d could not be read into a cache slot", e);
   }
   const int m = (int)chosen.size();
-  if (m > L->n_slots)
-    return fail(MOE_ERR_STATE, "call chose %d distinct experts but the cache has %d slots", m, L->n_slots);
-  std::vector<int32_t> slot(m), miss(m), evicted(m);
-  L->lfu->step(chosen.data(), m, slot.data(), miss.data(), evicted.data());
+  const int n_slots = P ? P->n_slots : L->n_slots;
+  if (m > n_slots) return fail(MOE_ERR_STATE, "call chose %d distinct experts but the cache has %d slots", m, n_slots);
+  std::vector<int32_t> slot(m), miss(m), ev_layer(m, -1), ev_expert(m, -1);
+  if (P)
+    P->policy->step(L->pool_id, chosen.data(), m, slot.data(), miss.data(), ev_layer.data(), ev_expert.data());
+  else
+    L->lfu->step(chosen.data(), m, slot.data(), miss.data(), ev_expert.data());
   const size_t stride = L->rl.stride;
+  uint8_t* base = P ? P->d_slots : L->d_slots;
+  hipStream_t side = P ? P->side : L->side;
   bool any = false;
+  uint64_t h2d = 0;
   for (int i = 0; i < m; ++i) {
     if (!miss[i]) continue;
-    if (!any) HIP_OK(hipEventRecord(L->ev_fill_start, L->side));
+    if (!any) HIP_OK(hipEventRecord(L->ev_fill_start, side));
     any = true;
-    uint8_t* dst = L->d_slots + (size_t)slot[i] * stride;
-    HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice, L->side));
-    if (evicted[i] >= 0) L->h_addr[evicted[i]] = 0;
+    uint8_t* dst = base + (size_t)slot[i] * stride;
+    HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice, side));
+    if (ev_expert[i] >= 0) {  // the slot's previous entry (of this layer, or of another for a pool)
+      moe_layer* owner = P ? (ev_layer[i] >= 0 ? P->members[ev_layer[i]] : nullptr) : L;
+      if (owner) owner->h_addr[ev_expert[i]] = 0;  // that layer re-uploads its table on its next call
+    }
     L->h_addr[chosen[i]] = reinterpret_cast<uint64_t>(dst);
-    L->stats.h2d_bytes += stride;
+    h2d += stride;
   }
-  L->stats.accesses = L->lfu->accesses;
-  L->stats.hits = L->lfu->hits;
-  L->stats.misses = L->lfu->misses;
-  L->stats.evictions = L->lfu->evictions;
+  if (P) {  // this layer's share of the pool's counts
+    int nm = 0, ne = 0;
+    for (int i = 0; i < m; ++i) {
+      nm += miss[i] ? 1 : 0;
+      ne += (miss[i] && ev_expert[i] >= 0) ? 1 : 0;
+    }
+    L->stats.accesses += m;
+    L->stats.hits += m - nm;
+    L->stats.misses += nm;
+    L->stats.evictions += ne;
+    P->stats.accesses = P->policy->accesses;
+    P->stats.hits = P->policy->hits;
+    P->stats.misses = P->policy->misses;
+    P->stats.evictions = P->policy->evictions;
+    P->stats.h2d_bytes += h2d;
+  } else {
+    L->stats.accesses = L->lfu->accesses;
+    L->stats.hits = L->lfu->hits;
+    L->stats.misses = L->lfu->misses;
+    L->stats.evictions = L->lfu->evictions;
+  }
+  L->stats.h2d_bytes += h2d;
   if (any) {
-    HIP_OK(hipEventRecord(L->ev_fill, L->side));
+    HIP_OK(hipEventRecord(L->ev_fill, side));
     HIP_OK(hipStreamWaitEvent(stream, L->ev_fill, 0));
     L->fill_pending = true;
   }
@@ -624,28 +693,155 @@ moe_status moe_layer_profile_read(moe_layer* L, int64_t* launches, double* total
 }
 
 // ---- cache ----
+namespace {
+// Routing copy and fill events of a streamed layer that gets a cache.
+moe_status cache_common(moe_layer* L) {
+  if (!L->h_ids &&
+      hipHostMalloc(reinterpret_cast<void**>(&L->h_ids), (size_t)L->max_tokens * L->K * 4, hipHostMallocDefault) !=
+          hipSuccess)
+    return fail(MOE_ERR_NOMEM, "pinned routing buffer failed");
+  if (!L->ev_fill) HIP_OK(hipEventCreate(&L->ev_fill));
+  if (!L->ev_fill_start) HIP_OK(hipEventCreate(&L->ev_fill_start));
+  return MOE_OK;
+}
+// Forget where the layer's experts were (every entry absent).
+moe_status clear_addresses(moe_layer* L) {
+  std::memset(L->h_addr, 0, (size_t)L->E * 8);
+  HIP_OK(hipMemcpy(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice));
+  return MOE_OK;
+}
+}  // namespace
+
 moe_status moe_cache_attach(moe_layer* L, int32_t n_slots, void* side_stream) {
   if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
   if (L->residency != MOE_STREAMED) return fail(MOE_ERR_STATE, "layer is not MOE_STREAMED");
-  if (L->lfu) return fail(MOE_ERR_STATE, "layer already has a cache");
+  if (L->lfu || L->pool) return fail(MOE_ERR_STATE, "layer already has a cache");
   if (n_slots < L->K || n_slots > L->E) return fail(MOE_ERR_INVALID, "n_slots=%d not in top_k..n_experts", n_slots);
   HIP_OK(hipSetDevice(L->dev));
   const size_t bytes = (size_t)n_slots * L->rl.stride;
   if (dalloc(&L->d_slots, bytes) != hipSuccess) return fail(MOE_ERR_NOMEM, "slot pool of %zu bytes failed", bytes);
-  if (hipHostMalloc(reinterpret_cast<void**>(&L->h_ids), (size_t)L->max_tokens * L->K * 4, hipHostMallocDefault) !=
-      hipSuccess)
-    return fail(MOE_ERR_NOMEM, "pinned routing buffer failed");
+  moe_status st = cache_common(L);
+  if (st != MOE_OK) return st;
   if (side_stream) {
     L->side = static_cast<hipStream_t>(side_stream);
   } else {
     HIP_OK(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
     L->own_side = true;
   }
-  HIP_OK(hipEventCreate(&L->ev_fill));
-  HIP_OK(hipEventCreate(&L->ev_fill_start));
   L->n_slots = n_slots;
   L->lfu.reset(new LfuPolicy(n_slots));
   L->device_bytes += bytes;
+  return MOE_OK;
+}
+
+moe_status moe_cache_pool_create(uint64_t budget_bytes, uint64_t expert_bytes, void* side_stream,
+                                 moe_cache_pool** out) {
+  if (!out) return fail(MOE_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (expert_bytes == 0 || budget_bytes < expert_bytes || budget_bytes / expert_bytes > (1u << 20))
+    return fail(MOE_ERR_INVALID, "budget %llu B holds no expert of %llu B (or more than 2^20)",
+                (unsigned long long)budget_bytes, (unsigned long long)expert_bytes);
+  std::unique_ptr<moe_cache_pool> P(new (std::nothrow) moe_cache_pool());
+  if (!P) return fail(MOE_ERR_NOMEM, "host allocation failed");
+  HIP_OK(hipGetDevice(&P->dev));
+  P->expert_bytes = expert_bytes;
+  P->n_slots = (int)(budget_bytes / expert_bytes);
+  if (dalloc(&P->d_slots, (size_t)P->n_slots * expert_bytes) != hipSuccess)
+    return fail(MOE_ERR_NOMEM, "slot pool of %llu bytes failed", (unsigned long long)budget_bytes);
+  if (side_stream) {
+    P->side = static_cast<hipStream_t>(side_stream);
+  } else if (hipStreamCreateWithFlags(&P->side, hipStreamNonBlocking) != hipSuccess) {
+    (void)hipFree(P->d_slots);
+    return fail(MOE_ERR_HIP, "side stream creation failed");
+  } else {
+    P->own_side = true;
+  }
+  P->policy.reset(new LruPool(P->n_slots));
+  *out = P.release();
+  return MOE_OK;
+}
+
+moe_status moe_cache_pool_destroy(moe_cache_pool* P) {
+  if (!P) return MOE_OK;
+  (void)hipSetDevice(P->dev);
+  (void)hipDeviceSynchronize();
+  for (moe_layer* L : P->members)
+    if (L) {  // the layer keeps running only after a new cache is attached
+      L->pool = nullptr;
+      L->pool_id = -1;
+      (void)clear_addresses(L);
+    }
+  (void)hipFree(P->d_slots);
+  if (P->own_side && P->side) (void)hipStreamDestroy(P->side);
+  delete P;
+  return MOE_OK;
+}
+
+moe_status moe_cache_attach_pool(moe_layer* L, moe_cache_pool* P) {
+  if (!L || !P) return fail(MOE_ERR_INVALID, "layer/pool is NULL");
+  if (L->residency != MOE_STREAMED) return fail(MOE_ERR_STATE, "layer is not MOE_STREAMED");
+  if (L->lfu || L->pool) return fail(MOE_ERR_STATE, "layer already has a cache");
+  if (L->dev != P->dev) return fail(MOE_ERR_INVALID, "layer and pool are on different devices");
+  if (L->rl.stride != P->expert_bytes)
+    return fail(MOE_ERR_INVALID, "expert blob of %zu B, the pool's slots hold %llu B", L->rl.stride,
+                (unsigned long long)P->expert_bytes);
+  if (P->n_slots < L->K * L->max_tokens && P->n_slots < L->E)
+    return fail(MOE_ERR_INVALID, "pool of %d slots cannot hold one call's %d experts", P->n_slots,
+                std::min(L->K * L->max_tokens, L->E));
+  HIP_OK(hipSetDevice(L->dev));
+  moe_status st = cache_common(L);
+  if (st != MOE_OK) return st;
+  L->pool = P;
+  L->pool_id = (int)P->members.size();
+  P->members.push_back(L);
+  return MOE_OK;
+}
+
+moe_status moe_cache_detach(moe_layer* L) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (!L->lfu && !L->pool) return fail(MOE_ERR_STATE, "layer has no cache");
+  HIP_OK(hipSetDevice(L->dev));
+  HIP_OK(hipDeviceSynchronize());
+  if (L->pool) {
+    leave_pool(L);
+  } else {
+    (void)hipFree(L->d_slots);
+    L->device_bytes -= (uint64_t)L->n_slots * L->rl.stride;
+    L->d_slots = nullptr;
+    L->n_slots = 0;
+    L->lfu.reset();
+    if (L->own_side && L->side) (void)hipStreamDestroy(L->side);
+    L->side = nullptr;
+    L->own_side = false;
+  }
+  L->fill_pending = false;
+  L->stats = moe_cache_stats{};
+  return clear_addresses(L);
+}
+
+moe_status moe_cache_pool_stats(const moe_cache_pool* P, moe_cache_stats* out) {
+  if (!P || !out) return fail(MOE_ERR_INVALID, "pool/out is NULL");
+  HIP_OK(hipSetDevice(P->dev));
+  HIP_OK(hipDeviceSynchronize());
+  moe_cache_stats st = P->stats;
+  st.h2d_ns = 0;
+  for (moe_layer* L : P->members) {
+    if (!L) continue;
+    moe_cache_stats ls{};
+    moe_status r = moe_cache_stats_get(L, &ls);
+    if (r != MOE_OK) return r;
+    st.h2d_ns += ls.h2d_ns;
+  }
+  *out = st;
+  return MOE_OK;
+}
+
+moe_status moe_cache_pool_contents(const moe_cache_pool* P, int32_t* layer_of_slot, int32_t* expert_of_slot) {
+  if (!P) return fail(MOE_ERR_INVALID, "pool is NULL");
+  for (int s = 0; s < P->n_slots; ++s) {
+    if (layer_of_slot) layer_of_slot[s] = P->policy->slots[s].layer;
+    if (expert_of_slot) expert_of_slot[s] = P->policy->slots[s].expert;
+  }
   return MOE_OK;
 }
 
@@ -664,23 +860,26 @@ moe_status moe_cache_stats_get(const moe_layer* L, moe_cache_stats* out) {
 
 moe_status moe_cache_reset(moe_layer* L, int32_t drop_contents) {
   if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
-  if (!L->lfu) return fail(MOE_ERR_STATE, "layer has no cache");
+  if (!L->lfu && !L->pool) return fail(MOE_ERR_STATE, "layer has no cache");
   HIP_OK(hipSetDevice(L->dev));
   HIP_OK(hipDeviceSynchronize());
   L->fill_pending = false;
   L->stats = moe_cache_stats{};
-  L->lfu->clear_counters();
+  if (L->lfu) L->lfu->clear_counters();
   if (drop_contents) {
-    L->lfu->clear_contents();
-    std::memset(L->h_addr, 0, (size_t)L->E * 8);
-    HIP_OK(hipMemcpy(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice));
+    if (L->lfu)
+      L->lfu->clear_contents();
+    else
+      L->pool->policy->drop_layer(L->pool_id);
+    return clear_addresses(L);
   }
   return MOE_OK;
 }
 
 moe_status moe_cache_contents(const moe_layer* L, int32_t* expert_of_slot, uint32_t* use_count) {
   if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
-  if (!L->lfu) return fail(MOE_ERR_STATE, "layer has no cache");
+  if (!L->lfu) return fail(MOE_ERR_STATE, L->pool ? "layer uses a shared pool: see moe_cache_pool_contents"
+                                                  : "layer has no cache");
   for (int s = 0; s < L->n_slots; ++s) {
     if (expert_of_slot) expert_of_slot[s] = L->lfu->slots[s].expert;
     if (use_count) use_count[s] = L->lfu->slots[s].count;
@@ -707,11 +906,29 @@ moe_status moe_stack_create(moe_layer* const* layers, int32_t n, float eps, moe_
       return fail(MOE_ERR_INVALID, "layer %d has a different d_model or activation type", i);
   }
   if (!(eps > 0.f)) return fail(MOE_ERR_INVALID, "rms_eps must be positive");
-  moe_stack* S = new (std::nothrow) moe_stack();
+  for (int i = 0; i < n; ++i)
+    if (layers[i]->dev != layers[0]->dev) return fail(MOE_ERR_INVALID, "layer %d is on another device", i);
+  std::unique_ptr<moe_stack> S(new (std::nothrow) moe_stack());
   if (!S) return fail(MOE_ERR_NOMEM, "host allocation failed");
   S->layers.assign(layers, layers + n);
   S->eps = eps;
-  *out = S;
+  S->dev = layers[0]->dev;
+  int maxE = 1, maxF = 1;
+  for (int i = 0; i < n; ++i) {
+    maxE = std::max(maxE, layers[i]->E);
+    maxF = std::max(maxF, layers[i]->fs + layers[i]->K * layers[i]->f);
+  }
+  HIP_OK(hipSetDevice(S->dev));
+  if (dalloc(&S->d_counter, decode_sync_bytes(maxE)) != hipSuccess ||
+      dalloc(&S->d_arep, decode_arep_bytes(maxF)) != hipSuccess) {
+    (void)hipFree(S->d_counter);
+    (void)hipFree(S->d_arep);
+    return fail(MOE_ERR_NOMEM, "stack synchronisation area failed");
+  }
+  HIP_OK(hipMemset(S->d_counter, 0, decode_sync_bytes(maxE)));
+  HIP_OK(hipMemset(S->d_arep, 0, decode_arep_bytes(maxF)));  // parity 0: older than any launch
+  HIP_OK(hipDeviceSynchronize());
+  *out = S.release();
   return MOE_OK;
 }
 
@@ -725,6 +942,8 @@ moe_status moe_stack_forward(void* h, moe_stack* S, int32_t n_tokens, const uint
     a.rms = 1;
     a.eps = S->eps;
     a.resid = h;
+    a.counter = S->d_counter;  // shared by the stack's layers (see moe_stack)
+    a.arep = S->d_arep;
     moe_fwd_opts o{};
     o.reuse_previous = reuse_mask ? reuse_mask[l] : 0;
     o.topk_ids = ids_out ? ids_out + l * (size_t)n_tokens * L->K : nullptr;
@@ -736,6 +955,12 @@ moe_status moe_stack_forward(void* h, moe_stack* S, int32_t n_tokens, const uint
 }
 
 moe_status moe_stack_destroy(moe_stack* S) {
+  if (S) {
+    (void)hipSetDevice(S->dev);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(S->d_counter);
+    (void)hipFree(S->d_arep);
+  }
   delete S;
   return MOE_OK;
 }
@@ -765,6 +990,37 @@ moe_status moe_lfu_stats(const moe_lfu* P, moe_cache_stats* out) {
 }
 
 moe_status moe_lfu_destroy(moe_lfu* P) {
+  delete P;
+  return MOE_OK;
+}
+
+moe_status moe_lru_create(int32_t n_slots, moe_lru** out) {
+  if (!out) return fail(MOE_ERR_INVALID, "out is NULL");
+  if (n_slots < 1 || n_slots > 1 << 20) return fail(MOE_ERR_INVALID, "n_slots=%d invalid", n_slots);
+  *out = new (std::nothrow) moe_lru(n_slots);
+  return *out ? MOE_OK : fail(MOE_ERR_NOMEM, "host allocation failed");
+}
+
+moe_status moe_lru_step(moe_lru* P, int32_t layer, const int32_t* chosen, int32_t n, int32_t* slot_out,
+                        int32_t* miss_out) {
+  if (!P || (n > 0 && (!chosen || !slot_out || !miss_out))) return fail(MOE_ERR_INVALID, "NULL argument");
+  if (layer < 0) return fail(MOE_ERR_INVALID, "layer key %d must be >= 0", layer);
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < i; ++j)
+      if (chosen[i] == chosen[j]) return fail(MOE_ERR_INVALID, "chosen ids must be distinct");
+  std::vector<int32_t> el(n > 0 ? n : 1), ee(n > 0 ? n : 1);
+  if (!P->policy.step(layer, chosen, n, slot_out, miss_out, el.data(), ee.data()))
+    return fail(MOE_ERR_STATE, "%d chosen experts exceed %zu slots", n, P->policy.slots.size());
+  return MOE_OK;
+}
+
+moe_status moe_lru_stats(const moe_lru* P, moe_cache_stats* out) {
+  if (!P || !out) return fail(MOE_ERR_INVALID, "NULL argument");
+  *out = moe_cache_stats{P->policy.accesses, P->policy.hits, P->policy.misses, P->policy.evictions, 0, 0};
+  return MOE_OK;
+}
+
+moe_status moe_lru_destroy(moe_lru* P) {
   delete P;
   return MOE_OK;
 }

@@ -70,3 +70,60 @@ bool LfuPolicy::step(const int32_t* chosen, int n, int32_t* slot_out, int32_t* m
 }
 
 }  // namespace moe
+
+namespace moe {
+
+int LruPool::find(int32_t layer, int32_t expert) const {
+  for (size_t s = 0; s < slots.size(); ++s)
+    if (slots[s].layer == layer && slots[s].expert == expert) return (int)s;
+  return -1;
+}
+
+void LruPool::drop_layer(int32_t layer) {
+  for (auto& s : slots)
+    if (s.layer == layer) s = Slot{};
+}
+
+bool LruPool::step(int32_t layer, const int32_t* chosen, int n, int32_t* slot_out, int32_t* miss_out,
+                   int32_t* ev_layer, int32_t* ev_expert) {
+  const int ns = (int)slots.size();
+  if (n > ns) return false;
+  ++now;
+  std::vector<char> pinned(ns, 0);
+  std::vector<int> miss_idx;
+  for (int i = 0; i < n; ++i) {  // hits first
+    const int s = find(layer, chosen[i]);
+    ++accesses;
+    ev_layer[i] = ev_expert[i] = -1;
+    if (s >= 0) {
+      ++hits;
+      slots[s].tick = now;
+      pinned[s] = 1;
+      slot_out[i] = s;
+      miss_out[i] = 0;
+    } else {
+      miss_idx.push_back(i);
+    }
+  }
+  std::sort(miss_idx.begin(), miss_idx.end(), [&](int a, int b) { return chosen[a] < chosen[b]; });
+  for (int i : miss_idx) {
+    int victim = -1;
+    for (int s = 0; s < ns && victim < 0; ++s)
+      if (slots[s].expert < 0) victim = s;
+    if (victim < 0) {
+      for (int s = 0; s < ns; ++s)
+        if (!pinned[s] && (victim < 0 || slots[s].tick < slots[victim].tick)) victim = s;
+      ++evictions;
+      ev_layer[i] = slots[victim].layer;
+      ev_expert[i] = slots[victim].expert;
+    }
+    slots[victim] = Slot{layer, chosen[i], now};
+    pinned[victim] = 1;
+    ++misses;
+    slot_out[i] = victim;
+    miss_out[i] = 1;
+  }
+  return true;
+}
+
+}  // namespace moe

@@ -42,3 +42,41 @@ struct LfuPolicy {
 };
 
 }  // namespace moe
+
+namespace moe {
+
+// Expert cache shared by several layers under one byte budget, LRU.
+//
+// BigMoeOnEdge, "the cache manages the expert working set": entries are
+// keyed by (layer, expert), the budget covers expert weights only, least
+// recently used entries go first, and the working set in use is protected
+// (the page lets residency exceed the budget for it; here every slot has
+// the size of one expert, and a call needing more slots than the budget
+// holds is refused).  Readings where the page is silent: an empty slot is
+// taken first (lowest index); among the other slots, entries chosen by the
+// current call are never its victims, the oldest last-use goes first, then
+// the lower slot; hits are applied before misses, misses in ascending
+// expert order; one access per (call, chosen expert).
+struct LruPool {
+  struct Slot {
+    int32_t layer = -1, expert = -1;
+    uint64_t tick = 0;
+  };
+  std::vector<Slot> slots;
+  uint64_t now = 0;
+  uint64_t accesses = 0, hits = 0, misses = 0, evictions = 0;
+
+  explicit LruPool(int n_slots) : slots(n_slots) {}
+
+  // Place the n distinct experts `chosen` of `layer` for one call.
+  // slot_out[i] / miss_out[i] describe chosen[i]; for a miss that evicted an
+  // entry, ev_layer[i] / ev_expert[i] name it (-1 if the slot was empty).
+  // Returns false (and changes nothing) if n exceeds the slot count.
+  bool step(int32_t layer, const int32_t* chosen, int n, int32_t* slot_out, int32_t* miss_out, int32_t* ev_layer,
+            int32_t* ev_expert);
+  int find(int32_t layer, int32_t expert) const;
+  void drop_layer(int32_t layer);  // empty every slot of `layer`
+  void clear_counters() { accesses = hits = misses = evictions = 0; }
+};
+
+}  // namespace moe

@@ -9,7 +9,7 @@ import pytest
 
 import routed_expert_ffn_int8_amd as M
 from gen.workloads import WORKLOADS, make_layer
-from oracle.lfu import LfuReplay
+from oracle.lfu import LfuReplay, LruPoolReplay
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -63,6 +63,56 @@ def test_lfu_golden_trace_through_abi():
         assert (st["accesses"], st["hits"], st["misses"], st["evictions"]) == (10, 2, 8, 4)
     finally:
         M.moe_lfu_destroy(lfu)
+
+
+def test_lru_golden_trace_through_abi():
+    here = os.path.dirname(os.path.abspath(__file__))
+    lru = M.moe_lru_create(4)
+    try:
+        for line in open(os.path.join(here, "golden", "lru_pool_trace.txt")):
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            step, layer, chosen, slots, misses = [list(map(int, p.split())) for p in line.split("|")]
+            s, m = M.moe_lru_step(lru, layer[0], chosen)
+            assert list(s) == slots and list(m) == misses, step
+        st = M.moe_lru_stats(lru)
+        assert (st["accesses"], st["hits"], st["misses"], st["evictions"]) == (13, 4, 9, 5)
+        with pytest.raises(M.MoeError):
+            M.moe_lru_step(lru, 0, [1, 1])
+        with pytest.raises(M.MoeError):
+            M.moe_lru_step(lru, 0, [1, 2, 3, 4, 5])
+        with pytest.raises(M.MoeError):
+            M.moe_lru_step(lru, -1, [1])
+    finally:
+        M.moe_lru_destroy(lru)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_lru_matches_replay_on_random_stack_traces(seed):
+    rng = np.random.default_rng(100 + seed)
+    n_slots, E, K, layers = 40, 64, 8, 5
+    zipf = 1.0 / np.arange(1, E + 1) ** 1.1
+    zipf /= zipf.sum()
+    lru = M.moe_lru_create(n_slots)
+    ref = LruPoolReplay(n_slots)
+    prev = [None] * layers
+    try:
+        for step in range(120):
+            for l in range(layers):
+                if prev[l] is not None and rng.random() < 0.6:
+                    chosen = prev[l]
+                else:
+                    chosen = np.sort(rng.choice(E, K, replace=False, p=zipf)).astype(np.int32)
+                s, m = M.moe_lru_step(lru, l, chosen)
+                rs, rm = ref.step(l, chosen.tolist())
+                assert list(s) == rs and [bool(v) for v in m] == rm, (step, l)
+                prev[l] = chosen
+        st = M.moe_lru_stats(lru)
+        assert (st["accesses"], st["hits"], st["misses"], st["evictions"]) == \
+            (ref.accesses, ref.hits, ref.misses, ref.evictions)
+    finally:
+        M.moe_lru_destroy(lru)
 
 
 @pytest.mark.parametrize("seed", range(5))

@@ -6,7 +6,7 @@ import pytest
 import routed_expert_ffn_int8_amd as M
 from gen.workloads import WORKLOADS, Workload, make_layer, make_tokens, make_reuse_coins
 from oracle import oracle as O
-from oracle.lfu import LfuReplay
+from oracle.lfu import LfuReplay, LruPoolReplay
 from tests.helpers import GpuLayer, to_device, to_host, torch_mod
 
 pytestmark = pytest.mark.gpu
@@ -146,6 +146,65 @@ def test_streamed_stack_equals_resident_stack_on_the_same_path():
     with pytest.raises(M.MoeError):
         M.moe_layer_set_default_path(res[0].handle, 7)
     for g in res + st:
+        g.close()
+
+
+def test_pooled_lru_stack_equals_resident_and_replays():
+    """Three streamed layers share one LRU pool smaller than their combined
+    working sets: the stack ends in exactly the resident stack's state (same
+    split kernels), the pool's contents and counters equal the oracle's
+    replay of the recorded routing, and the layers can then be detached and
+    given per-layer caches."""
+    torch = torch_mod()
+    w = Workload(92, "pool-stack-small", d=512, E=64, K=8, f=128, fs=128, act="bf16", zipf=1.1, T=1,
+                 layers=3, steps=14, reuse_p=0.6, slots=16, noise_sd=0.1)
+    arrays = [make_layer(w, layer=l, seed=9) for l in range(w.layers)]
+    res = [GpuLayer(w, a, 1) for a in arrays]
+    st = [GpuLayer(w, a, 1, residency=M.MOE_STREAMED) for a in arrays]
+    for g in res:
+        M.moe_layer_set_default_path(g.handle, M.MOE_PATH_DECODE)
+    _, eb = M.moe_layer_bytes(st[0].handle)
+    n_slots = 20
+    pool = M.moe_cache_pool_create(n_slots * eb + eb // 2, eb)  # the budget's remainder holds no expert
+    for g in st:
+        M.moe_cache_attach_pool(g.handle, pool)
+    coins = make_reuse_coins(w, w.steps).astype(np.uint8)
+    replay = LruPoolReplay(n_slots)
+    finals = []
+    for layers in (res, st):
+        stack = M.moe_stack_create([g.handle for g in layers], 1e-6)
+        h = to_device(make_tokens(w, 1, stream=27))
+        ids = torch.empty((w.layers, 1, w.K), dtype=torch.int32, device="cuda")
+        for t in range(w.steps):
+            M.moe_stack_forward(h, stack, 1, reuse_mask=coins[t], ids_out=ids)
+            if layers is st:
+                for l, row in enumerate(ids.cpu().numpy()[:, 0]):
+                    replay.step(l, sorted(set(row.tolist())))
+        torch.cuda.synchronize()
+        finals.append(to_host(h))
+        M.moe_stack_destroy(stack)
+    assert np.array_equal(finals[0], finals[1]), "pooled streamed stack differs from the resident stack"
+    tot = M.moe_cache_pool_stats(pool)
+    assert (tot["accesses"], tot["hits"], tot["misses"], tot["evictions"]) == \
+        (replay.accesses, replay.hits, replay.misses, replay.evictions)
+    assert replay.evictions > 0, "the pool never filled up"
+    assert tot["h2d_bytes"] == replay.misses * eb
+    per = [M.moe_cache_stats_get(g.handle) for g in st]
+    assert sum(p["misses"] for p in per) == replay.misses
+    lay, exp = M.moe_cache_pool_contents(pool, n_slots)
+    want = [k if k is not None else (-1, -1) for k in replay.key]
+    assert [(int(a), int(b)) for a, b in zip(lay, exp)] == want
+    with pytest.raises(M.MoeError):
+        M.moe_cache_attach(st[0].handle, 16)  # already cached by the pool
+    for g in st:
+        M.moe_cache_detach(g.handle)
+        M.moe_cache_attach(g.handle, 16)
+    y_r, _, _ = res[0].forward(make_tokens(w, 1, stream=28), path=M.MOE_PATH_DECODE)
+    y_s, _, _ = st[0].forward(make_tokens(w, 1, stream=28), path=M.MOE_PATH_DECODE)
+    assert np.array_equal(y_r, y_s)
+    M.moe_cache_pool_destroy(pool)
+    for g in res + st:
+        assert M.moe_layer_check_errors(g.handle) == 0
         g.close()
 
 

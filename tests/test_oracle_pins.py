@@ -9,7 +9,7 @@ import pytest
 from gen.workloads import WORKLOADS, Workload, make_layer, make_tokens, f32_to_bf16_bits
 from oracle import brute
 from oracle import oracle as O
-from oracle.lfu import LfuReplay
+from oracle.lfu import LfuReplay, LruPoolReplay
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -325,3 +325,44 @@ def test_lfu_golden_trace():
         assert got_slots == slots, step
         assert [int(m) for m in got_miss] == misses, step
     assert (lfu.accesses, lfu.hits, lfu.misses, lfu.evictions) == (10, 2, 8, 4)
+
+
+def _lru_golden_rows():
+    rows = []
+    for line in open(os.path.join(HERE, "golden", "lru_pool_trace.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            rows.append([list(map(int, part.split())) for part in line.split("|")])
+    return rows
+
+
+def test_lru_pool_golden_trace():
+    pool = LruPoolReplay(4)
+    for (step,), (layer,), chosen, slots, misses in _lru_golden_rows():
+        got_slots, got_miss = pool.step(layer, chosen)
+        assert got_slots == slots, step
+        assert [int(m) for m in got_miss] == misses, step
+    assert (pool.accesses, pool.hits, pool.misses, pool.evictions) == (13, 4, 9, 5)
+
+
+@pytest.mark.parametrize("n_slots", [1, 3, 8])
+def test_lru_pool_single_expert_calls_follow_stack_distance(n_slots):
+    """With one expert per call nothing is protected and the policy is plain
+    LRU, so an access misses exactly when its stack distance (distinct keys
+    touched since its previous use, infinite on first use) is >= the slot
+    count: the inclusion property of LRU (Mattson et al., 1970)."""
+    rng = np.random.default_rng(n_slots)
+    pool = LruPoolReplay(n_slots)
+    history = []
+    for step in range(600):
+        layer = int(rng.integers(0, 3))
+        e = int(min(rng.geometric(0.15), 40))
+        key = (layer, e)
+        if key in history:
+            last = len(history) - 1 - history[::-1].index(key)
+            dist = len(set(history[last + 1:]))
+        else:
+            dist = 10**9
+        _, miss = pool.step(layer, [e])
+        assert miss[0] == (dist >= n_slots), step
+        history.append(key)
