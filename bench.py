@@ -428,10 +428,10 @@ def run_stream(args, M, torch, np):
     # (no recurrence), same reuse coins, both caches starting empty.
     xs = torch.from_numpy(make_tokens(w, steps, stream=7).view(np.int16)).view(torch.bfloat16).cuda()
     hard = {}
-    for name in ("lfu", "lru"):
+    for name in ("lfu", "lfu_prefetch8", "lru"):
         for L in st_layers:
             M.moe_cache_detach(L)
-        if name == "lfu":
+        if name.startswith("lfu"):
             for L in st_layers:
                 M.moe_cache_attach(L, w.slots)
         else:
@@ -440,6 +440,8 @@ def run_stream(args, M, torch, np):
             for L in st_layers:
                 M.moe_cache_attach_pool(L, pool)
         stack = M.moe_stack_create(st_layers, 1e-6)
+        if name == "lfu_prefetch8":  # fetch the next layer's 8 most chosen absent experts ahead
+            M.moe_stack_set_prefetch(stack, 8)
         h = xs[0:1].clone()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -449,13 +451,17 @@ def run_stream(args, M, torch, np):
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         M.moe_stack_destroy(stack)
-        if name == "lfu":
+        if name.startswith("lfu"):
             ss = [M.moe_cache_stats_get(L) for L in st_layers]
             st = {k: sum(s[k] for s in ss) for k in ss[0]}
         else:
             st = M.moe_cache_pool_stats(pool)
         hard[name] = {"tok_s": round(steps / dt, 2), "hit_rate": round(st["hits"] / max(1, st["accesses"]), 4),
-                      "misses_per_token": st["misses"] / steps}
+                      "misses_per_token": st["misses"] / steps,
+                      "h2d_mb_per_token": round(st["h2d_bytes"] / steps / 1e6, 2)}
+        if st["prefetches"]:
+            hard[name]["prefetches_per_token"] = st["prefetches"] / steps
+            hard[name]["prefetch_used_frac"] = round(st["prefetch_used"] / st["prefetches"], 4)
         print(f"[bench] independent tokens, {name}: {hard[name]}", file=sys.stderr, flush=True)
     res = {
         "metric": "MoE FFN expert-streaming stack tok/s (decode b=1, 40 layers, 16-slot LFU per layer)",
@@ -478,7 +484,7 @@ def run_stream(args, M, torch, np):
             "h2d_bytes_per_token": lru["h2d_bytes"] / steps,
             "equals_resident_same_path": bool(torch.equal(finals["resident_split"], finals["streamed_lru"])),
         },
-        "independent_tokens_lfu_vs_lru": hard,
+        "independent_tokens_lfu_vs_lru": hard,  # also LFU with fetch-ahead
     }
     M.moe_cache_pool_destroy(pool)
     for L in res_layers + st_layers:

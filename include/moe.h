@@ -229,9 +229,11 @@ typedef struct {
   uint64_t accesses;   /* one per (call, token, chosen expert) that was looked up */
   uint64_t hits;
   uint64_t misses;
-  uint64_t evictions;  /* misses that replaced a resident expert */
-  uint64_t h2d_bytes;  /* misses * expert bytes */
+  uint64_t evictions;  /* entries replaced (by a miss or a prefetch) */
+  uint64_t h2d_bytes;  /* (misses + prefetches) * expert bytes */
   uint64_t h2d_ns;     /* wall time of the fills, host clock, summed */
+  uint64_t prefetches;    /* experts placed ahead of use (moe_cache_prefetch) */
+  uint64_t prefetch_used; /* of those, the ones a call then hit */
 } moe_cache_stats;
 
 moe_status moe_cache_stats_get(const moe_layer* layer, moe_cache_stats* out);
@@ -243,6 +245,17 @@ moe_status moe_cache_contents(const moe_layer* layer, int32_t* expert_of_slot, u
  * needs to fill an unreadable expert returns MOE_ERR_IO before enqueuing any
  * expert compute and leaves the slot table unchanged. */
 moe_status moe_cache_fail_expert(moe_layer* layer, int32_t expert, int32_t fail);
+
+/* Fetch ahead into a layer's own (LFU) cache, Rockchip-NPU plan §8
+ * ("readahead": predict the next layer's experts from the routing history
+ * and start reading them during the current layer) and §9.5 item 2.  The
+ * absent ones of experts[n] (HOST ids) are placed as described at
+ * moe_lfu_prefetch and copied on the layer's side stream; the layer's next
+ * call waits for those copies.  `stream` is the stream the layer's calls run
+ * on: this call first waits for it, so no slot still in use is refilled.
+ * Unreadable experts (moe_cache_fail_expert) are skipped.  MOE_ERR_STATE
+ * without a per-layer cache. */
+moe_status moe_cache_prefetch(moe_layer* layer, const int32_t* experts, int32_t n, void* stream);
 
 /* ---- shared expert cache under a byte budget (LRU) ---------------------
  * BigMoeOnEdge, "the cache manages the expert working set": one cache keyed
@@ -288,6 +301,13 @@ moe_status moe_stack_create(moe_layer* const* layers, int32_t n_layers, float rm
  * [n_layers][n_tokens][K] or NULL. */
 moe_status moe_stack_forward(void* h, moe_stack* stack, int32_t n_tokens, const uint8_t* reuse_mask,
                              int32_t* ids_out, void* stream);
+/* Fetch ahead in a stack of streamed layers with per-layer caches: once a
+ * layer's routing is back on the host (and its own fills are queued), the
+ * next layer's `depth` most often chosen experts so far (ties to the lower
+ * id) that are not in its cache are prefetched, so their copies overlap the
+ * current layer's expert compute.  0 (the default) turns it off; depth is at
+ * most 64. */
+moe_status moe_stack_set_prefetch(moe_stack* stack, int32_t depth);
 moe_status moe_stack_destroy(moe_stack* stack);
 
 /* ---- host-only cache policy (no GPU needed) ----------------------------
@@ -297,6 +317,15 @@ moe_status moe_lfu_create(int32_t n_slots, moe_lfu** out);
  * (HOST) receive the slot of each id and 1 where it was a miss. */
 moe_status moe_lfu_step(moe_lfu* lfu, const int32_t* chosen, int32_t n, int32_t* slot_out, int32_t* miss_out);
 moe_status moe_lfu_stats(const moe_lfu* lfu, moe_cache_stats* out);
+/* Place the absent ones of experts[n] ahead of use, in ascending id order,
+ * without counting an access: each takes the lowest empty slot, else evicts
+ * as a miss would, but never an entry placed by the same prefetch nor one
+ * the last call used (the working set; the guess is dropped when no other
+ * slot is left); a new entry
+ * starts at use count 0 with the last call's tick, and a later call's hit on
+ * it counts in prefetch_used.  slot_out[n] (HOST): slot given, or -1 where
+ * the expert was already present (or no slot was left). */
+moe_status moe_lfu_prefetch(moe_lfu* lfu, const int32_t* experts, int32_t n, int32_t* slot_out);
 moe_status moe_lfu_destroy(moe_lfu* lfu);
 /* The shared pool's LRU policy: one call of the layer with key `layer`
  * (>= 0); arguments as moe_lfu_step. */

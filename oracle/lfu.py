@@ -11,6 +11,15 @@ count ties (older first), then the slot index; experts chosen by the current
 step are never evicted by that step; counts are never aged; hits are
 processed before misses, misses in ascending expert order; one access per
 (step, chosen expert), forced-reuse steps included.
+
+Fetch ahead (plan §8 "readahead", §9.5 item 2: predict the next layer's
+experts from the routing history and load them early): absent experts are
+placed, in ascending id order, without counting an access; each takes an
+empty slot first, else evicts as a miss would but never an entry placed by
+the same prefetch nor one the last step used (BigMoeOnEdge protects the
+working set in use; without such a slot the guess is dropped); a new entry
+starts at count 0 with the last step's tick.
+A step's hit on such an entry counts as a used prefetch.
 """
 from __future__ import annotations
 
@@ -21,8 +30,10 @@ class LfuReplay:
         self.expert = [-1] * n_slots
         self.count = [0] * n_slots
         self.tick = [0] * n_slots
+        self.ahead = [False] * n_slots
         self.now = 0
         self.accesses = self.hits = self.misses = self.evictions = 0
+        self.prefetches = self.prefetch_used = 0
 
     def step(self, chosen):
         """chosen: iterable of distinct expert ids.  Returns (slot per chosen id
@@ -37,6 +48,9 @@ class LfuReplay:
             self.accesses += 1
             if e in where:
                 s = where[e]
+                if self.ahead[s]:
+                    self.prefetch_used += 1
+                self.ahead[s] = False
                 self.count[s] += 1
                 self.tick[s] = self.now
                 self.hits += 1
@@ -53,10 +67,34 @@ class LfuReplay:
             self.expert[s] = e
             self.count[s] = 1
             self.tick[s] = self.now
+            self.ahead[s] = False
             self.misses += 1
             pinned.add(s)
             slot_of[e], miss_of[e] = s, True
         return [slot_of[e] for e in chosen], [miss_of[e] for e in chosen]
+
+    def prefetch(self, experts):
+        """Place the absent experts ahead of use; returns {expert: slot} for those placed."""
+        placed = {}
+        pinned = set()
+        for e in sorted(set(experts)):
+            if e in self.expert:
+                continue
+            empties = [s for s in range(self.n_slots) if self.expert[s] < 0]
+            if empties:
+                s = empties[0]
+            else:
+                cands = [s for s in range(self.n_slots)
+                         if s not in pinned and not (self.tick[s] == self.now and not self.ahead[s])]
+                if not cands:
+                    continue
+                s = min(cands, key=lambda s: (self.count[s], self.tick[s], s))
+                self.evictions += 1
+            self.expert[s], self.count[s], self.tick[s], self.ahead[s] = e, 0, self.now, True
+            self.prefetches += 1
+            pinned.add(s)
+            placed[e] = s
+        return placed
 
 
 class LruPoolReplay:

@@ -50,7 +50,8 @@ class moe_fwd_opts(C.Structure):
 
 
 class moe_cache_stats(C.Structure):
-    _fields_ = [(n, C.c_uint64) for n in ("accesses", "hits", "misses", "evictions", "h2d_bytes", "h2d_ns")]
+    _fields_ = [(n, C.c_uint64) for n in ("accesses", "hits", "misses", "evictions", "h2d_bytes", "h2d_ns",
+                                          "prefetches", "prefetch_used")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -81,6 +82,9 @@ _SIGS = {
     "moe_lfu_step": [_P, _P, C.c_int32, _P, _P],
     "moe_lfu_stats": [_P, C.POINTER(moe_cache_stats)],
     "moe_lfu_destroy": [_P],
+    "moe_lfu_prefetch": [_P, _P, C.c_int32, _P],
+    "moe_cache_prefetch": [_P, _P, C.c_int32, _P],
+    "moe_stack_set_prefetch": [_P, C.c_int32],
     "moe_lru_create": [C.c_int32, C.POINTER(_P)],
     "moe_lru_step": [_P, C.c_int32, _P, C.c_int32, _P, _P],
     "moe_lru_stats": [_P, C.POINTER(moe_cache_stats)],
@@ -299,6 +303,22 @@ def moe_lfu_stats(lfu: int) -> dict:
 
 def moe_lfu_destroy(lfu: int):
     _check(load().moe_lfu_destroy(lfu))
+
+
+def moe_lfu_prefetch(lfu: int, experts):
+    e = np.ascontiguousarray(experts, dtype=np.int32)
+    slot = np.empty(max(1, len(e)), np.int32)
+    _check(load().moe_lfu_prefetch(lfu, e.ctypes.data, len(e), slot.ctypes.data))
+    return slot[:len(e)]
+
+
+def moe_cache_prefetch(layer: int, experts, stream=None):
+    e = np.ascontiguousarray(experts, dtype=np.int32)
+    _check(load().moe_cache_prefetch(layer, e.ctypes.data, len(e), _stream(stream)))
+
+
+def moe_stack_set_prefetch(stack: int, depth: int):
+    _check(load().moe_stack_set_prefetch(stack, depth))
 
 
 def moe_lru_create(n_slots: int) -> int:

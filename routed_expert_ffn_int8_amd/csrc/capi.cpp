@@ -130,6 +130,9 @@ struct moe_layer {
   bool own_side = false;
   hipEvent_t ev_fill = nullptr, ev_fill_start = nullptr;
   bool fill_pending = false;
+  hipEvent_t ev_ahead = nullptr;  // after the last prefetch's copies
+  bool ahead_pending = false;
+  std::vector<uint32_t> hist;     // calls that chose each expert (the prefetch predictor)
   uint64_t* h_addr = nullptr;  // pinned mirror of d_expert_addr
   int32_t* h_ids = nullptr;    // pinned routing copy
   std::vector<char> fail_expert;
@@ -143,6 +146,7 @@ moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_o
 struct moe_stack {
   std::vector<moe_layer*> layers;
   float eps = 1e-6f;
+  int prefetch_depth = 0;
   // One synchronisation area and one set of activation copies for every
   // layer's fused launches.  The layers run one after another, so a single
   // area's launch count serves them all (its tag just keeps counting), and
@@ -269,6 +273,7 @@ void free_layer(moe_layer* L) {
   if (L->h_ids) (void)hipHostFree(L->h_ids);
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
   if (L->ev_fill_start) (void)hipEventDestroy(L->ev_fill_start);
+  if (L->ev_ahead) (void)hipEventDestroy(L->ev_ahead);
   if (L->own_side && L->side) (void)hipStreamDestroy(L->side);
   delete L;
 }
@@ -395,12 +400,60 @@ LayerArgs base_args(moe_layer* L, const void* x, void* out, int T) {
   return a;
 }
 
+// Place experts ahead of use in L's own cache and copy them on its side
+// stream (after `after`, if given: the current layer's demand fills go
+// first); L's next call waits for them.  Everything earlier on the stream
+// L's calls use must be complete.
+moe_status prefetch_impl(moe_layer* L, const int32_t* experts, int n, hipEvent_t after) {
+  std::vector<int32_t> want;
+  for (int i = 0; i < n; ++i) {
+    const int32_t e = experts[i];
+    if (e < 0 || e >= L->E) return fail(MOE_ERR_INVALID, "expert %d out of range", e);
+    if (!L->fail_expert[e]) want.push_back(e);
+  }
+  if (want.empty()) return MOE_OK;
+  std::vector<int32_t> slot(want.size()), evicted(want.size());
+  L->lfu->prefetch(want.data(), (int)want.size(), slot.data(), evicted.data());
+  const size_t stride = L->rl.stride;
+  bool any = false;
+  for (size_t i = 0; i < want.size(); ++i) {
+    if (slot[i] < 0) continue;
+    if (!any && after) HIP_OK(hipStreamWaitEvent(L->side, after, 0));
+    any = true;
+    uint8_t* dst = L->d_slots + (size_t)slot[i] * stride;
+    HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)want[i] * stride, stride, hipMemcpyHostToDevice, L->side));
+    if (evicted[i] >= 0) L->h_addr[evicted[i]] = 0;
+    L->h_addr[want[i]] = reinterpret_cast<uint64_t>(dst);
+    L->stats.h2d_bytes += stride;
+  }
+  L->stats.prefetches = L->lfu->prefetches;
+  L->stats.evictions = L->lfu->evictions;
+  if (any) {
+    HIP_OK(hipEventRecord(L->ev_ahead, L->side));
+    L->ahead_pending = true;
+  }
+  return MOE_OK;
+}
+
+// The prefetch predictor: the `depth` experts the layer's calls chose most
+// often (ties to the lower id), among those not in its cache.
+std::vector<int32_t> predict_next(const moe_layer* L, int depth) {
+  std::vector<int32_t> cand;
+  for (int e = 0; e < L->E && !L->hist.empty(); ++e)
+    if (L->hist[e] > 0 && L->lfu->find(e) < 0) cand.push_back(e);
+  std::sort(cand.begin(), cand.end(), [&](int32_t a, int32_t b) {
+    return L->hist[a] != L->hist[b] ? L->hist[a] > L->hist[b] : a < b;
+  });
+  if ((int)cand.size() > depth) cand.resize(depth);
+  return cand;
+}
+
 // Make every expert chosen by the routing in L->d_ids resident in a slot of
 // the layer's cache (its own LFU slots or a shared LRU pool), after the
 // router has run on `stream`.  Blocks on the routing copy: once it is back,
 // everything queued earlier on `stream` is done, so no slot about to be
 // refilled is still being read.
-moe_status stream_in(moe_layer* L, int T, hipStream_t stream) {
+moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = nullptr, int depth = 0) {
   moe_cache_pool* P = L->pool;
   if (!L->lfu && !P) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
   const size_t n = (size_t)T * L->K;
@@ -410,6 +463,10 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream) {
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, L->ev_fill_start, L->ev_fill) == hipSuccess) L->stats.h2d_ns += (uint64_t)(ms * 1e6);
     L->fill_pending = false;
+  }
+  if (L->ahead_pending) {  // this call may use what was fetched ahead
+    HIP_OK(hipStreamWaitEvent(stream, L->ev_ahead, 0));
+    L->ahead_pending = false;
   }
   std::vector<int32_t> chosen(L->h_ids, L->h_ids + n);
   std::sort(chosen.begin(), chosen.end());
@@ -465,12 +522,20 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream) {
     L->stats.hits = L->lfu->hits;
     L->stats.misses = L->lfu->misses;
     L->stats.evictions = L->lfu->evictions;
+    L->stats.prefetch_used = L->lfu->prefetch_used;
   }
   L->stats.h2d_bytes += h2d;
+  if (L->hist.empty()) L->hist.assign(L->E, 0);
+  for (int32_t e : chosen) ++L->hist[e];
   if (any) {
     HIP_OK(hipEventRecord(L->ev_fill, side));
     HIP_OK(hipStreamWaitEvent(stream, L->ev_fill, 0));
     L->fill_pending = true;
+  }
+  if (next && depth > 0 && next->lfu) {  // fetch ahead for the next layer, behind this layer's fills
+    const std::vector<int32_t> guess = predict_next(next, depth);
+    moe_status st = prefetch_impl(next, guess.data(), (int)guess.size(), any ? L->ev_fill : nullptr);
+    if (st != MOE_OK) return st;
   }
   HIP_OK(hipMemcpyAsync(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice, stream));
   uint64_t* h_sel = reinterpret_cast<uint64_t*>(L->h_addr + L->E);
@@ -479,7 +544,8 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream) {
   return MOE_OK;
 }
 
-moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStream_t s) {
+moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStream_t s, moe_layer* next = nullptr,
+                        int depth = 0) {
   const int T = a.T;
   if (T == 0) return MOE_OK;
   if (T < 0 || T > L->max_tokens) return fail(MOE_ERR_INVALID, "n_tokens=%d not in 0..%d", T, L->max_tokens);
@@ -540,7 +606,7 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
     LayerArgs a1 = a;
     a1.stages = kStageRouter | kStageShared;
     HIP_OK(launch_decode(a1, s));
-    moe_status st = stream_in(L, T, s);
+    moe_status st = stream_in(L, T, s, next, depth);
     if (st != MOE_OK) return st;
     LayerArgs a2 = a;
     a2.stages = kStageRouted | kStageDown;
@@ -702,6 +768,7 @@ moe_status cache_common(moe_layer* L) {
     return fail(MOE_ERR_NOMEM, "pinned routing buffer failed");
   if (!L->ev_fill) HIP_OK(hipEventCreate(&L->ev_fill));
   if (!L->ev_fill_start) HIP_OK(hipEventCreate(&L->ev_fill_start));
+  if (!L->ev_ahead) HIP_OK(hipEventCreate(&L->ev_ahead));
   return MOE_OK;
 }
 // Forget where the layer's experts were (every entry absent).
@@ -815,8 +882,19 @@ moe_status moe_cache_detach(moe_layer* L) {
     L->own_side = false;
   }
   L->fill_pending = false;
+  L->ahead_pending = false;
   L->stats = moe_cache_stats{};
+  L->hist.clear();
   return clear_addresses(L);
+}
+
+moe_status moe_cache_prefetch(moe_layer* L, const int32_t* experts, int32_t n, void* stream) {
+  if (!L || (n > 0 && !experts)) return fail(MOE_ERR_INVALID, "NULL argument");
+  if (!L->lfu) return fail(MOE_ERR_STATE, "prefetch needs the layer's own cache (moe_cache_attach)");
+  if (n < 0 || n > L->n_slots) return fail(MOE_ERR_INVALID, "n=%d not in 0..%d", n, L->n_slots);
+  HIP_OK(hipSetDevice(L->dev));
+  HIP_OK(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  return prefetch_impl(L, experts, n, nullptr);
 }
 
 moe_status moe_cache_pool_stats(const moe_cache_pool* P, moe_cache_stats* out) {
@@ -948,9 +1026,17 @@ moe_status moe_stack_forward(void* h, moe_stack* S, int32_t n_tokens, const uint
     o.reuse_previous = reuse_mask ? reuse_mask[l] : 0;
     o.topk_ids = ids_out ? ids_out + l * (size_t)n_tokens * L->K : nullptr;
     o.path = MOE_PATH_AUTO;  // the rmsnorm input rules out the prefill path
-    moe_status st = forward_impl(L, a, &o, s);
+    moe_layer* next = l + 1 < S->layers.size() ? S->layers[l + 1] : nullptr;
+    moe_status st = forward_impl(L, a, &o, s, next, S->prefetch_depth);
     if (st != MOE_OK) return st;
   }
+  return MOE_OK;
+}
+
+moe_status moe_stack_set_prefetch(moe_stack* S, int32_t depth) {
+  if (!S) return fail(MOE_ERR_INVALID, "stack is NULL");
+  if (depth < 0 || depth > 64) return fail(MOE_ERR_INVALID, "depth=%d not in 0..64", depth);
+  S->prefetch_depth = depth;
   return MOE_OK;
 }
 
@@ -985,7 +1071,16 @@ moe_status moe_lfu_step(moe_lfu* P, const int32_t* chosen, int32_t n, int32_t* s
 
 moe_status moe_lfu_stats(const moe_lfu* P, moe_cache_stats* out) {
   if (!P || !out) return fail(MOE_ERR_INVALID, "NULL argument");
-  *out = moe_cache_stats{P->policy.accesses, P->policy.hits, P->policy.misses, P->policy.evictions, 0, 0};
+  *out = moe_cache_stats{P->policy.accesses, P->policy.hits,       P->policy.misses,       P->policy.evictions, 0, 0,
+                         P->policy.prefetches, P->policy.prefetch_used};
+  return MOE_OK;
+}
+
+moe_status moe_lfu_prefetch(moe_lfu* P, const int32_t* experts, int32_t n, int32_t* slot_out) {
+  if (!P || (n > 0 && (!experts || !slot_out))) return fail(MOE_ERR_INVALID, "NULL argument");
+  if (n < 0) return fail(MOE_ERR_INVALID, "n=%d negative", n);
+  std::vector<int32_t> ev(n > 0 ? n : 1);
+  P->policy.prefetch(experts, n, slot_out, ev.data());
   return MOE_OK;
 }
 
@@ -1016,7 +1111,7 @@ moe_status moe_lru_step(moe_lru* P, int32_t layer, const int32_t* chosen, int32_
 
 moe_status moe_lru_stats(const moe_lru* P, moe_cache_stats* out) {
   if (!P || !out) return fail(MOE_ERR_INVALID, "NULL argument");
-  *out = moe_cache_stats{P->policy.accesses, P->policy.hits, P->policy.misses, P->policy.evictions, 0, 0};
+  *out = moe_cache_stats{P->policy.accesses, P->policy.hits, P->policy.misses, P->policy.evictions, 0, 0, 0, 0};
   return MOE_OK;
 }
 

@@ -4,6 +4,39 @@
 
 namespace moe {
 
+void LfuPolicy::prefetch(const int32_t* experts, int n, int32_t* slot_out, int32_t* evicted_out) {
+  const int ns = (int)slots.size();
+  std::vector<char> pinned(ns, 0);
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) {
+    order[i] = i;
+    slot_out[i] = evicted_out[i] = -1;
+  }
+  std::sort(order.begin(), order.end(), [&](int a, int b) { return experts[a] < experts[b]; });
+  for (int i : order) {
+    if (find(experts[i]) >= 0) continue;
+    int victim = -1;
+    for (int s = 0; s < ns && victim < 0; ++s)
+      if (slots[s].expert < 0) victim = s;
+    if (victim < 0) {
+      for (int s = 0; s < ns; ++s) {
+        if (pinned[s] || (slots[s].tick == now && !slots[s].fetched_ahead)) continue;  // last call's working set
+        const Slot& a = slots[s];
+        if (victim < 0 || a.count < slots[victim].count ||
+            (a.count == slots[victim].count && a.tick < slots[victim].tick))
+          victim = s;
+      }
+      if (victim < 0) continue;  // every slot holds this prefetch's entries
+      ++evictions;
+      evicted_out[i] = slots[victim].expert;
+    }
+    slots[victim] = Slot{experts[i], 0, now, true};
+    pinned[victim] = 1;
+    ++prefetches;
+    slot_out[i] = victim;
+  }
+}
+
 int LfuPolicy::find(int32_t expert) const {
   for (size_t s = 0; s < slots.size(); ++s)
     if (slots[s].expert == expert) return (int)s;
@@ -26,6 +59,8 @@ bool LfuPolicy::step(const int32_t* chosen, int n, int32_t* slot_out, int32_t* m
     ++accesses;
     if (s >= 0) {
       ++hits;
+      if (slots[s].fetched_ahead) ++prefetch_used;
+      slots[s].fetched_ahead = false;
       slots[s].count += 1;
       slots[s].tick = now;
       pinned[s] = 1;
@@ -61,6 +96,7 @@ bool LfuPolicy::step(const int32_t* chosen, int n, int32_t* slot_out, int32_t* m
     slots[victim].expert = chosen[i];
     slots[victim].count = 1;
     slots[victim].tick = now;
+    slots[victim].fetched_ahead = false;
     pinned[victim] = 1;
     ++misses;
     slot_out[i] = victim;

@@ -22,12 +22,25 @@ struct LfuPolicy {
     int32_t expert = -1;
     uint32_t count = 0;
     uint64_t tick = 0;
+    bool fetched_ahead = false;  // placed by prefetch and not yet used by a call
   };
   std::vector<Slot> slots;
   uint64_t now = 0;
   uint64_t accesses = 0, hits = 0, misses = 0, evictions = 0;
+  uint64_t prefetches = 0, prefetch_used = 0;
 
   explicit LfuPolicy(int n_slots) : slots(n_slots) {}
+
+  // Fetch ahead (Rockchip-NPU plan §8 readahead, §9.5 item 2): place the
+  // experts of `experts` that are absent, in ascending id order, without
+  // counting an access.  Each takes the lowest empty slot, else evicts as a
+  // miss would, but never an entry placed by the same prefetch nor one the
+  // last call used (the working set, BigMoeOnEdge: the working set in use is
+  // protected); with no such slot left the guess is dropped.  A new entry
+  // starts at count 0 with the last call's tick, so a guess that no call
+  // uses is the first to go; a call's hit on it counts as prefetch_used.
+  // slot_out[i] / evicted_out[i] for experts[i]: -1 where it was present.
+  void prefetch(const int32_t* experts, int n, int32_t* slot_out, int32_t* evicted_out);
 
   // Decide where each chosen expert lives for this call.  `chosen` holds n
   // distinct ids.  slot_out[i] / miss_out[i] describe chosen[i]; for a miss,
@@ -38,7 +51,7 @@ struct LfuPolicy {
   // Look where an expert is without counting an access (-1 if absent).
   int find(int32_t expert) const;
   void clear_contents();
-  void clear_counters() { accesses = hits = misses = evictions = 0; }
+  void clear_counters() { accesses = hits = misses = evictions = prefetches = prefetch_used = 0; }
 };
 
 }  // namespace moe

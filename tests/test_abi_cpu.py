@@ -65,6 +65,55 @@ def test_lfu_golden_trace_through_abi():
         M.moe_lfu_destroy(lfu)
 
 
+def test_lfu_prefetch_golden_trace_through_abi():
+    here = os.path.dirname(os.path.abspath(__file__))
+    lfu = M.moe_lfu_create(4)
+    try:
+        for line in open(os.path.join(here, "golden", "lfu_prefetch_trace.txt")):
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            op, experts, slots, misses = [p.strip() for p in line.split("|")]
+            experts, slots = list(map(int, experts.split())), list(map(int, slots.split()))
+            if op == "step":
+                s, m = M.moe_lfu_step(lfu, experts)
+                assert list(s) == slots and list(m) == list(map(int, misses.split())), line
+            else:
+                assert list(M.moe_lfu_prefetch(lfu, experts)) == slots, line
+        st = M.moe_lfu_stats(lfu)
+        assert (st["accesses"], st["hits"], st["misses"], st["evictions"], st["prefetches"],
+                st["prefetch_used"]) == (6, 2, 4, 4, 4, 2)
+    finally:
+        M.moe_lfu_destroy(lfu)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_lfu_prefetch_matches_replay_on_random_traces(seed):
+    rng = np.random.default_rng(200 + seed)
+    n_slots, E, K = 16, 128, 8
+    zipf = 1.0 / np.arange(1, E + 1) ** 1.1
+    zipf /= zipf.sum()
+    lfu = M.moe_lfu_create(n_slots)
+    ref = LfuReplay(n_slots)
+    try:
+        for step in range(300):
+            if rng.random() < 0.5:
+                guess = rng.choice(E, int(rng.integers(1, 9)), replace=False, p=zipf).astype(np.int32)
+                got = M.moe_lfu_prefetch(lfu, guess)
+                placed = ref.prefetch(guess.tolist())
+                assert list(got) == [placed.get(int(e), -1) for e in guess], step
+            chosen = np.sort(rng.choice(E, K, replace=False, p=zipf)).astype(np.int32)
+            s, m = M.moe_lfu_step(lfu, chosen)
+            rs, rm = ref.step(chosen.tolist())
+            assert list(s) == rs and [bool(v) for v in m] == rm, step
+        st = M.moe_lfu_stats(lfu)
+        assert (st["accesses"], st["hits"], st["misses"], st["evictions"], st["prefetches"],
+                st["prefetch_used"]) == (ref.accesses, ref.hits, ref.misses, ref.evictions, ref.prefetches,
+                                         ref.prefetch_used)
+    finally:
+        M.moe_lfu_destroy(lfu)
+
+
 def test_lru_golden_trace_through_abi():
     here = os.path.dirname(os.path.abspath(__file__))
     lru = M.moe_lru_create(4)

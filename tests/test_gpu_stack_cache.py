@@ -149,6 +149,65 @@ def test_streamed_stack_equals_resident_stack_on_the_same_path():
         g.close()
 
 
+def test_stack_prefetch_equals_resident_and_replays():
+    """Fetch-ahead in a streamed stack (each layer prefetches the next
+    layer's historically most chosen absent experts): outputs stay exactly the
+    resident stack's, and every layer's counters, prefetches included, equal
+    the oracle replay with the same predictor on the recorded routing."""
+    torch = torch_mod()
+    w = Workload(93, "prefetch-stack-small", d=512, E=64, K=8, f=128, fs=128, act="bf16", zipf=1.1, T=1,
+                 layers=3, steps=16, reuse_p=0.6, slots=16, noise_sd=0.1)
+    depth = 6
+    arrays = [make_layer(w, layer=l, seed=11) for l in range(w.layers)]
+    res = [GpuLayer(w, a, 1) for a in arrays]
+    st = [GpuLayer(w, a, 1, residency=M.MOE_STREAMED) for a in arrays]
+    for g in res:
+        M.moe_layer_set_default_path(g.handle, M.MOE_PATH_DECODE)
+    for g in st:
+        M.moe_cache_attach(g.handle, w.slots)
+    _, eb = M.moe_layer_bytes(st[0].handle)
+    coins = make_reuse_coins(w, w.steps).astype(np.uint8)
+    xs = make_tokens(w, w.steps, stream=29)  # a fresh token every step: misses to predict
+    s_res = M.moe_stack_create([g.handle for g in res], 1e-6)
+    s_st = M.moe_stack_create([g.handle for g in st], 1e-6)
+    M.moe_stack_set_prefetch(s_st, depth)
+    ref = [LfuReplay(w.slots) for _ in range(w.layers)]
+    hist = np.zeros((w.layers, w.E), np.int64)
+
+    def guess(l):
+        cand = [e for e in range(w.E) if hist[l][e] > 0 and e not in ref[l].expert]
+        return sorted(cand, key=lambda e: (-hist[l][e], e))[:depth]
+
+    ids = torch.empty((w.layers, 1, w.K), dtype=torch.int32, device="cuda")
+    for t in range(w.steps):
+        ha, hb = to_device(xs[t:t + 1]), to_device(xs[t:t + 1])
+        M.moe_stack_forward(ha, s_res, 1, reuse_mask=coins[t])
+        M.moe_stack_forward(hb, s_st, 1, reuse_mask=coins[t], ids_out=ids)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(ha), to_host(hb)), f"step {t}: streamed with prefetch differs"
+        for l, row in enumerate(ids.cpu().numpy()[:, 0]):
+            chosen = sorted(set(row.tolist()))
+            ref[l].step(chosen)
+            hist[l][chosen] += 1
+            if l + 1 < w.layers:
+                ref[l + 1].prefetch(guess(l + 1))
+    used = 0
+    for g, r in zip(st, ref):
+        s = M.moe_cache_stats_get(g.handle)
+        assert (s["accesses"], s["hits"], s["misses"], s["evictions"], s["prefetches"], s["prefetch_used"]) == \
+            (r.accesses, r.hits, r.misses, r.evictions, r.prefetches, r.prefetch_used)
+        assert s["h2d_bytes"] == (r.misses + r.prefetches) * eb
+        used += r.prefetch_used
+    assert used > 0, "no prefetch was ever used"
+    with pytest.raises(M.MoeError):
+        M.moe_stack_set_prefetch(s_st, 65)
+    M.moe_stack_destroy(s_res)
+    M.moe_stack_destroy(s_st)
+    for g in res + st:
+        assert M.moe_layer_check_errors(g.handle) == 0
+        g.close()
+
+
 def test_pooled_lru_stack_equals_resident_and_replays():
     """Three streamed layers share one LRU pool smaller than their combined
     working sets: the stack ends in exactly the resident stack's state (same

@@ -327,6 +327,24 @@ def test_lfu_golden_trace():
     assert (lfu.accesses, lfu.hits, lfu.misses, lfu.evictions) == (10, 2, 8, 4)
 
 
+def test_lfu_prefetch_golden_trace():
+    lfu = LfuReplay(4)
+    for line in open(os.path.join(HERE, "golden", "lfu_prefetch_trace.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        op, experts, slots, misses = [p.strip() for p in line.split("|")]
+        experts, slots = list(map(int, experts.split())), list(map(int, slots.split()))
+        if op == "step":
+            got_slots, got_miss = lfu.step(experts)
+            assert got_slots == slots and [int(m) for m in got_miss] == list(map(int, misses.split())), line
+        else:
+            placed = lfu.prefetch(experts)
+            assert [placed.get(e, -1) for e in experts] == slots, line
+    assert (lfu.accesses, lfu.hits, lfu.misses, lfu.evictions, lfu.prefetches, lfu.prefetch_used) == \
+        (6, 2, 4, 4, 4, 2)
+
+
 def _lru_golden_rows():
     rows = []
     for line in open(os.path.join(HERE, "golden", "lru_pool_trace.txt")):
