@@ -195,6 +195,27 @@ def run_decode(args, M, torch, np):
     kernels = kernel_table(prof, alg)
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     achieved = kernels[dom]["gbps"]
+    # Cold: a 512 MB device copy before every token evicts the 256 MB
+    # Infinity Cache; the layer's own kernel events time each token, so the
+    # copies are outside the measurement.
+    cold = None
+    if not args.no_extra:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        call = fwd(path)
+        M.moe_layer_profile(layer, True)
+        for i in list(timed)[:200]:
+            dst.copy_(src)
+            call(i, stream)
+        torch.cuda.synchronize()
+        pc = kernel_table(M.moe_layer_profile_read(layer), alg)
+        M.moe_layer_profile(layer, False)
+        del src, dst
+        tot_us = sum(v["avg_us"] for v in pc.values())
+        cold_bytes = w.K * (2 * gu + dn) + 2 * sgu + sdn + router_bytes(w)
+        cold = {"tokens": min(200, args.steps), "flush": "512 MB device copy before each token",
+                "kernel_us_per_token": round(tot_us, 3), "hbm_gbps": round(cold_bytes / (tot_us * 1e3), 1),
+                "kernels": pc}
     bytes_token = w.K * (2 * gu + dn) + 2 * sgu + sdn + router_bytes(w)
     result = {
         "metric": "MoE FFN tok/s (decode b=1, one layer, int4 g64 experts, int8 router)",
@@ -223,6 +244,7 @@ def run_decode(args, M, torch, np):
         "decode_path": args.decode_path,
         "kernels": kernels,
         "three_kernel_path": {"tok_s": round(args.steps / dt3, 1), "kernels": kernel_table(prof3, alg)},
+        "cold": cold,
     }
     M.moe_layer_destroy(layer)
     if not args.no_cpu:
