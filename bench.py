@@ -318,6 +318,25 @@ def run_prefill(args, M, torch, np, chunks=None, summary=False):
         "kernels": kernels,
     }
     if not summary:
+        # Dense routing: every token forced to experts 0..K-1, so each expert
+        # tile is full and only K + 1 experts are read (~460 flop/B, past the
+        # bf16 ridge): the GEMMs' own compute efficiency.
+        forced = torch.arange(w.K, dtype=torch.int32, device="cuda").repeat(C, 1).contiguous()
+
+        def dense(i, s):
+            o = M.fwd_opts(forced_ids=forced, path=M.MOE_PATH_PREFILL)
+            M.moe_layer_forward_ex(x[i * C:(i + 1) * C], layer, out[i * C:(i + 1) * C], C, o, s)
+
+        dense(0, stream)
+        torch.cuda.synchronize()
+        ddt = graph_time(torch, [lambda s, i=i: dense(i, s) for i in range(nch)], 10) / nch
+        dprof, _ = gated_profile(M, torch, layer, [lambda i=i: dense(i, stream) for i in range(nch)], stream, 10)
+        dk = kernel_table(dprof, {}, kflops)
+        res["dense_routing"] = {
+            "what": "all tokens forced to experts 0..7 (full 16-token tiles, 9 experts read)",
+            "ms_per_chunk": round(ddt * 1e3, 4), "tflops": round(flops / ddt / 1e12, 2),
+            "mfma_util": round(flops / ddt / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": {k: dk[k] for k in ("prefill_gate_up", "prefill_down") if k in dk}}
         for T in (512, 2048):  # longer prompts as sequential 128-token chunks inside one call
             if T > C * nch:
                 continue

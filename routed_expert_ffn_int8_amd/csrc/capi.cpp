@@ -134,7 +134,10 @@ struct moe_layer {
   bool ahead_pending = false;
   std::vector<uint32_t> hist;     // calls that chose each expert (the prefetch predictor)
   uint64_t* h_addr = nullptr;  // pinned mirror of d_expert_addr
-  int32_t* h_ids = nullptr;    // pinned routing copy
+  bool addr_dirty = false;     // h_addr changed since d_expert_addr was last uploaded
+  int32_t* h_ids = nullptr;    // pinned, coherent routing copy [max_tokens*K], then a sequence word
+  void* d_host_ids = nullptr;  // its device view
+  uint32_t host_seq = 0;       // sequence number of the last one-token routing written by the GPU
   std::vector<char> fail_expert;
   moe_cache_stats stats{};
   uint64_t device_bytes = 0;
@@ -310,9 +313,8 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
     if (hipHostMalloc(reinterpret_cast<void**>(&L->h_store), E * stride, hipHostMallocDefault) != hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned host store of %zu bytes failed", E * stride);
     pack_parallel(D, L->rl, L->h_store);
-    // pinned: expert table [E] followed by the chosen-blob table [max_tokens*K]
-    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_addr), (E + (size_t)L->max_tokens * L->K) * 8,
-                      hipHostMallocDefault) != hipSuccess)
+    // pinned mirror of the device expert table [E]
+    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_addr), E * 8, hipHostMallocDefault) != hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned expert table failed");
     std::memset(L->h_addr, 0, E * 8);
     L->fail_expert.assign(E, 0);
@@ -424,6 +426,7 @@ moe_status prefetch_impl(moe_layer* L, const int32_t* experts, int n, hipEvent_t
     HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)want[i] * stride, stride, hipMemcpyHostToDevice, L->side));
     if (evicted[i] >= 0) L->h_addr[evicted[i]] = 0;
     L->h_addr[want[i]] = reinterpret_cast<uint64_t>(dst);
+    L->addr_dirty = true;
     L->stats.h2d_bytes += stride;
   }
   L->stats.prefetches = L->lfu->prefetches;
@@ -433,6 +436,22 @@ moe_status prefetch_impl(moe_layer* L, const int32_t* experts, int n, hipEvent_t
     L->ahead_pending = true;
   }
   return MOE_OK;
+}
+
+// Byte offset of the sequence word behind the routing copy in h_ids.
+size_t host_flag_offset(const moe_layer* L) { return ((size_t)L->max_tokens * L->K * 4 + 63) / 64 * 64; }
+
+// Spin until the GPU has written `seq` behind the routing in h_ids (about
+// 2 s at most); true when it has.
+bool wait_host_flag(const moe_layer* L, uint32_t seq) {
+  const uint32_t* flag = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(L->h_ids) +
+                                                           host_flag_offset(L));
+  const auto t0 = std::chrono::steady_clock::now();
+  for (uint32_t i = 1;; ++i) {
+    if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == seq) return true;
+    if ((i & 4095) == 0 && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(2)) return false;
+    __builtin_ia32_pause();
+  }
 }
 
 // The prefetch predictor: the `depth` experts the layer's calls chose most
@@ -452,13 +471,23 @@ std::vector<int32_t> predict_next(const moe_layer* L, int depth) {
 // the layer's cache (its own LFU slots or a shared LRU pool), after the
 // router has run on `stream`.  Blocks on the routing copy: once it is back,
 // everything queued earlier on `stream` is done, so no slot about to be
-// refilled is still being read.
-moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = nullptr, int depth = 0) {
+// refilled is still being read.  (A one-token call instead spins until the
+// top-K kernel has published the routing: stream order then also puts every
+// earlier command of the stream behind it.)
+moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = nullptr, int depth = 0,
+                     uint32_t seq = 0) {
   moe_cache_pool* P = L->pool;
   if (!L->lfu && !P) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
   const size_t n = (size_t)T * L->K;
-  HIP_OK(hipMemcpyAsync(L->h_ids, L->d_ids, n * 4, hipMemcpyDeviceToHost, stream));
-  HIP_OK(hipStreamSynchronize(stream));
+  if (seq) {  // one token: the top-K kernel writes the ids and then seq into host memory
+    if (!wait_host_flag(L, seq)) {  // not within the time limit: the stream's own status decides
+      HIP_OK(hipStreamSynchronize(stream));
+      if (!wait_host_flag(L, seq)) return fail(MOE_ERR_STATE, "the routing of the call did not reach the host");
+    }
+  } else {
+    HIP_OK(hipMemcpyAsync(L->h_ids, L->d_ids, n * 4, hipMemcpyDeviceToHost, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+  }
   if (L->fill_pending) {  // account the previous call's fills (complete by now)
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, L->ev_fill_start, L->ev_fill) == hipSuccess) L->stats.h2d_ns += (uint64_t)(ms * 1e6);
@@ -497,9 +526,13 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
     HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice, side));
     if (ev_expert[i] >= 0) {  // the slot's previous entry (of this layer, or of another for a pool)
       moe_layer* owner = P ? (ev_layer[i] >= 0 ? P->members[ev_layer[i]] : nullptr) : L;
-      if (owner) owner->h_addr[ev_expert[i]] = 0;  // that layer re-uploads its table on its next call
+      if (owner) {  // that layer re-uploads its table on its next call
+        owner->h_addr[ev_expert[i]] = 0;
+        owner->addr_dirty = true;
+      }
     }
     L->h_addr[chosen[i]] = reinterpret_cast<uint64_t>(dst);
+    L->addr_dirty = true;
     h2d += stride;
   }
   if (P) {  // this layer's share of the pool's counts
@@ -537,10 +570,14 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
     moe_status st = prefetch_impl(next, guess.data(), (int)guess.size(), any ? L->ev_fill : nullptr);
     if (st != MOE_OK) return st;
   }
-  HIP_OK(hipMemcpyAsync(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice, stream));
-  uint64_t* h_sel = reinterpret_cast<uint64_t*>(L->h_addr + L->E);
-  for (size_t i = 0; i < n; ++i) h_sel[i] = L->h_addr[L->h_ids[i]];
-  HIP_OK(hipMemcpyAsync(L->d_sel, h_sel, n * 8, hipMemcpyHostToDevice, stream));
+  // The routed kernel reads each chosen expert's address from the device
+  // table, so the table goes up only when a fill, a fetch-ahead or another
+  // layer's eviction changed it (the stream was synchronised above, so no
+  // earlier upload of h_addr is still pending).
+  if (L->addr_dirty) {
+    HIP_OK(hipMemcpyAsync(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice, stream));
+    L->addr_dirty = false;
+  }
   return MOE_OK;
 }
 
@@ -605,11 +642,20 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
   if (L->residency == MOE_STREAMED) {
     LayerArgs a1 = a;
     a1.stages = kStageRouter | kStageShared;
+    uint32_t seq = 0;
+    if (T == 1 && L->d_host_ids) {
+      seq = ++L->host_seq;
+      if (seq == 0) seq = ++L->host_seq;  // 0 means "no flag"
+      a1.host_ids = static_cast<int32_t*>(L->d_host_ids);
+      a1.host_flag = reinterpret_cast<uint32_t*>(static_cast<char*>(L->d_host_ids) + host_flag_offset(L));
+      a1.host_seq = seq;
+    }
     HIP_OK(launch_decode(a1, s));
-    moe_status st = stream_in(L, T, s, next, depth);
+    moe_status st = stream_in(L, T, s, next, depth, seq);
     if (st != MOE_OK) return st;
     LayerArgs a2 = a;
     a2.stages = kStageRouted | kStageDown;
+    a2.sel_from_table = 1;
     HIP_OK(launch_decode(a2, s));
   } else {
     a.topk_in_gate_up = 1;
@@ -762,10 +808,14 @@ moe_status moe_layer_profile_read(moe_layer* L, int64_t* launches, double* total
 namespace {
 // Routing copy and fill events of a streamed layer that gets a cache.
 moe_status cache_common(moe_layer* L) {
-  if (!L->h_ids &&
-      hipHostMalloc(reinterpret_cast<void**>(&L->h_ids), (size_t)L->max_tokens * L->K * 4, hipHostMallocDefault) !=
-          hipSuccess)
-    return fail(MOE_ERR_NOMEM, "pinned routing buffer failed");
+  if (!L->h_ids) {  // coherent, so the top-K kernel can write a one-token routing straight into it
+    const size_t bytes = host_flag_offset(L) + 64;
+    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_ids), bytes, hipHostMallocCoherent | hipHostMallocMapped) !=
+        hipSuccess)
+      return fail(MOE_ERR_NOMEM, "pinned routing buffer failed");
+    std::memset(L->h_ids, 0, bytes);
+    HIP_OK(hipHostGetDevicePointer(&L->d_host_ids, L->h_ids, 0));
+  }
   if (!L->ev_fill) HIP_OK(hipEventCreate(&L->ev_fill));
   if (!L->ev_fill_start) HIP_OK(hipEventCreate(&L->ev_fill_start));
   if (!L->ev_ahead) HIP_OK(hipEventCreate(&L->ev_ahead));
@@ -775,6 +825,7 @@ moe_status cache_common(moe_layer* L) {
 moe_status clear_addresses(moe_layer* L) {
   std::memset(L->h_addr, 0, (size_t)L->E * 8);
   HIP_OK(hipMemcpy(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice));
+  L->addr_dirty = false;
   return MOE_OK;
 }
 }  // namespace

@@ -447,6 +447,12 @@ __global__ __launch_bounds__(64) void topk_kernel(LayerArgs a) {
   float w;
   topk_wave<NE>(a, blockIdx.x, s_logits, &id, &w, scratch);
   publish_routing(a, blockIdx.x, threadIdx.x, id, w);
+  if (a.host_ids) {  // one token (one workgroup): its ids into host memory, then the sequence number
+    if (threadIdx.x < a.K)
+      __hip_atomic_store(a.host_ids + threadIdx.x, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(a.host_flag, a.host_seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
 // ---------------------------------------------------------------- kernel B
@@ -479,6 +485,11 @@ __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
     }
     __syncthreads();
     blob = a.expert_base + (size_t)scratch[0] * a.expert_stride;
+  } else if (a.sel_from_table) {  // streamed experts: the table was brought up to date after the routing
+    const size_t o = (size_t)t * a.K + k;
+    const uint64_t addr = a.expert_addr[a.ids[o]];
+    if (rb == 0 && threadIdx.x == 0) a.sel_addr[o] = addr;  // for the down kernel, which runs after this one
+    blob = reinterpret_cast<const uint8_t*>(addr);
   } else {
     blob = reinterpret_cast<const uint8_t*>(a.sel_addr[(size_t)t * a.K + k]);
   }

@@ -74,6 +74,11 @@ struct LayerArgs {
   // 4 routed gate/up, 8 down + combine
   int stages;
   int topk_in_gate_up;  // 1: every routed gate/up workgroup runs the top-K itself
+  int32_t* host_ids;    // T == 1, streamed layers: the top-K kernel also writes the chosen ids here
+  uint32_t* host_flag;  // (host memory, device view), then host_seq into *host_flag
+  uint32_t host_seq;
+  int sel_from_table;   // 1: routed gate/up takes each chosen expert's address from expert_addr[ids]
+                        // (current after the call's fills) and writes it to sel_addr for the down kernel
   int fused;            // 1: one launch per layer (batch 1, bf16, resident experts)
   Profiler* prof;  // host pointer, never read by the kernels
 };
