@@ -138,6 +138,7 @@ struct moe_layer {
   int32_t* h_ids = nullptr;    // pinned, coherent routing copy [max_tokens*K], then a sequence word
   void* d_host_ids = nullptr;  // its device view
   uint32_t host_seq = 0;       // sequence number of the last one-token routing written by the GPU
+  uint32_t* d_go = nullptr;    // device copy of the verdict word of a call launched ahead
   std::vector<char> fail_expert;
   moe_cache_stats stats{};
   uint64_t device_bytes = 0;
@@ -274,6 +275,7 @@ void free_layer(moe_layer* L) {
   if (L->h_store) (void)hipHostFree(L->h_store);
   if (L->h_addr) (void)hipHostFree(L->h_addr);
   if (L->h_ids) (void)hipHostFree(L->h_ids);
+  (void)hipFree(L->d_go);
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
   if (L->ev_fill_start) (void)hipEventDestroy(L->ev_fill_start);
   if (L->ev_ahead) (void)hipEventDestroy(L->ev_ahead);
@@ -441,6 +443,16 @@ moe_status prefetch_impl(moe_layer* L, const int32_t* experts, int n, hipEvent_t
 // Byte offset of the sequence word behind the routing copy in h_ids.
 size_t host_flag_offset(const moe_layer* L) { return ((size_t)L->max_tokens * L->K * 4 + 63) / 64 * 64; }
 
+// The verdict word of a call whose routed and down kernels were launched
+// before the cache step (its own 64-byte line after the sequence word):
+// 2*seq to run them, 2*seq+1 to skip them.
+uint32_t* go_word(const moe_layer* L) {
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(L->h_ids) + host_flag_offset(L) + 64);
+}
+void set_go(const moe_layer* L, uint32_t seq, bool run) {
+  __atomic_store_n(go_word(L), 2u * seq + (run ? 0u : 1u), __ATOMIC_RELEASE);
+}
+
 // Spin until the GPU has written `seq` behind the routing in h_ids (about
 // 2 s at most); true when it has.
 bool wait_host_flag(const moe_layer* L, uint32_t seq) {
@@ -475,7 +487,7 @@ std::vector<int32_t> predict_next(const moe_layer* L, int depth) {
 // top-K kernel has published the routing: stream order then also puts every
 // earlier command of the stream behind it.)
 moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = nullptr, int depth = 0,
-                     uint32_t seq = 0) {
+                     uint32_t seq = 0, int* verdict = nullptr) {
   moe_cache_pool* P = L->pool;
   if (!L->lfu && !P) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
   const size_t n = (size_t)T * L->K;
@@ -513,6 +525,12 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
     P->policy->step(L->pool_id, chosen.data(), m, slot.data(), miss.data(), ev_layer.data(), ev_expert.data());
   else
     L->lfu->step(chosen.data(), m, slot.data(), miss.data(), ev_expert.data());
+  if (verdict) {  // kernels launched ahead: they run now when every chosen expert was a hit
+    bool any_miss = false;
+    for (int i = 0; i < m; ++i) any_miss |= miss[i] != 0;
+    set_go(L, seq, !any_miss);
+    *verdict = any_miss ? 0 : 1;
+  }
   const size_t stride = L->rl.stride;
   uint8_t* base = P ? P->d_slots : L->d_slots;
   hipStream_t side = P ? P->side : L->side;
@@ -645,18 +663,38 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
     uint32_t seq = 0;
     if (T == 1 && L->d_host_ids) {
       seq = ++L->host_seq;
-      if (seq == 0) seq = ++L->host_seq;  // 0 means "no flag"
+      if (seq >= (1u << 30)) seq = L->host_seq = 1;  // 0 means "no flag"; the verdict word holds 2*seq+1
       a1.host_ids = static_cast<int32_t*>(L->d_host_ids);
       a1.host_flag = reinterpret_cast<uint32_t*>(static_cast<char*>(L->d_host_ids) + host_flag_offset(L));
       a1.host_seq = seq;
     }
     HIP_OK(launch_decode(a1, s));
-    moe_status st = stream_in(L, T, s, next, depth, seq);
-    if (st != MOE_OK) return st;
     LayerArgs a2 = a;
     a2.stages = kStageRouted | kStageDown;
     a2.sel_from_table = 1;
-    HIP_OK(launch_decode(a2, s));
+    // One token and an up-to-date device table: the routed and down kernels
+    // go out now and wait on the GPU for the host's verdict, so their launch
+    // overlaps the routing hand-off and the cache step.  A call with a miss
+    // skips them and runs them again behind its fills.
+    const bool ahead = seq != 0 && !L->addr_dirty;
+    if (ahead) {
+      if (L->ahead_pending) {  // fetched-ahead copies land before these kernels read their slots
+        HIP_OK(hipStreamWaitEvent(s, L->ev_ahead, 0));
+        L->ahead_pending = false;
+      }
+      LayerArgs a3 = a2;
+      a3.go_host = reinterpret_cast<const uint32_t*>(static_cast<char*>(L->d_host_ids) + host_flag_offset(L) + 64);
+      a3.go_dev = L->d_go;
+      a3.host_seq = seq;
+      HIP_OK(launch_decode(a3, s));
+    }
+    int verdict = -1;
+    moe_status st = stream_in(L, T, s, next, depth, seq, ahead ? &verdict : nullptr);
+    if (st != MOE_OK) {
+      if (ahead && verdict < 0) set_go(L, seq, false);
+      return st;
+    }
+    if (verdict != 1) HIP_OK(launch_decode(a2, s));
   } else {
     a.topk_in_gate_up = 1;
     HIP_OK(launch_decode(a, s));
@@ -809,12 +847,16 @@ namespace {
 // Routing copy and fill events of a streamed layer that gets a cache.
 moe_status cache_common(moe_layer* L) {
   if (!L->h_ids) {  // coherent, so the top-K kernel can write a one-token routing straight into it
-    const size_t bytes = host_flag_offset(L) + 64;
+    const size_t bytes = host_flag_offset(L) + 128;  // + the sequence word, + the verdict word
     if (hipHostMalloc(reinterpret_cast<void**>(&L->h_ids), bytes, hipHostMallocCoherent | hipHostMallocMapped) !=
         hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned routing buffer failed");
     std::memset(L->h_ids, 0, bytes);
     HIP_OK(hipHostGetDevicePointer(&L->d_host_ids, L->h_ids, 0));
+  }
+  if (!L->d_go) {
+    if (dalloc(&L->d_go, 256) != hipSuccess) return fail(MOE_ERR_NOMEM, "verdict word alloc failed");
+    HIP_OK(hipMemset(L->d_go, 0, 256));
   }
   if (!L->ev_fill) HIP_OK(hipEventCreate(&L->ev_fill));
   if (!L->ev_fill_start) HIP_OK(hipEventCreate(&L->ev_fill_start));

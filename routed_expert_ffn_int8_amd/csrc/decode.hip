@@ -456,6 +456,36 @@ __global__ __launch_bounds__(64) void topk_kernel(LayerArgs a) {
 }
 
 // ---------------------------------------------------------------- kernel B
+// Kernels launched before the host has run the cache step of the call wait
+// for its verdict: block 0 polls the host's word (over the host link, one
+// lane, one load in flight) and relays it into device memory, where the
+// other blocks poll it.  Bounded: a wait that runs out sets the error flag and
+// skips.  Returns true to run the call, false to skip it.
+constexpr uint32_t kGoSpinLimit = 1u << 21;  // relay polls (about 1.5 us each); the others poll 2x as often
+__device__ bool wait_go(const LayerArgs& a) {
+  __shared__ uint32_t s_go;
+  const uint32_t run = 2u * a.host_seq;
+  if (threadIdx.x == 0) {
+    const bool relay = blockIdx.x == 0 && blockIdx.y == 0;
+    uint32_t v = 0;
+    for (uint32_t it = 0;; ++it) {
+      v = relay ? __hip_atomic_load(a.go_host, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                : __hip_atomic_load(a.go_dev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((v >> 1) == a.host_seq) break;
+      if (it == (relay ? kGoSpinLimit : 2 * kGoSpinLimit)) {
+        atomicOr(a.err, kErrSyncTimeout);
+        v = run + 1;
+        break;
+      }
+      if (!relay) __builtin_amdgcn_s_sleep(1);  // the relay's own load is a host-link round trip
+    }
+    if (relay) __hip_atomic_store(a.go_dev, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_go = v;
+  }
+  __syncthreads();
+  return s_go == run;
+}
+
 template <int ACT, int MAXI, int NE>
 __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -486,6 +516,7 @@ __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
     __syncthreads();
     blob = a.expert_base + (size_t)scratch[0] * a.expert_stride;
   } else if (a.sel_from_table) {  // streamed experts: the table was brought up to date after the routing
+    if (a.go_host && !wait_go(a)) return;  // skipped: the host runs the call again after its fills
     const size_t o = (size_t)t * a.K + k;
     const uint64_t addr = a.expert_addr[a.ids[o]];
     if (rb == 0 && threadIdx.x == 0) a.sel_addr[o] = addr;  // for the down kernel, which runs after this one
@@ -659,6 +690,8 @@ template <int ACT, int MAXI>
 __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int t = blockIdx.y;
+  // launched before the host's cache step: the routed kernel before this one relayed the verdict
+  if (a.go_dev && __hip_atomic_load(a.go_dev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 2u * a.host_seq) return;
   down_block<ACT, MAXI>(a, t, blockIdx.x, a.sel_addr + (size_t)t * a.K, a.wts + (size_t)t * a.K, smem);
 }
 

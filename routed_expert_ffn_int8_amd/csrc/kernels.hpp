@@ -77,6 +77,9 @@ struct LayerArgs {
   int32_t* host_ids;    // T == 1, streamed layers: the top-K kernel also writes the chosen ids here
   uint32_t* host_flag;  // (host memory, device view), then host_seq into *host_flag
   uint32_t host_seq;
+  const uint32_t* go_host;  // routed/down kernels launched before the host's cache step: the host writes
+  uint32_t* go_dev;         // 2*host_seq (run) or 2*host_seq+1 (skip) into *go_host; routed gate/up
+                            // block 0 relays it into *go_dev, read by its other blocks and the down kernel
   int sel_from_table;   // 1: routed gate/up takes each chosen expert's address from expert_addr[ids]
                         // (current after the call's fills) and writes it to sel_addr for the down kernel
   int fused;            // 1: one launch per layer (batch 1, bf16, resident experts)
