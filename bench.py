@@ -317,7 +317,7 @@ def run_prefill(args, M, torch, np, chunks=None, summary=False):
                      "traffic": read_traffic(dom, "prefill_chunk"), "kernel": dom},
         "kernels": kernels,
     }
-    if not summary:
+    if not summary and not args.no_extra:
         # Dense routing: every token forced to experts 0..K-1, so each expert
         # tile is full and only K + 1 experts are read (~460 flop/B, past the
         # bf16 ridge): the GEMMs' own compute efficiency.
@@ -540,7 +540,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", choices=("decode", "prefill", "stack", "stream"), default="decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="decode only, without the prefill summary")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="decode: without the prefill summary; prefill: without the dense-routing run")
     ap.add_argument("--cpu-tokens", type=int, default=48)
     ap.add_argument("--decode-path", choices=("fused", "split"), default="fused",
                     help="fused: one kernel per layer and token; split: router+shared | routed gate/up | down")
