@@ -292,7 +292,14 @@ def test_streamed_fault_injection_leaves_state_unchanged():
     assert M.moe_cache_stats_get(st.handle)["misses"] == stats0["misses"]
     for e in range(w.E):
         M.moe_cache_fail_expert(st.handle, e, False)
-    st.forward(x[2:3], path=M.MOE_PATH_DECODE)  # recovers
+    y_s, _, _ = st.forward(x[2:3], path=M.MOE_PATH_DECODE)  # recovers
+    res = GpuLayer(w, arrays, 1)
+    y_r, _, _ = res.forward(x[2:3], path=M.MOE_PATH_DECODE)
+    assert np.array_equal(y_r, y_s)
+    # the failed call's routed and down kernels, launched before the cache
+    # step, were told to skip: none of their bounded waits ran out
+    assert M.moe_layer_check_errors(st.handle) == 0
+    res.close()
     st.close()
 
 
