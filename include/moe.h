@@ -127,8 +127,13 @@ moe_status moe_layer_destroy(moe_layer* layer);
  * x, out: DEVICE [n_tokens][d_model] of act_dtype, row-major; may not alias.
  * n_tokens: 0..max_tokens (0 is a no-op).
  * Resident layers: only enqueues work on `stream`.  Streamed layers: blocks
- * the calling thread until the routing of this call is known on the host
- * (one small device->host copy), then enqueues the cache fills and compute. */
+ * the calling thread until the routing of this call is known on the host,
+ * then enqueues the cache fills and compute.  With one token the top-K kernel
+ * writes the routing into pinned host memory and the thread spins on it (up
+ * to about 2 s, then it waits for the stream); the expert kernels are then
+ * already enqueued and run as soon as the host reports that every chosen
+ * expert was cached, or are skipped and enqueued again behind the fills.
+ * More tokens: one small device->host copy and a stream synchronisation. */
 moe_status moe_layer_forward(const void* x, moe_layer* layer, void* out, int32_t n_tokens, void* stream);
 
 /* Optional controls of one forward call.  Every field may be 0/NULL. */
