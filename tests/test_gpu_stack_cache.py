@@ -117,6 +117,37 @@ def test_streamed_layer_bit_identical_and_counters_replay(w):
     st.close()
 
 
+def test_streamed_one_and_two_token_calls_interleave():
+    """One-token calls hand the routing over through host memory and launch
+    their expert kernels ahead; two-token calls copy and synchronise.  Mixed
+    on one layer they stay bit-identical to a resident layer, and the cache
+    follows the replay of the calls' chosen sets."""
+    w = CACHE_W
+    arrays = make_layer(w)
+    res = GpuLayer(w, arrays, 2)
+    st = GpuLayer(w, arrays, 2, residency=M.MOE_STREAMED)
+    M.moe_cache_attach(st.handle, w.slots)
+    x = make_tokens(w, 40, stream=31)
+    replay = LfuReplay(w.slots)
+    i = 0
+    for T in [1, 2, 1, 1, 2, 2, 1, 2, 1, 1, 2, 1] * 2:
+        y_r, ids_r, w_r = res.forward(x[i:i + T], path=M.MOE_PATH_DECODE)
+        y_s, ids_s, w_s = st.forward(x[i:i + T], path=M.MOE_PATH_DECODE)
+        assert np.array_equal(y_r, y_s), f"call at token {i} (T={T}) differs from resident"
+        assert np.array_equal(ids_r, ids_s) and np.array_equal(w_r, w_s)
+        replay.step(sorted(set(int(e) for e in ids_s.flatten())))
+        i += T
+    stats = M.moe_cache_stats_get(st.handle)
+    assert (stats["accesses"], stats["hits"], stats["misses"], stats["evictions"]) == \
+        (replay.accesses, replay.hits, replay.misses, replay.evictions)
+    assert replay.misses > 0 and replay.hits > 0
+    experts, counts = M.moe_cache_contents(st.handle, w.slots)
+    assert list(experts) == replay.expert and list(counts) == replay.count
+    assert M.moe_layer_check_errors(st.handle) == 0
+    res.close()
+    st.close()
+
+
 def test_streamed_stack_equals_resident_stack_on_the_same_path():
     """A stack of streamed layers (16-slot LFU caches, fills on a side stream)
     ends in exactly the state of the same stack with every expert resident,
