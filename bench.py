@@ -530,7 +530,48 @@ def run_stream(args, M, torch, np):
     M.moe_cache_pool_destroy(pool)
     for L in res_layers + st_layers:
         M.moe_layer_destroy(L)
+    res["prefill_through_cache"] = run_stream_prefill(M, torch, np, w)
     return res
+
+
+def run_stream_prefill(M, torch, np, w, nch=4):
+    """Prefill (128-token chunks) of one streaming-shape layer whose experts
+    live in host memory: each chunk's experts go through the 16-slot LFU cache
+    in groups; against the same layer resident in HBM."""
+    from gen.workloads import make_layer, make_tokens
+    arrays = make_layer(w, layer=0)
+    d1, k1 = M.make_desc(arrays, w.d, w.E, w.K, w.f, w.fs, M.MOE_ACT_BF16, 128)
+    d2, k2 = M.make_desc(arrays, w.d, w.E, w.K, w.f, w.fs, M.MOE_ACT_BF16, 128, M.MOE_STREAMED)
+    res_l, st_l = M.moe_layer_create(d1), M.moe_layer_create(d2)
+    del k1, k2, arrays
+    M.moe_cache_attach(st_l, w.slots)
+    x = torch.from_numpy(make_tokens(w, 128 * nch, stream=8).view(np.int16)).view(torch.bfloat16).cuda()
+    outs = {}
+    times = {}
+    for name, L in (("resident", res_l), ("streamed", st_l)):
+        out = torch.empty_like(x)
+        M.moe_layer_forward_ex(x[:128], L, out[:128], 128, M.fwd_opts(path=M.MOE_PATH_PREFILL))  # warm-up
+        torch.cuda.synchronize()
+        if name == "streamed":
+            M.moe_cache_reset(L, 1)  # the timed chunks start from an empty cache and zero counts
+        t0 = time.perf_counter()
+        for i in range(nch):
+            M.moe_layer_forward_ex(x[i * 128:(i + 1) * 128], L, out[i * 128:(i + 1) * 128], 128,
+                                   M.fwd_opts(path=M.MOE_PATH_PREFILL))
+        torch.cuda.synchronize()
+        times[name] = (time.perf_counter() - t0) / nch
+        outs[name] = out
+    st = M.moe_cache_stats_get(st_l)
+    r = {"chunks": nch, "ms_per_chunk": round(times["streamed"] * 1e3, 3),
+         "tok_s": round(128 / times["streamed"], 1), "resident_ms_per_chunk": round(times["resident"] * 1e3, 4),
+         "misses_per_chunk": st["misses"] / nch, "hits_per_chunk": st["hits"] / nch,
+         "h2d_mb_per_chunk": round(st["h2d_bytes"] / nch / 1e6, 1),
+         "h2d_gbps": round(st["h2d_bytes"] / nch / times["streamed"] / 1e9, 2),
+         "equals_resident": bool(torch.equal(outs["resident"], outs["streamed"]))}
+    print(f"[bench] prefill through the cache: {r}", file=sys.stderr, flush=True)
+    M.moe_layer_destroy(res_l)
+    M.moe_layer_destroy(st_l)
+    return r
 
 
 def main():

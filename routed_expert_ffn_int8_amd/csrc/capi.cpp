@@ -139,6 +139,12 @@ struct moe_layer {
   void* d_host_ids = nullptr;  // its device view
   uint32_t host_seq = 0;       // sequence number of the last one-token routing written by the GPU
   uint32_t* d_go = nullptr;    // device copy of the verdict word of a call launched ahead
+  int32_t* h_pf = nullptr;     // prefill through the cache: pinned counts [E], then group tile lists
+  int32_t* d_pf_tiles = nullptr;  // the group tile lists on the device
+  size_t pf_ints = 0;          // capacity of both lists, in ints
+  uint64_t* h_pf_addr = nullptr;  // pinned snapshots of the expert table, one per group of a chunk
+  size_t pf_groups = 0;           // their count
+  hipEvent_t ev_pf = nullptr;  // a prefill group's GEMMs are done (its slots may be refilled)
   std::vector<char> fail_expert;
   moe_cache_stats stats{};
   uint64_t device_bytes = 0;
@@ -275,6 +281,10 @@ void free_layer(moe_layer* L) {
   if (L->h_store) (void)hipHostFree(L->h_store);
   if (L->h_addr) (void)hipHostFree(L->h_addr);
   if (L->h_ids) (void)hipHostFree(L->h_ids);
+  if (L->h_pf) (void)hipHostFree(L->h_pf);
+  if (L->h_pf_addr) (void)hipHostFree(L->h_pf_addr);
+  (void)hipFree(L->d_pf_tiles);
+  if (L->ev_pf) (void)hipEventDestroy(L->ev_pf);
   (void)hipFree(L->d_go);
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
   if (L->ev_fill_start) (void)hipEventDestroy(L->ev_fill_start);
@@ -631,7 +641,7 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
   if (path == MOE_PATH_AUTO) {
     if (fused_ok)
       path = MOE_PATH_FUSED;
-    else if (L->act == MOE_ACT_BF16 && T >= 16 && L->d_prefill && L->d <= 4096 && resident && !a.rms)
+    else if (L->act == MOE_ACT_BF16 && T >= 16 && L->d_prefill && L->d <= 4096 && (resident || L->lfu) && !a.rms)
       path = MOE_PATH_PREFILL;
     else
       path = MOE_PATH_DECODE;
@@ -649,7 +659,8 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
   if (path == MOE_PATH_PREFILL) {
     if (L->act != MOE_ACT_BF16 || !L->d_prefill)
       return fail(MOE_ERR_INVALID, "the prefill path needs bf16 activations and max_tokens > 1");
-    if (L->residency == MOE_STREAMED) return fail(MOE_ERR_INVALID, "the prefill path needs resident experts");
+    if (L->residency == MOE_STREAMED && !L->lfu)
+      return fail(MOE_ERR_INVALID, "prefill of a streamed layer needs its own LFU cache (moe_cache_attach)");
     if (L->d > 4096) return fail(MOE_ERR_INVALID, "the prefill path supports d_model <= 4096");
     if (a.rms) return fail(MOE_ERR_INVALID, "the prefill path takes the layer input directly (no rmsnorm)");
     moe_status st = launch_prefill_path(L, a, o, s);
@@ -705,13 +716,150 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
 
 }  // namespace
 
+// Prefill through the streamed layer's LFU cache (Rockchip-NPU plan §2.5:
+// the prefill chunk fetches each chosen expert once for all its rows).  The
+// chunk's distinct experts go through the cache in groups of at most n_slots:
+// first those already cached (ascending id: hits, used before anything can
+// evict them), then the rest least chosen first (ties: lower id), so that
+// the cache ends up holding the chunk's most chosen experts.  Each group is
+// one cache step (its ids ascending).  A group's fills wait for the previous
+// group's GEMMs, whose slots they may reuse.
+struct StreamPrefill final : PrefillStreamer {
+  moe_layer* L;
+  moe_status err = MOE_OK;
+  std::vector<std::vector<int32_t>> groups;
+  std::vector<size_t> list_at;  // each group's tile list, in ints from d_pf_tiles
+  explicit StreamPrefill(moe_layer* l) : L(l) {}
+
+  hipError_t plan(const PrefillArgs& p, int C, hipStream_t s, int* n_groups) override {
+    hipError_t e = hipMemcpyAsync(L->h_pf, p.counts, (size_t)L->E * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    if (L->ahead_pending) {  // fetched-ahead copies land before anything reads their slots
+      if ((e = hipStreamWaitEvent(s, L->ev_ahead, 0)) != hipSuccess) return e;
+      L->ahead_pending = false;
+    }
+    std::vector<int32_t> order, rest;
+    for (int x = 0; x < L->E; ++x)
+      if (L->h_pf[x] > 0) (L->lfu->find(x) >= 0 ? order : rest).push_back(x);
+    std::stable_sort(rest.begin(), rest.end(), [&](int32_t u, int32_t v) { return L->h_pf[u] < L->h_pf[v]; });
+    order.insert(order.end(), rest.begin(), rest.end());
+    const int n_slots = L->n_slots;
+    groups.clear();
+    for (size_t i = 0; i < order.size(); i += n_slots) {
+      std::vector<int32_t> g(order.begin() + i, order.begin() + std::min(order.size(), i + n_slots));
+      std::sort(g.begin(), g.end());
+      groups.push_back(g);
+    }
+    if (groups.empty()) groups.emplace_back();  // no routed expert: the shared expert still runs
+    // tile lists: [n, (expert, tile) x n]; the shared expert's tiles go with group 0
+    int32_t* h = L->h_pf + L->E;
+    size_t at = 0;
+    list_at.clear();
+    for (size_t g = 0; g < groups.size(); ++g) {
+      list_at.push_back(at);
+      const size_t head = at++;
+      int n = 0;
+      for (int32_t x : groups[g])
+        for (int tt = 0; tt * 16 < L->h_pf[x]; ++tt, ++n) {
+          h[at++] = x;
+          h[at++] = tt;
+        }
+      if (g == 0 && L->fs > 0)
+        for (int tt = 0; tt * 16 < C; ++tt, ++n) {
+          h[at++] = L->E;
+          h[at++] = tt;
+        }
+      h[head] = n;
+    }
+    if (at > L->pf_ints) return hipErrorInvalidValue;  // cannot happen: sized for the worst case
+    if ((e = hipMemcpyAsync(L->d_pf_tiles, h, at * 4, hipMemcpyHostToDevice, s)) != hipSuccess) return e;
+    *n_groups = (int)groups.size();
+    return hipSuccess;
+  }
+
+  hipError_t group(int gi, hipStream_t s, int32_t** tiles) override {
+    const std::vector<int32_t>& chosen = groups[gi];
+    const int m = (int)chosen.size();
+    for (int32_t x : chosen)
+      if (!(L->lfu->find(x) >= 0) && L->fail_expert[x]) {
+        err = fail(MOE_ERR_IO, "expert %d could not be read into a cache slot", x);
+        return hipErrorUnknown;
+      }
+    std::vector<int32_t> slot(m), miss(m), ev_expert(m, -1);
+    if (m > 0) L->lfu->step(chosen.data(), m, slot.data(), miss.data(), ev_expert.data());
+    const size_t stride = L->rl.stride;
+    bool any = false;
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < m; ++i) {
+      if (!miss[i]) continue;
+      if (!any && gi > 0 && (e = hipStreamWaitEvent(L->side, L->ev_pf, 0)) != hipSuccess) return e;
+      any = true;
+      uint8_t* dst = L->d_slots + (size_t)slot[i] * stride;
+      e = hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice, L->side);
+      if (e != hipSuccess) return e;
+      if (ev_expert[i] >= 0) L->h_addr[ev_expert[i]] = 0;
+      L->h_addr[chosen[i]] = reinterpret_cast<uint64_t>(dst);
+      L->addr_dirty = true;
+      L->stats.h2d_bytes += stride;
+    }
+    L->stats.accesses = L->lfu->accesses;
+    L->stats.hits = L->lfu->hits;
+    L->stats.misses = L->lfu->misses;
+    L->stats.evictions = L->lfu->evictions;
+    L->stats.prefetch_used = L->lfu->prefetch_used;
+    if (L->hist.empty()) L->hist.assign(L->E, 0);
+    for (int32_t x : chosen) ++L->hist[x];
+    if (any) {
+      if ((e = hipEventRecord(L->ev_fill, L->side)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(s, L->ev_fill, 0)) != hipSuccess) return e;
+    }
+    if (L->addr_dirty) {
+      // from a snapshot of its own: the host takes the next group's step
+      // (and changes h_addr) before this copy runs
+      if ((size_t)gi >= L->pf_groups) return hipErrorInvalidValue;  // cannot happen: sized for every group
+      uint64_t* snap = L->h_pf_addr + (size_t)gi * L->E;
+      std::memcpy(snap, L->h_addr, (size_t)L->E * 8);
+      e = hipMemcpyAsync(L->d_expert_addr, snap, (size_t)L->E * 8, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return e;
+      L->addr_dirty = false;
+    }
+    *tiles = L->d_pf_tiles + list_at[gi];
+    return hipSuccess;
+  }
+
+  hipError_t done(int, hipStream_t s) override { return hipEventRecord(L->ev_pf, s); }
+};
+
 moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_opts* o, hipStream_t s) {
   PrefillArgs p{};
   p.L = a;
   prefill_carve(p, L->d_prefill, a.T, L->d, L->E, L->K, L->f, L->fs);
   p.sort_offsets_out = o ? o->sort_offsets : nullptr;
   p.sort_perm_out = o ? o->sort_perm : nullptr;
-  HIP_OK(launch_prefill(p, s));
+  if (L->residency != MOE_STREAMED) {
+    HIP_OK(launch_prefill(p, s));
+    return MOE_OK;
+  }
+  if (!L->lfu) return fail(MOE_ERR_INVALID, "prefill of a streamed layer needs its own LFU cache (moe_cache_attach)");
+  if (!L->h_pf) {
+    const int C = std::min(L->max_tokens, 128);
+    L->pf_ints = (size_t)C * L->K * 2 + (size_t)L->E * 3 + (size_t)(C + 15) / 16 * 2 + 64;
+    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_pf), ((size_t)L->E + L->pf_ints) * 4, hipHostMallocDefault) !=
+        hipSuccess)
+      return fail(MOE_ERR_NOMEM, "pinned prefill lists failed");
+    if (dalloc(&L->d_pf_tiles, L->pf_ints * 4) != hipSuccess) return fail(MOE_ERR_NOMEM, "prefill list alloc failed");
+    L->pf_groups = (size_t)(L->E + L->n_slots - 1) / L->n_slots + 1;
+    if (hipHostMalloc(reinterpret_cast<void**>(&L->h_pf_addr), L->pf_groups * L->E * 8, hipHostMallocDefault) !=
+        hipSuccess)
+      return fail(MOE_ERR_NOMEM, "pinned table snapshots failed");
+    HIP_OK(hipEventCreateWithFlags(&L->ev_pf, hipEventDisableTiming));
+  }
+  StreamPrefill sp(L);
+  p.streamer = &sp;
+  const hipError_t e = launch_prefill(p, s);
+  if (sp.err != MOE_OK) return sp.err;
+  HIP_OK(e);
   return MOE_OK;
 }
 

@@ -111,6 +111,21 @@ struct PrefillArgs {
   float* Ys;         // [T][d] fp32 shared-expert outputs
   int32_t* sort_offsets_out;
   int32_t* sort_perm_out;
+  struct PrefillStreamer* streamer;  // host object (streamed experts), never read by the kernels
+};
+
+// Prefill of a layer whose experts live in host memory: after a chunk's
+// routing and grouping are enqueued, the chunk's experts go through the cache
+// in groups; the grouped GEMMs run once per group on that group's tile list.
+struct PrefillStreamer {
+  // the chunk's grouping is enqueued on s (C tokens); returns the group count
+  virtual hipError_t plan(const PrefillArgs& p, int C, hipStream_t s, int* n_groups) = 0;
+  // group g's experts are made resident and the device table updated, all
+  // ordered before what is enqueued next on s; *tiles: its work list (device)
+  virtual hipError_t group(int g, hipStream_t s, int32_t** tiles) = 0;
+  // group g's GEMMs are enqueued on s
+  virtual hipError_t done(int g, hipStream_t s) = 0;
+  virtual ~PrefillStreamer() = default;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);

@@ -258,7 +258,9 @@ __device__ __forceinline__ TileInfo tile_info(const PrefillArgs& p, int tile) {
   ti.rows = ti.shared ? a.T : p.counts[ti.e];
   ti.base = ti.shared ? 0 : p.offsets[ti.e];
   ti.m_valid = min(kTile, ti.rows - ti.tt * kTile);
-  ti.blob = ti.shared ? a.shared_blob : a.expert_base + (size_t)ti.e * a.expert_stride;
+  ti.blob = ti.shared ? a.shared_blob
+                      : (a.expert_base ? a.expert_base + (size_t)ti.e * a.expert_stride  // resident
+                                       : reinterpret_cast<const uint8_t*>(a.expert_addr[ti.e]));  // cache slot
   return ti;
 }
 
@@ -716,28 +718,34 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
     // 2. grouping + tiles
     launch_timed(a.prof, kKSort, sort_kernel, dim3(1), dim3(1024), sort_lds_bytes(C, a.E), s, (const int32_t*)a.ids,
                  C, a.K, a.E, p.counts, p.offsets, p.perm, p.inv, p.tiles, a.fs > 0 ? 1 : 0);
-    // 3. gate/up, 4. down, 5. combine
+    // 3. gate/up, 4. down (per group of cached experts when they are streamed), 5. combine
     const size_t mt = max_tiles(C, a.K, a.E);
-    const int nch_gu = (((a.f > a.fs) ? a.f : a.fs) + kGuRowsPerWG - 1) / kGuRowsPerWG;
-    const size_t lds_gu = prefill_lds_gate_up(a.d);
-    const dim3 g_gu((unsigned)(mt * nch_gu)), blk(kPThreads);
-    switch (stage_words(a.d)) {
-      case 1: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<1>, g_gu, blk, lds_gu, s, p); break;
-      case 2: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<2>, g_gu, blk, lds_gu, s, p); break;
-      case 4: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<4>, g_gu, blk, lds_gu, s, p); break;
-      case 8: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<8>, g_gu, blk, lds_gu, s, p); break;
-      default: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<16>, g_gu, blk, lds_gu, s, p); break;
-    }
-    const int fmax = (a.f > a.fs) ? a.f : a.fs;
-    const int nch_dn = (a.d + kDnRowsPerWG - 1) / kDnRowsPerWG;
-    const size_t lds_dn = (size_t)kTile * (fmax / 8 + 1) * 16 + (size_t)(fmax / 64) * kTile * 4;
-    const dim3 g_dn((unsigned)(mt * nch_dn));
-    switch (stage_words(fmax)) {
-      case 1: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<1>, g_dn, blk, lds_dn, s, p); break;
-      case 2: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<2>, g_dn, blk, lds_dn, s, p); break;
-      case 4: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<4>, g_dn, blk, lds_dn, s, p); break;
-      case 8: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<8>, g_dn, blk, lds_dn, s, p); break;
-      default: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<16>, g_dn, blk, lds_dn, s, p); break;
+    int n_groups = 1;
+    if (p0.streamer && (e = p0.streamer->plan(p, C, s, &n_groups)) != hipSuccess) return e;
+    for (int grp = 0; grp < n_groups; ++grp) {
+      if (p0.streamer && (e = p0.streamer->group(grp, s, &p.tiles)) != hipSuccess) return e;
+      const int nch_gu = (((a.f > a.fs) ? a.f : a.fs) + kGuRowsPerWG - 1) / kGuRowsPerWG;
+      const size_t lds_gu = prefill_lds_gate_up(a.d);
+      const dim3 g_gu((unsigned)(mt * nch_gu)), blk(kPThreads);
+      switch (stage_words(a.d)) {
+        case 1: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<1>, g_gu, blk, lds_gu, s, p); break;
+        case 2: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<2>, g_gu, blk, lds_gu, s, p); break;
+        case 4: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<4>, g_gu, blk, lds_gu, s, p); break;
+        case 8: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<8>, g_gu, blk, lds_gu, s, p); break;
+        default: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<16>, g_gu, blk, lds_gu, s, p); break;
+      }
+      const int fmax = (a.f > a.fs) ? a.f : a.fs;
+      const int nch_dn = (a.d + kDnRowsPerWG - 1) / kDnRowsPerWG;
+      const size_t lds_dn = (size_t)kTile * (fmax / 8 + 1) * 16 + (size_t)(fmax / 64) * kTile * 4;
+      const dim3 g_dn((unsigned)(mt * nch_dn));
+      switch (stage_words(fmax)) {
+        case 1: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<1>, g_dn, blk, lds_dn, s, p); break;
+        case 2: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<2>, g_dn, blk, lds_dn, s, p); break;
+        case 4: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<4>, g_dn, blk, lds_dn, s, p); break;
+        case 8: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<8>, g_dn, blk, lds_dn, s, p); break;
+        default: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<16>, g_dn, blk, lds_dn, s, p); break;
+      }
+      if (p0.streamer && (e = p0.streamer->done(grp, s)) != hipSuccess) return e;
     }
     launch_timed(a.prof, kKPrefillCombine, pf_combine_kernel, dim3((a.d + 255) / 256, C), dim3(256), 0, s, p);
     if (p0.sort_offsets_out)

@@ -148,6 +148,55 @@ def test_streamed_one_and_two_token_calls_interleave():
     st.close()
 
 
+def _prefill_groups(ids, E, slots, cached):
+    """The cache steps of a prefill chunk through the cache: its distinct
+    experts, those in `cached` first (ascending), then the rest least chosen
+    first (ties: lower id), in groups of `slots`, each group's ids ascending."""
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    chosen = [e for e in range(E) if counts[e] > 0]
+    order = [e for e in chosen if e in cached] + sorted((e for e in chosen if e not in cached),
+                                                        key=lambda e: (counts[e], e))
+    return [sorted(order[i:i + slots]) for i in range(0, len(order), slots)]
+
+
+def test_streamed_prefill_goes_through_the_cache():
+    """Prefill of a streamed layer runs the chunk's experts through the LFU
+    cache group by group: outputs bit-identical to the resident prefill, cache
+    state equal to the replay of the groups, and one-token calls afterwards
+    still match."""
+    w = Workload(89, "prefill-cache", d=512, E=64, K=8, f=128, fs=128, act="bf16", zipf=1.1, T=96,
+                 layers=1, steps=1, slots=16)
+    arrays = make_layer(w)
+    res = GpuLayer(w, arrays, 256)
+    st = GpuLayer(w, arrays, 256, residency=M.MOE_STREAMED)
+    M.moe_cache_attach(st.handle, w.slots)
+    _, stride = M.moe_layer_bytes(st.handle)
+    x = make_tokens(w, 96 + 130 + 2, stream=41)
+    replay = LfuReplay(w.slots)
+    for lo, hi in ((0, 96), (96, 226)):  # one chunk, then 130 tokens (chunks of 128 and 2)
+        y_r, ids_r, w_r = res.forward(x[lo:hi], path=M.MOE_PATH_PREFILL)
+        y_s, ids_s, w_s = st.forward(x[lo:hi], path=M.MOE_PATH_PREFILL)
+        assert np.array_equal(y_r, y_s), f"prefill of tokens {lo}..{hi} differs from resident"
+        assert np.array_equal(ids_r, ids_s) and np.array_equal(w_r, w_s)
+        for c0 in range(0, hi - lo, 128):
+            for g in _prefill_groups(ids_s[c0:c0 + 128], w.E, w.slots, set(e for e in replay.expert if e >= 0)):
+                replay.step(g)
+    stats = M.moe_cache_stats_get(st.handle)
+    assert (stats["accesses"], stats["hits"], stats["misses"], stats["evictions"]) == \
+        (replay.accesses, replay.hits, replay.misses, replay.evictions)
+    assert stats["h2d_bytes"] == replay.misses * stride
+    experts, counts = M.moe_cache_contents(st.handle, w.slots)
+    assert list(experts) == replay.expert and list(counts) == replay.count
+    assert replay.hits > 0  # the second call's chunks start with what the cache holds
+    for t in (226, 227):  # decode after prefill, on the warmed cache
+        y_r, _, _ = res.forward(x[t:t + 1], path=M.MOE_PATH_DECODE)
+        y_s, ids_s, _ = st.forward(x[t:t + 1], path=M.MOE_PATH_DECODE)
+        assert np.array_equal(y_r, y_s)
+    assert M.moe_layer_check_errors(st.handle) == 0
+    res.close()
+    st.close()
+
+
 def test_streamed_stack_equals_resident_stack_on_the_same_path():
     """A stack of streamed layers (16-slot LFU caches, fills on a side stream)
     ends in exactly the state of the same stack with every expert resident,
