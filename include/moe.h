@@ -53,9 +53,15 @@ enum { MOE_RESIDENT = 0, MOE_STREAMED = 1 };        /* where routed experts live
  *           (its workgroups hand results to each other through device-scope
  *           flags and counters), for d_model <= 4096 when its LDS fits;
  *           MOE_ERR_INVALID otherwise;
- *   PREFILL grouped bf16 matrix-core GEMMs for token chunks on resident experts.
- * AUTO takes FUSED where it applies, PREFILL for T >= 16 bf16 resident layers
- * with d_model <= 4096 and no rmsnorm, DECODE otherwise. */
+ *   PREFILL grouped bf16 matrix-core GEMMs for 128-token chunks, on resident
+ *           experts or on streamed experts through the layer's own LFU cache
+ *           (moe_cache_attach; not a shared pool): each chunk's experts are
+ *           taken in groups of at most the slot count (cached ones first,
+ *           then least chosen first), the GEMMs run per group, and the call
+ *           blocks the thread once per chunk to read its expert counts.
+ * AUTO takes FUSED where it applies, PREFILL for T >= 16 bf16 layers (resident,
+ * or streamed with an LFU cache) with d_model <= 4096 and no rmsnorm, DECODE
+ * otherwise. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, MOE_PATH_FUSED = 3 };
 
 typedef struct moe_layer moe_layer; /* opaque, owned by the library */

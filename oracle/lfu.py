@@ -20,8 +20,30 @@ the same prefetch nor one the last step used (BigMoeOnEdge protects the
 working set in use; without such a slot the guess is dropped); a new entry
 starts at count 0 with the last step's tick.
 A step's hit on such an entry counts as a used prefetch.
+
+Prefill through the cache (plan §2.5: one fetched expert serves every row of
+the chunk that chose it): a chunk's distinct experts are taken as cache steps
+of at most n_slots experts each: first those already cached (ascending id),
+then the others least chosen first (ties: lower id); each step's ids
+ascending (reading: the cached ones are used before anything can evict them,
+and the cache ends with the chunk's most chosen experts).
 """
 from __future__ import annotations
+
+
+def prefill_steps(chunk_ids, n_experts: int, n_slots: int, cached) -> list:
+    """The cache steps of one prefill chunk: chunk_ids is the chunk's [T][K]
+    routing (distinct ids per token), cached the experts in the cache before
+    the chunk."""
+    counts = [0] * n_experts
+    for row in chunk_ids:
+        for e in row:
+            counts[int(e)] += 1
+    chosen = [e for e in range(n_experts) if counts[e] > 0]
+    cached = set(cached)
+    order = [e for e in chosen if e in cached]
+    order += sorted((e for e in chosen if e not in cached), key=lambda e: (counts[e], e))
+    return [sorted(order[i:i + n_slots]) for i in range(0, len(order), n_slots)]
 
 
 class LfuReplay:

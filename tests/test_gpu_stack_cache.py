@@ -6,7 +6,7 @@ import pytest
 import routed_expert_ffn_int8_amd as M
 from gen.workloads import WORKLOADS, Workload, make_layer, make_tokens, make_reuse_coins
 from oracle import oracle as O
-from oracle.lfu import LfuReplay, LruPoolReplay
+from oracle.lfu import LfuReplay, LruPoolReplay, prefill_steps
 from tests.helpers import GpuLayer, to_device, to_host, torch_mod
 
 pytestmark = pytest.mark.gpu
@@ -148,17 +148,6 @@ def test_streamed_one_and_two_token_calls_interleave():
     st.close()
 
 
-def _prefill_groups(ids, E, slots, cached):
-    """The cache steps of a prefill chunk through the cache: its distinct
-    experts, those in `cached` first (ascending), then the rest least chosen
-    first (ties: lower id), in groups of `slots`, each group's ids ascending."""
-    counts = np.bincount(ids.reshape(-1), minlength=E)
-    chosen = [e for e in range(E) if counts[e] > 0]
-    order = [e for e in chosen if e in cached] + sorted((e for e in chosen if e not in cached),
-                                                        key=lambda e: (counts[e], e))
-    return [sorted(order[i:i + slots]) for i in range(0, len(order), slots)]
-
-
 def test_streamed_prefill_goes_through_the_cache():
     """Prefill of a streamed layer runs the chunk's experts through the LFU
     cache group by group: outputs bit-identical to the resident prefill, cache
@@ -179,7 +168,7 @@ def test_streamed_prefill_goes_through_the_cache():
         assert np.array_equal(y_r, y_s), f"prefill of tokens {lo}..{hi} differs from resident"
         assert np.array_equal(ids_r, ids_s) and np.array_equal(w_r, w_s)
         for c0 in range(0, hi - lo, 128):
-            for g in _prefill_groups(ids_s[c0:c0 + 128], w.E, w.slots, set(e for e in replay.expert if e >= 0)):
+            for g in prefill_steps(ids_s[c0:c0 + 128], w.E, w.slots, [e for e in replay.expert if e >= 0]):
                 replay.step(g)
     stats = M.moe_cache_stats_get(st.handle)
     assert (stats["accesses"], stats["hits"], stats["misses"], stats["evictions"]) == \

@@ -384,3 +384,24 @@ def test_lru_pool_single_expert_calls_follow_stack_distance(n_slots):
         _, miss = pool.step(layer, [e])
         assert miss[0] == (dist >= n_slots), step
         history.append(key)
+
+
+def test_prefill_steps_hand_worked():
+    """Prefill through the cache, worked by hand: 3 tokens, top-2, 6 experts,
+    2 slots, expert 5 cached.  Counts: e0 1, e1 2, e3 1, e4 1, e5 1.  Cached
+    first: [5]; then least chosen first, ties to the lower id: 0, 3, 4, then
+    1 (count 2).  Steps of 2, ids ascending: [0, 5], [3, 4], [1]."""
+    from oracle.lfu import prefill_steps, LfuReplay
+    ids = [[1, 5], [0, 1], [3, 4]]
+    steps = prefill_steps(ids, 6, 2, cached=[5])
+    assert steps == [[0, 5], [3, 4], [1]]
+    r = LfuReplay(2)
+    r.step([5])  # the state before the chunk
+    for g in steps:
+        r.step(g)
+    # [0, 5]: 5 hits (count 2), 0 fills the empty slot; [3, 4]: both miss and
+    # evict 0 and 5 (counts 1 and 2 are not protected: neither is chosen);
+    # (4 in slot 0, 3 in slot 1); [1]: 3 and 4 tie on count and tick, so the
+    # lower slot goes: the chunk's most chosen expert, 1, stays in the cache
+    assert r.hits == 1 and r.misses == 5
+    assert r.expert == [1, 3]
