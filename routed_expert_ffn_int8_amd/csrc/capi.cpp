@@ -128,6 +128,8 @@ struct moe_layer {
   int pool_id = -1;                // this layer's key in it
   hipStream_t side = nullptr;
   bool own_side = false;
+  hipStream_t side2 = nullptr;   // a second fill stream (own LFU cache): a call's fills alternate
+  hipEvent_t ev_fill2 = nullptr;  // between the two, so that two copy engines share them
   hipEvent_t ev_fill = nullptr, ev_fill_start = nullptr;
   bool fill_pending = false;
   hipEvent_t ev_ahead = nullptr;  // after the last prefetch's copies
@@ -290,6 +292,8 @@ void free_layer(moe_layer* L) {
   if (L->ev_fill_start) (void)hipEventDestroy(L->ev_fill_start);
   if (L->ev_ahead) (void)hipEventDestroy(L->ev_ahead);
   if (L->own_side && L->side) (void)hipStreamDestroy(L->side);
+  if (L->side2) (void)hipStreamDestroy(L->side2);
+  if (L->ev_fill2) (void)hipEventDestroy(L->ev_fill2);
   delete L;
 }
 
@@ -544,14 +548,23 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
   const size_t stride = L->rl.stride;
   uint8_t* base = P ? P->d_slots : L->d_slots;
   hipStream_t side = P ? P->side : L->side;
-  bool any = false;
+  hipStream_t side2 = P ? nullptr : L->side2;
+  bool any = false, any2 = false;
+  int nfill = 0;
   uint64_t h2d = 0;
   for (int i = 0; i < m; ++i) {
     if (!miss[i]) continue;
     if (!any) HIP_OK(hipEventRecord(L->ev_fill_start, side));
     any = true;
     uint8_t* dst = base + (size_t)slot[i] * stride;
-    HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice, side));
+    const bool second = side2 && (nfill++ & 1);
+    if (second && !any2) {  // starts no earlier than the first stream's fills
+      HIP_OK(hipEventRecord(L->ev_fill2, side));
+      HIP_OK(hipStreamWaitEvent(side2, L->ev_fill2, 0));
+    }
+    any2 |= second;
+    HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice,
+                          second ? side2 : side));
     if (ev_expert[i] >= 0) {  // the slot's previous entry (of this layer, or of another for a pool)
       moe_layer* owner = P ? (ev_layer[i] >= 0 ? P->members[ev_layer[i]] : nullptr) : L;
       if (owner) {  // that layer re-uploads its table on its next call
@@ -589,6 +602,10 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
   if (L->hist.empty()) L->hist.assign(L->E, 0);
   for (int32_t e : chosen) ++L->hist[e];
   if (any) {
+    if (any2) {  // the second stream's fills, then the first's event covers both
+      HIP_OK(hipEventRecord(L->ev_fill2, side2));
+      HIP_OK(hipStreamWaitEvent(side, L->ev_fill2, 0));
+    }
     HIP_OK(hipEventRecord(L->ev_fill, side));
     HIP_OK(hipStreamWaitEvent(stream, L->ev_fill, 0));
     L->fill_pending = true;
@@ -789,14 +806,22 @@ struct StreamPrefill final : PrefillStreamer {
     std::vector<int32_t> slot(m), miss(m), ev_expert(m, -1);
     if (m > 0) L->lfu->step(chosen.data(), m, slot.data(), miss.data(), ev_expert.data());
     const size_t stride = L->rl.stride;
-    bool any = false;
+    bool any = false, any2 = false;
+    int nfill = 0;
     hipError_t e = hipSuccess;
     for (int i = 0; i < m; ++i) {
       if (!miss[i]) continue;
       if (!any && gi > 0 && (e = hipStreamWaitEvent(L->side, L->ev_pf, 0)) != hipSuccess) return e;
       any = true;
+      const bool second = nfill++ & 1;
+      if (second && !any2) {  // the second stream starts behind the first one's wait
+        if ((e = hipEventRecord(L->ev_fill2, L->side)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(L->side2, L->ev_fill2, 0)) != hipSuccess) return e;
+      }
+      any2 |= second;
       uint8_t* dst = L->d_slots + (size_t)slot[i] * stride;
-      e = hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice, L->side);
+      e = hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice,
+                         second ? L->side2 : L->side);
       if (e != hipSuccess) return e;
       if (ev_expert[i] >= 0) L->h_addr[ev_expert[i]] = 0;
       L->h_addr[chosen[i]] = reinterpret_cast<uint64_t>(dst);
@@ -811,6 +836,10 @@ struct StreamPrefill final : PrefillStreamer {
     if (L->hist.empty()) L->hist.assign(L->E, 0);
     for (int32_t x : chosen) ++L->hist[x];
     if (any) {
+      if (any2) {
+        if ((e = hipEventRecord(L->ev_fill2, L->side2)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(L->side, L->ev_fill2, 0)) != hipSuccess) return e;
+      }
       if ((e = hipEventRecord(L->ev_fill, L->side)) != hipSuccess) return e;
       if ((e = hipStreamWaitEvent(s, L->ev_fill, 0)) != hipSuccess) return e;
     }
@@ -1036,6 +1065,8 @@ moe_status moe_cache_attach(moe_layer* L, int32_t n_slots, void* side_stream) {
     HIP_OK(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
     L->own_side = true;
   }
+  if (!L->side2) HIP_OK(hipStreamCreateWithFlags(&L->side2, hipStreamNonBlocking));
+  if (!L->ev_fill2) HIP_OK(hipEventCreateWithFlags(&L->ev_fill2, hipEventDisableTiming));
   L->n_slots = n_slots;
   L->lfu.reset(new LfuPolicy(n_slots));
   L->device_bytes += bytes;
@@ -1121,6 +1152,8 @@ moe_status moe_cache_detach(moe_layer* L) {
     if (L->own_side && L->side) (void)hipStreamDestroy(L->side);
     L->side = nullptr;
     L->own_side = false;
+    if (L->side2) (void)hipStreamDestroy(L->side2);
+    L->side2 = nullptr;
   }
   L->fill_pending = false;
   L->ahead_pending = false;
