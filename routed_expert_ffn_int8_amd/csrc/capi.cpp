@@ -770,6 +770,11 @@ struct StreamPrefill final : PrefillStreamer {
     }
     if (groups.empty()) groups.emplace_back();  // no routed expert: the shared expert still runs
     // tile lists: [n, (expert, tile) x n]; the shared expert's tiles go with group 0
+    const int shared_tiles = L->fs > 0 ? (C + 15) / 16 : 0;
+    size_t need = groups.size() + 2 * (size_t)shared_tiles;
+    for (const auto& g : groups)
+      for (int32_t x : g) need += 2 * (size_t)((L->h_pf[x] + 15) / 16);
+    if (need > L->pf_ints) return hipErrorInvalidValue;  // cannot happen: sized for the worst case
     int32_t* h = L->h_pf + L->E;
     size_t at = 0;
     list_at.clear();
@@ -782,14 +787,13 @@ struct StreamPrefill final : PrefillStreamer {
           h[at++] = x;
           h[at++] = tt;
         }
-      if (g == 0 && L->fs > 0)
-        for (int tt = 0; tt * 16 < C; ++tt, ++n) {
+      if (g == 0)
+        for (int tt = 0; tt < shared_tiles; ++tt, ++n) {
           h[at++] = L->E;
           h[at++] = tt;
         }
       h[head] = n;
     }
-    if (at > L->pf_ints) return hipErrorInvalidValue;  // cannot happen: sized for the worst case
     if ((e = hipMemcpyAsync(L->d_pf_tiles, h, at * 4, hipMemcpyHostToDevice, s)) != hipSuccess) return e;
     *n_groups = (int)groups.size();
     return hipSuccess;
