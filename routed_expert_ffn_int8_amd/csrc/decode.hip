@@ -727,7 +727,9 @@ constexpr int kSyncStride = 4160 / 4;  // words between counter words
 constexpr int kParts = 8;  // a stage counter is split in parts: producer i adds to part i % kParts
 constexpr int kReps = 8;   // each part is kept in replicas: a consumer polls replica (workgroup % kReps)
 constexpr int kLogitReplicas = 64;
-enum : int { kCntRouter = 0, kCntShared = 1, kCntRouted = 2, kCntDone = 3, kNumCnt = 4 };
+// Counter 0 is free: the routing needs no counter, its logits carry the full
+// launch tag and readers re-read stale entries.
+enum : int { kCntShared = 1, kCntRouted = 2, kCntDone = 3, kNumCnt = 4 };
 constexpr int kSyncSlots = kNumCnt * kParts * kReps;
 
 // Logit table entries: tag << 32 | fp32 bits.  Entries between replicas (the
@@ -814,7 +816,9 @@ __device__ __forceinline__ void stage_logits_dev(const LayerArgs& a, const uint6
 // The launch tag comes from a 64-bit count of down workgroups that have
 // passed their last wait (8 parts, replica 0; part i % 8 for down workgroup
 // i).  A down workgroup passes it only after every other workgroup of the
-// launch has arrived somewhere, i.e. started and read the count, and the count
+// launch has started and read the count (shared and routed workgroups arrive
+// on the counters it waits for; every routed workgroup has read every router
+// workgroup's tagged logits), and the count
 // cannot reach the next multiple of nd before every down workgroup, the
 // reader included, has passed.  So every workgroup of launch n reads a total
 // in [(n-1) nd, n nd) and takes tag = total / nd + 1 = n, with no reset
@@ -925,7 +929,7 @@ __device__ __forceinline__ void stage_a_coherent(const LayerArgs& a, char* lds_a
 // part; SS shared and SR routed weight slots.  The shared slots are loaded at
 // once, the routed ones as soon as the routing is known.
 template <int SS, int SR, int NE>
-__device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_router, uint32_t members_shared,
+__device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_shared,
                            uint32_t members_routed, const uint64_t* lrep, char* smem, float* s_logits,
                            uint32_t* scratch, uint64_t* s_sel, float* s_w) {
   const int tid = threadIdx.x, r = tid & 7, jj = tid >> 3;
@@ -948,8 +952,7 @@ __device__ void down_fused(const LayerArgs& a, int rb, int nd, uint32_t members_
   bulk_delay();
 #pragma unroll
   for (int s = 0; s < SS; ++s) load_slot(s, a.shared_blob, Gs, min(jj + 32 * s, Gs - 1), a.so.dq, a.so.dsb);
-  // routing
-  wait_count<1>(a, area, kCntRouter, tag, (int)members_router);
+  // routing: the tagged logits are read as they arrive (no counter round trip)
   stage_logits_dev<NE>(a, lrep, tag, s_logits);
   if (threadIdx.x < 64) {
     int id;
@@ -1047,7 +1050,6 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
       st_dev16(rs, (uint32_t)off, v4u{__float_as_uint(s_w[0]), tag, __float_as_uint(s_w[1]), tag});
       st_dev16(rs, (uint32_t)off + 16, v4u{__float_as_uint(s_w[2]), tag, __float_as_uint(s_w[3]), tag});
     }
-    arrive(area, kCntRouter, b);
   } else if (b < NR + NS) {
     const uint32_t tag = launch_tag(area, ND);
     XRegs xr;
@@ -1062,8 +1064,7 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
     XRegs xr;
     x_issue<1>(a, 0, xr);
     __builtin_amdgcn_s_setprio(2);
-    wait_count<1>(a, area, kCntRouter, tag, NR);
-    stage_logits_dev<NE>(a, my_rep, tag, s_logits);
+    stage_logits_dev<NE>(a, my_rep, tag, s_logits);  // re-reads entries until they carry this launch's tag
     if (threadIdx.x < 64) {  // one wavefront finds the expert
       const int id = topk_kth<NE>(a, 0, s_logits, k);
       if (threadIdx.x == 0) scratch[0] = (uint32_t)id;
@@ -1075,7 +1076,7 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
                                                a.fs + k * a.f, S, xr, tag);
     arrive(area, kCntRouted, g);
   } else {
-    down_fused<SS, SR, NE>(a, b - NR - NS - NG, ND, (uint32_t)NR, (uint32_t)NS, (uint32_t)NG, my_rep, smem,
+    down_fused<SS, SR, NE>(a, b - NR - NS - NG, ND, (uint32_t)NS, (uint32_t)NG, my_rep, smem,
                            s_logits, scratch, s_sel, s_w);
   }
 }
