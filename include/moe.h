@@ -25,6 +25,10 @@
  *    without waiting for the GPU unless stated otherwise.
  *  - One host thread may use a given layer/stack object at a time.  Distinct
  *    objects may be used concurrently on distinct streams.
+ *  - Calls on one object must run in order on the GPU (one stream, or streams
+ *    ordered with events): every call reuses the object's device workspace
+ *    (routing, activations, the fused kernel's counters, the verdict word of
+ *    a streamed call).
  */
 #ifndef MOE_H
 #define MOE_H
