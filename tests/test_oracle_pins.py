@@ -298,6 +298,34 @@ def test_rmsnorm_closed_form_and_numpy():
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0**-8)   # within half a bf16 ulp
 
 
+def test_residual_rounds_once_and_keeps_h():
+    """h <- RNE_bf16(h + y) with y in fp64: one rounding of the exact sum.
+    y = 2^-8 + 2^-30 on h = 1 lies just above the tie between 1 and 1 + 2^-7,
+    so it must round up; rounding y to bf16 first would leave the exact tie
+    (2^-30 is far below a bf16 ulp of 2^-8) and give the even 1.0.  A dropped
+    h, or a sign error on either term, fails every case."""
+    one = np.array([0x3F80], np.uint16)
+    assert O.residual_bf16(one, np.array([2.0**-8 + 2.0**-30]))[0] == 0x3F81
+    assert O.residual_bf16(one, np.array([2.0**-8]))[0] == 0x3F80          # exact tie -> even
+    assert O.residual_bf16(one, np.array([3 * 2.0**-8]))[0] == 0x3F82      # tie -> even (up)
+    assert O.residual_bf16(one, np.array([-1.0]))[0] == 0x0000             # y = -h gives +0
+    assert O.residual_bf16(one, np.array([0.0]))[0] == 0x3F80              # y = 0 keeps h
+    assert O.residual_bf16(np.array([0x4040], np.uint16), np.array([-0.5]))[0] == 0x4020  # 3 - 0.5 = 2.5
+    # random cases whose exact sum is representable in fp32: |h| in [2^-3, 2^3)
+    # (bf16: lowest bit >= 2^-10) and y a multiple of 2^-16 below 8 in magnitude,
+    # so h + y needs at most 20 significant bits; then RNE_bf16 of the fp32 sum
+    # (the fp32 -> bf16 route, pinned above) is the only correct answer
+    rng = np.random.default_rng(17)
+    n = 4096
+    hv = rng.uniform(0.125, 8.0, n) * rng.choice([-1.0, 1.0], n)
+    h = f32_to_bf16_bits(hv.astype(np.float32))
+    y = rng.integers(-(2**19) + 1, 2**19, n).astype(np.float64) * 2.0**-16
+    hf = (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    s32 = (hf + y).astype(np.float32)
+    assert np.array_equal(s32.astype(np.float64), hf + y)  # the sums are exact in fp32
+    assert np.array_equal(O.residual_bf16(h, y), f32_to_bf16_bits(s32))
+
+
 def test_stack_step_composes_layers():
     w, L0 = tiny(d=128, E=4, K=2, f=64, fs=64, zipf=1.0, seed=1)
     _, L1 = tiny(d=128, E=4, K=2, f=64, fs=64, zipf=1.0, seed=2)
