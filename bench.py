@@ -8,7 +8,8 @@ the whole layer (router GEMV, softmax top-K, shared + routed gate/up SiLU,
 down + weighted combine).  The timed steps are replayed from HIP graphs; the
 per-kernel durations come from extended-launch HIP events in a second pass
 over the same tokens.  Prints one JSON line, which also carries a short
-prefill summary (128-token chunk of the d_model 2048 / 256-expert layer).
+prefill summary (128-token chunk of the d_model 2048 / 256-expert layer) and
+a short leg of the 30-layer decode stack (32 steps of its recurrence).
 
 Other workloads (one JSON line each):
   --workload prefill : 128-token chunks, d_model 2048, 256 experts, top-8,
@@ -67,20 +68,46 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(w, arrays, n_tokens: int, tokens_per_call: int = 1):
-    """The fp64 oracle, timed on this host's cores over a bounded sample."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, arrays, n_tokens: int, tokens_per_call: int = 1, n_single: int = 0):
+    """The fp64 oracle, timed on this host's cores over a bounded sample: once
+    with its OpenMP loops on every core, and once on a single core."""
     from gen.workloads import make_tokens
     from oracle import oracle as O
     OL = O.OracleLayer.from_workload(w, arrays)
     x = make_tokens(w, n_tokens, stream=4242)
     OL.forward(x[:1])  # warm (page in, thread pool)
-    t0 = time.perf_counter()
-    for t in range(0, n_tokens, tokens_per_call):
-        OL.forward(x[t:t + tokens_per_call])
-    dt = time.perf_counter() - t0
-    return {"value": round(n_tokens / dt, 3), "unit": "tok/s", "cores": O.threads(), "kind": "oracle",
-            "sample": f"{n_tokens} tokens of the same layer in calls of {tokens_per_call} "
-                      f"(fp64 plain loops, OpenMP over output rows), {dt:.1f} s"}
+
+    def timed(n):
+        t0 = time.perf_counter()
+        for t in range(0, n, tokens_per_call):
+            OL.forward(x[t:t + tokens_per_call])
+        return time.perf_counter() - t0
+
+    cores = O.threads()
+    dt = timed(n_tokens)
+    res = {"value": round(n_tokens / dt, 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
+           "sample": f"{n_tokens} tokens of the same layer in calls of {tokens_per_call} "
+                     f"(fp64 plain loops, OpenMP over output rows), {dt:.1f} s",
+           "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+    if n_single:
+        O.set_threads(1)
+        try:
+            dt1 = timed(n_single)
+        finally:
+            O.set_threads(cores)
+        res["single_thread"] = {"value": round(n_single / dt1, 4), "unit": "tok/s", "cores": 1,
+                                "sample": f"{n_single} tokens, {dt1:.1f} s"}
+    return res
 
 
 def kernel_table(prof: dict, alg: dict, flops: dict | None = None) -> dict:
@@ -217,6 +244,8 @@ def run_decode(args, M, torch, np):
                 "kernel_us_per_token": round(tot_us, 3), "hbm_gbps": round(cold_bytes / (tot_us * 1e3), 1),
                 "kernels": pc}
     bytes_token = w.K * (2 * gu + dn) + 2 * sgu + sdn + router_bytes(w)
+    # sticky kernel error flags over every pass above (0: every output valid)
+    flags = M.moe_layer_check_errors(layer)
     result = {
         "metric": "MoE FFN tok/s (decode b=1, one layer, int4 g64 experts, int8 router)",
         "value": round(tok_s, 1),
@@ -245,10 +274,11 @@ def run_decode(args, M, torch, np):
         "kernels": kernels,
         "three_kernel_path": {"tok_s": round(args.steps / dt3, 1), "kernels": kernel_table(prof3, alg)},
         "cold": cold,
+        "error_flags": flags,
     }
     M.moe_layer_destroy(layer)
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_tokens, n_single=args.cpu_single_tokens)
     return result
 
 
@@ -356,7 +386,7 @@ def run_prefill(args, M, torch, np, chunks=None, summary=False):
 
 
 # --------------------------------------------------------------------- stack
-def run_stack(args, M, torch, np):
+def run_stack(args, M, torch, np, steps=None):
     from gen.workloads import WORKLOADS, make_layer, make_tokens, make_noise, matrix_bytes, router_bytes
     w = WORKLOADS[2]
     layers = []
@@ -367,7 +397,7 @@ def run_stack(args, M, torch, np):
         del keep, arrays
         print(f"[bench] stack layer {l + 1}/{w.layers} created", file=sys.stderr, flush=True)
     stack = M.moe_stack_create(layers, 1e-6)
-    steps = w.steps
+    steps = steps or w.steps
     noise = torch.from_numpy(make_noise(w, steps)).cuda()
     h0 = torch.from_numpy(make_tokens(w, 1, stream=5).view(np.int16)).view(torch.bfloat16).cuda()
     h = h0.clone()
@@ -384,6 +414,24 @@ def run_stack(args, M, torch, np):
     h.copy_(h0)
     dt = graph_time(torch, [lambda s, t=t: step(t, s) for t in range(steps)], 32)
     finite = bool(torch.isfinite(h.float()).all())
+    # per-layer kernel durations (HIP events on each launch) over the same
+    # steps, launched directly: their share of the graph-timed step is what
+    # the launch gaps and the per-step noise update leave
+    for L in layers:
+        M.moe_layer_profile(L, True)
+    h.copy_(h0)
+    for t in range(steps):
+        step(t, stream)
+    torch.cuda.synchronize()
+    kern_ms, kern_n = 0.0, 0
+    for L in layers:
+        for _, (n, ms) in M.moe_layer_profile_read(L).items():
+            kern_ms += ms
+            kern_n += n
+        M.moe_layer_profile(L, False)
+    flags = 0
+    for L in layers:
+        flags |= M.moe_layer_check_errors(L)
     per_layer = w.K * (2 * matrix_bytes(w.f, w.d) + matrix_bytes(w.d, w.f)) + \
         2 * matrix_bytes(w.fs, w.d) + matrix_bytes(w.d, w.fs) + router_bytes(w)
     bytes_step = per_layer * w.layers
@@ -396,6 +444,9 @@ def run_stack(args, M, torch, np):
         "stack_hbm_gbps": round(bytes_step * steps / dt / 1e9, 1),
         "stack_hbm_frac": round(bytes_step * steps / dt / 1e9 / PEAK_HBM_GBPS, 4),
         "bytes_per_token": bytes_step, "finite": finite,
+        "layer_kernel_us": round(kern_ms * 1e3 / max(1, kern_n), 3),
+        "kernel_share_of_step": round(kern_ms / steps / (dt * 1e3 / steps), 4),
+        "error_flags": flags,
     }
     M.moe_stack_destroy(stack)
     for L in layers:
@@ -583,7 +634,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="decode: without the prefill summary; prefill: without the dense-routing run")
-    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=160, help="oracle tokens on every core")
+    ap.add_argument("--cpu-single-tokens", type=int, default=6, help="oracle tokens on one core")
+    ap.add_argument("--stack-steps", type=int, default=32, help="steps of the 30-layer stack leg (default line)")
     ap.add_argument("--decode-path", choices=("fused", "split"), default="fused",
                     help="fused: one kernel per layer and token; split: router+shared | routed gate/up | down")
     ap.add_argument("--mode", choices=("graph", "direct"), default="graph",
@@ -611,6 +664,10 @@ def main():
             result["prefill_128"] = {k: p[k] for k in ("value", "unit", "ms_per_step", "mfma_util", "tflops",
                                                        "hbm_gbps_distinct_expert_bytes", "hbm_frac",
                                                        "distinct_experts_per_chunk")}
+            st = run_stack(args, M, torch, np, steps=args.stack_steps)
+            result["stack30"] = {k: st[k] for k in ("value", "unit", "steps", "ms_per_step", "stack_hbm_gbps",
+                                                    "stack_hbm_frac", "layer_kernel_us", "kernel_share_of_step",
+                                                    "finite", "error_flags", "config")}
     elif args.workload == "prefill":
         result = run_prefill(args, M, torch, np)
     elif args.workload == "stack":

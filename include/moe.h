@@ -161,8 +161,13 @@ typedef struct {
   int32_t residual;           /* nonzero: out = act(x_in + y) where x_in is the
                                  `residual_src` tensor (stack glue) */
   const void* residual_src;   /* DEVICE [T][d_model] of act_dtype, or NULL */
-  int32_t* sort_offsets;      /* DEVICE [E+1] out (prefill path only) */
-  int32_t* sort_perm;         /* DEVICE [T*K] out (prefill path only) */
+  int32_t* sort_offsets;      /* DEVICE [ceil(T/128)][E+1] out (prefill path
+                                 only): the grouping of each 128-token chunk,
+                                 offsets into that chunk's part of sort_perm */
+  int32_t* sort_perm;         /* DEVICE [T*K] out (prefill path only): chunk c
+                                 fills entries [128*c*K, 128*c*K + C*K) with
+                                 its pairs in (expert, token) order, each as
+                                 (t - 128*c)*K + k (chunk-local token index) */
 } moe_fwd_opts;
 
 moe_status moe_layer_forward_ex(const void* x, moe_layer* layer, void* out, int32_t n_tokens,
@@ -186,10 +191,22 @@ moe_status moe_layer_sort(const int32_t* ids, moe_layer* layer, int32_t n_tokens
 moe_status moe_layer_bytes(const moe_layer* layer, uint64_t* device_bytes, uint64_t* expert_bytes);
 
 /* Waits for the device, then returns and clears the layer's sticky kernel
- * error flags in *flags (HOST): bit 0 = a forced expert id was outside
- * 0..E-1 (it was replaced by 0), bit 1 = a chosen expert was not resident,
- * bit 2 = a workgroup of the fused kernel gave up waiting for its inputs
- * (bounded wait; that call's output is not valid). */
+ * error flags in *flags (HOST):
+ *   bit 0  a forced expert id was outside 0..E-1 (it was replaced by 0);
+ *   bit 1  a chosen expert was not resident (its output read as zero);
+ *   bit 2  a workgroup gave up waiting for another one's results: a bounded
+ *          wait of the fused kernel, or of expert kernels launched ahead of a
+ *          streamed call's cache step, ran out (seconds; for example when
+ *          another process holds most of the GPU);
+ *   bit 3  an intermediate activation |silu(gate.x) * up.x| reached 65504,
+ *          the largest fp16 value: bf16 layers on the DECODE and FUSED paths
+ *          hand these activations between kernels as fp16, so such inputs are
+ *          outside their range (the PREFILL path keeps them in bf16).
+ * Any set bit means the output of some call since the last check is not
+ * valid.  The forward calls return MOE_OK without waiting for the GPU, so
+ * MOE_OK from a FUSED call, or from a streamed call whose expert kernels
+ * were launched ahead, does not prove that its output is valid: check the
+ * flags after the calls whose outputs matter. */
 moe_status moe_layer_check_errors(moe_layer* layer, int32_t* flags);
 
 /* The path run by calls that pass MOE_PATH_AUTO (moe_layer_forward, a NULL
@@ -349,6 +366,21 @@ moe_status moe_lru_step(moe_lru* lru, int32_t layer, const int32_t* chosen, int3
                         int32_t* miss_out);
 moe_status moe_lru_stats(const moe_lru* lru, moe_cache_stats* out);
 moe_status moe_lru_destroy(moe_lru* lru);
+
+/* ---- test hooks ----------------------------------------------------------
+ * Dequantise matrix `which` (0 gate, 1 up, 2 down) of routed expert `expert`
+ * (-1: the shared expert) on the GPU from the library's device layout, with
+ * the same addressing as the GEMV kernels: host_out[r][c] =
+ * fma(scale, q, bias) in fp32, [rows][cols] row-major (gate/up: d_ff x
+ * d_model, down: d_model x d_ff).  Blocks; allocates a temporary device
+ * buffer.  Checks the device repack against the canonical layout (an
+ * all-q = 8 group gives 8*scale + bias; a one-hot nibble lands at its own
+ * row and column). */
+moe_status moe_debug_dequant(const moe_layer* layer, int32_t which, int32_t expert, float* host_out);
+/* How long a streamed one-token call spins for its routing in host memory
+ * before it waits for the stream instead (default 2 000 000 us).  0 makes
+ * every such call take the waiting branch, which must give the same output. */
+moe_status moe_debug_host_wait(moe_layer* layer, int64_t microseconds);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* moe_last_error(void);

@@ -47,6 +47,15 @@ int oracle_threads(void) {
 #endif
 }
 
+/* Set that number (n >= 1); used to time the oracle on one core. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---- exact storage-format decoding ------------------------------------- */
 
 double oracle_f16_to_f64(uint16_t h) {

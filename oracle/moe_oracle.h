@@ -19,6 +19,7 @@ typedef struct {
 } oracle_layer;
 
 int oracle_threads(void);
+void oracle_set_threads(int n);
 double oracle_f16_to_f64(uint16_t h);
 double oracle_bf16_to_f64(uint16_t b);
 uint16_t oracle_f64_to_bf16(double v);

@@ -48,6 +48,8 @@ def lib():
         P, I = C.c_void_p, C.c_int
         L.oracle_threads.restype = C.c_int
         L.oracle_threads.argtypes = []
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [C.c_int]
         L.oracle_f16_to_f64.restype = C.c_double
         L.oracle_f16_to_f64.argtypes = [C.c_uint16]
         L.oracle_bf16_to_f64.restype = C.c_double
@@ -156,6 +158,10 @@ def sort(ids: np.ndarray, E: int):
 
 def threads() -> int:
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
 
 
 def f16_to_f64(h: int) -> float:

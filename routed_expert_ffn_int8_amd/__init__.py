@@ -95,6 +95,8 @@ _SIGS = {
     "moe_cache_detach": [_P],
     "moe_cache_pool_stats": [_P, C.POINTER(moe_cache_stats)],
     "moe_cache_pool_contents": [_P, _P, _P],
+    "moe_debug_dequant": [_P, C.c_int32, C.c_int32, _P],
+    "moe_debug_host_wait": [_P, C.c_int64],
 }
 
 _lib = None
@@ -375,3 +377,16 @@ def moe_cache_pool_contents(pool: int, n_slots: int):
     exp = np.empty(n_slots, np.int32)
     _check(load().moe_cache_pool_contents(pool, lay.ctypes.data, exp.ctypes.data))
     return lay, exp
+
+
+# ----------------------------------------------------------------- test hooks
+def moe_debug_dequant(layer: int, which: int, expert: int, rows: int, cols: int) -> np.ndarray:
+    """fp32 [rows][cols] of matrix `which` (0 gate, 1 up, 2 down) of `expert`
+    (-1 = shared), dequantised on the GPU from the device layout."""
+    out = np.empty((rows, cols), np.float32)
+    _check(load().moe_debug_dequant(layer, which, expert, out.ctypes.data))
+    return out
+
+
+def moe_debug_host_wait(layer: int, microseconds: int):
+    _check(load().moe_debug_host_wait(layer, int(microseconds)))

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <chrono>
 #include <cstdarg>
 #include <cstdio>
@@ -140,6 +141,7 @@ struct moe_layer {
   int32_t* h_ids = nullptr;    // pinned, coherent routing copy [max_tokens*K], then a sequence word
   void* d_host_ids = nullptr;  // its device view
   uint32_t host_seq = 0;       // sequence number of the last one-token routing written by the GPU
+  int64_t host_wait_us = 2000000;  // how long the host spins for that routing before it waits for the stream
   uint32_t* d_go = nullptr;    // device copy of the verdict word of a call launched ahead
   int32_t* h_pf = nullptr;     // prefill through the cache: pinned counts [E], then group tile lists
   int32_t* d_pf_tiles = nullptr;  // the group tile lists on the device
@@ -159,13 +161,18 @@ struct moe_stack {
   std::vector<moe_layer*> layers;
   float eps = 1e-6f;
   int prefetch_depth = 0;
-  // One synchronisation area and one set of activation copies for every
-  // layer's fused launches.  The layers run one after another, so a single
-  // area's launch count serves them all (its tag just keeps counting), and
-  // the area stays in cache instead of each layer touching its own cold one.
+  // One synchronisation area and one set of activation copies per layer
+  // shape (E, K, d_ff, d_ff_shared), shared by the fused launches of every
+  // layer of that shape.  The layers run one after another, so one area's
+  // launch count serves them all (its tag just keeps counting), and the area
+  // stays in cache instead of each layer touching its own cold one.  Layers
+  // of another shape need their own: a stage counter grows by the number of
+  // that stage's workgroups per launch, which depends on the shape, and the
+  // activation copies are laid out for one vector length.
   int dev = 0;
-  uint32_t* d_counter = nullptr;
-  void* d_arep = nullptr;
+  std::vector<uint32_t*> d_counter;  // per shape
+  std::vector<void*> d_arep;         // per shape
+  std::vector<int> area_of;          // per layer: index of its shape's area
 };
 
 struct moe_lfu {
@@ -467,15 +474,17 @@ void set_go(const moe_layer* L, uint32_t seq, bool run) {
   __atomic_store_n(go_word(L), 2u * seq + (run ? 0u : 1u), __ATOMIC_RELEASE);
 }
 
-// Spin until the GPU has written `seq` behind the routing in h_ids (about
-// 2 s at most); true when it has.
+// Spin until the GPU has written `seq` behind the routing in h_ids (at most
+// the layer's host_wait_us, 2 s unless a test shortened it); true when it has.
 bool wait_host_flag(const moe_layer* L, uint32_t seq) {
   const uint32_t* flag = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(L->h_ids) +
                                                            host_flag_offset(L));
   const auto t0 = std::chrono::steady_clock::now();
+  const auto limit = std::chrono::microseconds(L->host_wait_us);
   for (uint32_t i = 1;; ++i) {
     if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == seq) return true;
-    if ((i & 4095) == 0 && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(2)) return false;
+    if ((i & 4095) == 0 || L->host_wait_us == 0)
+      if (std::chrono::steady_clock::now() - t0 >= limit) return false;
     __builtin_ia32_pause();
   }
 }
@@ -505,8 +514,18 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
   moe_cache_pool* P = L->pool;
   if (!L->lfu && !P) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
   const size_t n = (size_t)T * L->K;
+  bool verdict_given = false;
   if (seq) {  // one token: the top-K kernel writes the ids and then seq into host memory
     if (!wait_host_flag(L, seq)) {  // not within the time limit: the stream's own status decides
+      // Expert kernels launched ahead on `stream` wait for this call's
+      // verdict, so the synchronisation below would wait for them until their
+      // own bounded waits ran out.  They are told to skip first; the call then
+      // runs them again behind its fills, as after a miss.
+      if (verdict) {
+        set_go(L, seq, false);
+        *verdict = 0;
+        verdict_given = true;
+      }
       HIP_OK(hipStreamSynchronize(stream));
       if (!wait_host_flag(L, seq)) return fail(MOE_ERR_STATE, "the routing of the call did not reach the host");
     }
@@ -539,7 +558,7 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
     P->policy->step(L->pool_id, chosen.data(), m, slot.data(), miss.data(), ev_layer.data(), ev_expert.data());
   else
     L->lfu->step(chosen.data(), m, slot.data(), miss.data(), ev_expert.data());
-  if (verdict) {  // kernels launched ahead: they run now when every chosen expert was a hit
+  if (verdict && !verdict_given) {  // kernels launched ahead: they run now when every chosen expert was a hit
     bool any_miss = false;
     for (int i = 0; i < m; ++i) any_miss |= miss[i] != 0;
     set_go(L, seq, !any_miss);
@@ -988,6 +1007,47 @@ moe_status moe_layer_check_errors(moe_layer* L, int32_t* flags) {
   return MOE_OK;
 }
 
+moe_status moe_debug_dequant(const moe_layer* L, int32_t which, int32_t expert, float* host_out) {
+  if (!L || !host_out) return fail(MOE_ERR_INVALID, "layer/host_out is NULL");
+  if (which < 0 || which > 2) return fail(MOE_ERR_INVALID, "which=%d not in 0..2 (gate, up, down)", which);
+  if (expert < -1 || expert >= L->E) return fail(MOE_ERR_INVALID, "expert %d not in -1..%d", expert, L->E - 1);
+  if (expert == -1 && L->fs == 0) return fail(MOE_ERR_INVALID, "the layer has no shared expert");
+  HIP_OK(hipSetDevice(L->dev));
+  const BlobLayout& B = expert < 0 ? L->sl : L->rl;
+  const MatLayout& m = which == 0 ? B.gate : which == 1 ? B.up : B.down;
+  const uint8_t* blob = nullptr;
+  uint8_t* tmp = nullptr;  // a streamed expert's blob, copied from the pinned store
+  if (expert < 0) {
+    blob = L->d_shared;
+  } else if (L->residency == MOE_RESIDENT) {
+    blob = L->d_experts + (size_t)expert * L->rl.stride;
+  } else {
+    if (dalloc(&tmp, L->rl.stride) != hipSuccess) return fail(MOE_ERR_NOMEM, "blob copy alloc failed");
+    blob = tmp;
+  }
+  float* d_out = nullptr;
+  const size_t n = (size_t)m.rows * m.cols;
+  if (dalloc(&d_out, n * 4) != hipSuccess) {
+    (void)hipFree(tmp);
+    return fail(MOE_ERR_NOMEM, "dequant output alloc failed");
+  }
+  hipError_t e = hipSuccess;
+  if (tmp) e = hipMemcpy(tmp, L->h_store + (size_t)expert * L->rl.stride, L->rl.stride, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = launch_dequant(blob, (uint32_t)m.q_off, (uint32_t)m.sb_off, m.rows, m.cols, d_out, nullptr);
+  if (e == hipSuccess) e = hipMemcpy(host_out, d_out, n * 4, hipMemcpyDeviceToHost);
+  (void)hipFree(d_out);
+  (void)hipFree(tmp);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "dequant failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+moe_status moe_debug_host_wait(moe_layer* L, int64_t microseconds) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (microseconds < 0) return fail(MOE_ERR_INVALID, "microseconds=%lld is negative", (long long)microseconds);
+  L->host_wait_us = microseconds;
+  return MOE_OK;
+}
+
 moe_status moe_layer_profile(moe_layer* L, int32_t enable) {
   if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
   if (enable && !L->prof) L->prof.reset(new EventProfiler());
@@ -1269,20 +1329,33 @@ moe_status moe_stack_create(moe_layer* const* layers, int32_t n, float eps, moe_
   S->layers.assign(layers, layers + n);
   S->eps = eps;
   S->dev = layers[0]->dev;
-  int maxE = 1, maxF = 1;
-  for (int i = 0; i < n; ++i) {
-    maxE = std::max(maxE, layers[i]->E);
-    maxF = std::max(maxF, layers[i]->fs + layers[i]->K * layers[i]->f);
-  }
   HIP_OK(hipSetDevice(S->dev));
-  if (dalloc(&S->d_counter, decode_sync_bytes(maxE)) != hipSuccess ||
-      dalloc(&S->d_arep, decode_arep_bytes(maxF)) != hipSuccess) {
-    (void)hipFree(S->d_counter);
-    (void)hipFree(S->d_arep);
-    return fail(MOE_ERR_NOMEM, "stack synchronisation area failed");
+  std::vector<std::array<int, 4>> shapes;
+  for (int i = 0; i < n; ++i) {
+    const moe_layer* L = layers[i];
+    const std::array<int, 4> key{L->E, L->K, L->f, L->fs};
+    size_t j = std::find(shapes.begin(), shapes.end(), key) - shapes.begin();
+    if (j == shapes.size()) {
+      shapes.push_back(key);
+      const size_t F = (size_t)L->fs + (size_t)L->K * L->f;
+      uint32_t* cnt = nullptr;
+      void* rep = nullptr;
+      if (dalloc(&cnt, decode_sync_bytes(L->E)) != hipSuccess || dalloc(&rep, decode_arep_bytes((int)F)) != hipSuccess) {
+        (void)hipFree(cnt);
+        (void)hipFree(rep);
+        for (size_t k = 0; k < S->d_counter.size(); ++k) {
+          (void)hipFree(S->d_counter[k]);
+          (void)hipFree(S->d_arep[k]);
+        }
+        return fail(MOE_ERR_NOMEM, "stack synchronisation area failed");
+      }
+      S->d_counter.push_back(cnt);
+      S->d_arep.push_back(rep);
+      HIP_OK(hipMemset(cnt, 0, decode_sync_bytes(L->E)));
+      HIP_OK(hipMemset(rep, 0, decode_arep_bytes((int)F)));  // parity 0: older than any launch
+    }
+    S->area_of.push_back((int)j);
   }
-  HIP_OK(hipMemset(S->d_counter, 0, decode_sync_bytes(maxE)));
-  HIP_OK(hipMemset(S->d_arep, 0, decode_arep_bytes(maxF)));  // parity 0: older than any launch
   HIP_OK(hipDeviceSynchronize());
   *out = S.release();
   return MOE_OK;
@@ -1298,8 +1371,8 @@ moe_status moe_stack_forward(void* h, moe_stack* S, int32_t n_tokens, const uint
     a.rms = 1;
     a.eps = S->eps;
     a.resid = h;
-    a.counter = S->d_counter;  // shared by the stack's layers (see moe_stack)
-    a.arep = S->d_arep;
+    a.counter = S->d_counter[S->area_of[l]];  // shared by the stack's layers of this shape (see moe_stack)
+    a.arep = S->d_arep[S->area_of[l]];
     moe_fwd_opts o{};
     o.reuse_previous = reuse_mask ? reuse_mask[l] : 0;
     o.topk_ids = ids_out ? ids_out + l * (size_t)n_tokens * L->K : nullptr;
@@ -1322,8 +1395,10 @@ moe_status moe_stack_destroy(moe_stack* S) {
   if (S) {
     (void)hipSetDevice(S->dev);
     (void)hipDeviceSynchronize();
-    (void)hipFree(S->d_counter);
-    (void)hipFree(S->d_arep);
+    for (size_t k = 0; k < S->d_counter.size(); ++k) {
+      (void)hipFree(S->d_counter[k]);
+      (void)hipFree(S->d_arep[k]);
+    }
   }
   delete S;
   return MOE_OK;

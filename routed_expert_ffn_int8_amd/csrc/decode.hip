@@ -341,6 +341,7 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
     const float usum =
         (S.red[r * 2 + 1] + S.red[W + r * 2 + 1]) + (S.red[2 * W + r * 2 + 1] + S.red[3 * W + r * 2 + 1]);
     const float v = silu(gsum) * usum;
+    if (ACT == 1 && !(fabsf(v) < kF16HandoffMax)) atomicOr(a.err, kErrRange);
     if (REPS) {  // S.xf is free: the bf16 products read S.xp
       const int m = r & 7;
       reinterpret_cast<uint16_t*>(S.xf)[(r & ~7) + (m & 3) * 2 + (m >> 2)] = f32_to_f16_tagged(v, tag);
@@ -1184,7 +1185,30 @@ hipError_t launch_fused(const LayerArgs& a, hipStream_t s) {
   return launch_fused_ne<16>(a, s);
 }
 
+// One thread per weight: the 16-byte word and the scale/bias word that the
+// GEMV kernels read for (row, col), decoded the same way.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* blob, uint32_t q_off, uint32_t sb_off, int rows,
+                                                      int cols, float* out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * cols) return;
+  const int row = (int)(i / cols), col = (int)(i % cols);
+  const int G = cols >> 6, rb = row >> 3, r = row & 7, g = col >> 6, c = col & 63;
+  const size_t off = (((size_t)rb * G + g) * 2) * 128 + (c >> 5) * 128 + r * 16;  // as gate_up_block / down_block
+  const v4u q = ldg<v4u>(blob + q_off + off);
+  const uint32_t w = q[(c & 31) >> 3];
+  const uint32_t nib = (w >> (4 * (c & 7))) & 0xFu;
+  const uint32_t sb = ldg<uint32_t>(blob + sb_off + (((size_t)rb * G + g) * 8 + r) * 4);
+  out[i] = fmaf(f16_to_f32((uint16_t)(sb & 0xFFFFu)), (float)nib, f16_to_f32((uint16_t)(sb >> 16)));
+}
+
 }  // namespace
+
+hipError_t launch_dequant(const uint8_t* blob, uint32_t q_off, uint32_t sb_off, int rows, int cols, float* out,
+                          hipStream_t s) {
+  const size_t n = (size_t)rows * cols;
+  dequant_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(blob, q_off, sb_off, rows, cols, out);
+  return hipGetLastError();
+}
 
 size_t decode_lds_bytes_x(int d) { return x_stage_bytes(d); }
 size_t decode_sync_bytes(int E) { return sync_area_bytes(E); }

@@ -88,9 +88,18 @@ struct LayerArgs {
 
 enum : int { kStageRouter = 1, kStageShared = 2, kStageRouted = 4, kStageDown = 8, kStageAll = 15 };
 
-enum : int32_t { kErrBadForcedId = 1, kErrMissingExpert = 2, kErrSyncTimeout = 4 };
+enum : int32_t { kErrBadForcedId = 1, kErrMissingExpert = 2, kErrSyncTimeout = 4, kErrRange = 8 };
+
+// The decode kernels hand the intermediate activations silu(g)*u between
+// workgroups as fp16; a value at or above this magnitude (the largest fp16
+// value) would not survive the hand-off, so the kernel raises kErrRange.
+constexpr float kF16HandoffMax = 65504.f;
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s);
+// Dequantise one matrix of an expert blob from the device layout into fp32
+// out[rows][cols] = fma(scale, q, bias) (test hook).
+hipError_t launch_dequant(const uint8_t* blob, uint32_t q_off, uint32_t sb_off, int rows, int cols, float* out,
+                          hipStream_t s);
 // Whether the single-launch decode kernel can serve these arguments.
 bool decode_fused_ok(const LayerArgs& a);
 // Bytes of its synchronisation area for E experts.

@@ -696,6 +696,11 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
     a.x = static_cast<const char*>(a0.x) + xo;
     a.out = static_cast<char*>(a0.out) + xo;
     if (a0.resid) a.resid = static_cast<const char*>(a0.resid) + xo;
+    // The call's routing workspace is [T][K]: each chunk keeps its own rows, so
+    // a later call that reuses this call's sets finds every chunk's sets.
+    a.ids = a0.ids + (size_t)c0 * a.K;
+    a.wts = a0.wts + (size_t)c0 * a.K;
+    a.sel_addr = a0.sel_addr + (size_t)c0 * a.K;
     if (a0.forced) a.forced = a0.forced + (size_t)c0 * a.K;
     if (a0.ids_out) a.ids_out = a0.ids_out + (size_t)c0 * a.K;
     if (a0.w_out) a.w_out = a0.w_out + (size_t)c0 * a.K;
@@ -748,9 +753,9 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
       if (p0.streamer && (e = p0.streamer->done(grp, s)) != hipSuccess) return e;
     }
     launch_timed(a.prof, kKPrefillCombine, pf_combine_kernel, dim3((a.d + 255) / 256, C), dim3(256), 0, s, p);
-    if (p0.sort_offsets_out)
-      if ((e = hipMemcpyAsync(p0.sort_offsets_out, p.offsets, (a.E + 1) * 4, hipMemcpyDeviceToDevice, s)) !=
-          hipSuccess)
+    if (p0.sort_offsets_out)  // one row of E + 1 offsets per chunk
+      if ((e = hipMemcpyAsync(p0.sort_offsets_out + (size_t)(c0 / kChunkTokens) * (a.E + 1), p.offsets,
+                              (a.E + 1) * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
         return e;
     if (p0.sort_perm_out)
       if ((e = hipMemcpyAsync(p0.sort_perm_out + (size_t)c0 * a.K, p.perm, (size_t)C * a.K * 4,

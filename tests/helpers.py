@@ -117,3 +117,30 @@ def check_layer(gl: GpuLayer, OL: O.OracleLayer, x: np.ndarray, y_gpu, ids_gpu, 
         assert mx <= abs_tol * rms, f"token {t}: max abs {mx:.3e} > {abs_tol} * rms {rms:.3e}"
         worst = max(worst, rel)
     return worst
+
+
+def _bf16_ulp(v):
+    a = np.abs(v.astype(np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0**-126)))
+    return 2.0 ** (e - 7)
+
+
+def check_stack_layer(OL: O.OracleLayer, K: int, h_in: np.ndarray, h_out: np.ndarray, ids_gpu: np.ndarray):
+    """Teacher forcing of one stack layer on the GPU's own input h_in (bf16
+    bits [d]): the oracle takes n = bf16(rmsnorm(h_in)), routes it (the GPU's
+    set must be the oracle's outside the tie band; inside it the oracle is
+    forced to the GPU's set) and forms bf16(h_in + MoE(n)); the GPU's h_out
+    must lie within the layer tolerance of that, plus one bf16 ulp of the
+    result for its final rounding.  Returns the relative error."""
+    n = O.rmsnorm_bf16(h_in)
+    logits = OL.logits(n[None, :])
+    y_ref, ids_ref, _, margin = OL.forward(n[None, :])
+    swapped = check_selection(ids_gpu.reshape(1, K), ids_ref, logits, margin, K)
+    if swapped:
+        y_ref, *_ = OL.forward(n[None, :], forced=ids_gpu.reshape(1, K))
+    ref = O.residual_bf16(h_in, y_ref[0])
+    got, want = O.tokens_to_f64(h_out), O.tokens_to_f64(ref)
+    ynorm = np.linalg.norm(y_ref[0])
+    err = np.linalg.norm(got - want)
+    assert err <= 5e-3 * ynorm + np.linalg.norm(_bf16_ulp(want)), (err, ynorm)
+    return err / ynorm

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import routed_expert_ffn_int8_amd as M
-from gen.workloads import WORKLOADS, Workload, make_layer, make_tokens
+from gen.workloads import WORKLOADS, Workload, f32_to_bf16_bits, make_layer, make_tokens
 from oracle import oracle as O
 from tests.helpers import GpuLayer, check_layer, empty_like_act, to_device, to_host, torch_mod
 
@@ -43,6 +43,21 @@ def test_fused_decode_layer_tokens(decode_layer):
         worst = max(worst, check_layer(gl, OL, x[t:t + 1], *got))
         _agree(got, gl.forward(x[t:t + 1], path=M.MOE_PATH_DECODE))
     print(f"fused: worst rel L2 over 16 tokens {worst:.3e}")
+    assert M.moe_layer_check_errors(gl.handle) == 0
+
+
+def test_fused_router_integer_inputs_bit_exact(decode_layer):
+    """The fused kernel's router workgroups on integer-valued tokens: exact
+    fp32 sums, so the chosen sets equal the oracle's with no tie band."""
+    w, gl, OL = decode_layer
+    rng = np.random.default_rng(13)
+    x = f32_to_bf16_bits(rng.integers(-2, 3, size=(12, w.d)).astype(np.float32))
+    logits = OL.logits(x)
+    for t in range(12):
+        _, ids, wt = gl.forward(x[t:t + 1], path=M.MOE_PATH_FUSED)
+        ids_ref, w_ref, _ = O.select(logits[t], w.K)
+        assert np.array_equal(ids[0], ids_ref), t
+        assert np.allclose(wt[0], w_ref, rtol=2e-5, atol=1e-7)
     assert M.moe_layer_check_errors(gl.handle) == 0
 
 

@@ -4,9 +4,9 @@ import numpy as np
 import pytest
 
 import routed_expert_ffn_int8_amd as M
-from gen.workloads import WORKLOADS, Workload, make_layer, make_tokens
+from gen.workloads import WORKLOADS, Workload, f32_to_bf16_bits, make_layer, make_tokens
 from oracle import oracle as O
-from tests.helpers import GpuLayer, check_layer, to_device, torch_mod
+from tests.helpers import GpuLayer, check_layer, check_selection, to_device, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -15,9 +15,21 @@ pytestmark = pytest.mark.gpu
 def prefill_layer():
     w = WORKLOADS[3]
     arrays = make_layer(w)
-    gl = GpuLayer(w, arrays, 512)
+    gl = GpuLayer(w, arrays, 2048)
     yield w, gl, O.OracleLayer.from_workload(w, arrays)
     gl.close()
+
+
+def _oracle_selection(OL, x, K):
+    """The oracle's logits, sets, coefficients and margins of every token
+    (router and selection only)."""
+    logits = OL.logits(x)
+    ids = np.empty((x.shape[0], K), np.int32)
+    wts = np.empty((x.shape[0], K))
+    margin = np.empty(x.shape[0])
+    for t in range(x.shape[0]):
+        ids[t], wts[t], margin[t] = O.select(logits[t], K)
+    return logits, ids, wts, margin
 
 
 def test_prefill_chunk_128_full(prefill_layer):
@@ -28,28 +40,82 @@ def test_prefill_chunk_128_full(prefill_layer):
     print(f"prefill chunk: worst rel L2 {worst:.3e}")
 
 
-def test_prefill_512_as_four_chunks_sampled(prefill_layer):
+def test_prefill_512_as_four_chunks_full(prefill_layer):
+    """The 512-token run of the prefill workload (four 128-token chunks in
+    one call), every token against the oracle."""
     w, gl, OL = prefill_layer
     x = make_tokens(w, 512, stream=32)
     y, ids, wt = gl.forward(x, path=M.MOE_PATH_PREFILL)
-    sample = np.r_[0:3, 125:131, 254:258, 380:384, 509:512]
-    check_layer(gl, OL, x[sample], y[sample], ids[sample], wt[sample])
+    worst = check_layer(gl, OL, x, y, ids, wt)
+    print(f"prefill 512: worst rel L2 {worst:.3e}")
+
+
+def test_prefill_2048_as_sixteen_chunks(prefill_layer):
+    """The 2048-token run (sixteen chunks in one call): every token's expert
+    set against the oracle's selection, and outputs on the first two and last
+    two tokens of every chunk plus one inside it (80 tokens, every chunk edge)."""
+    w, gl, OL = prefill_layer
+    x = make_tokens(w, 2048, stream=36)
+    y, ids, wt = gl.forward(x, path=M.MOE_PATH_PREFILL)
+    logits, ids_ref, _, margin = _oracle_selection(OL, x, w.K)
+    check_selection(ids, ids_ref, logits, margin, w.K)
+    sample = np.concatenate([c * 128 + np.array([0, 1, 61, 126, 127]) for c in range(16)])
+    worst = check_layer(gl, OL, x[sample], y[sample], ids[sample], wt[sample])
+    print(f"prefill 2048: worst rel L2 on {len(sample)} sampled tokens {worst:.3e}")
 
 
 def test_prefill_sort_outputs(prefill_layer):
+    """Grouping outputs of a two-chunk call: one row of offsets per chunk and
+    each chunk's pairs (chunk-local token index) in its part of the perm."""
     w, gl, OL = prefill_layer
     torch = torch_mod()
-    x = make_tokens(w, 100, stream=33)
-    out = torch.empty((100, w.d), dtype=torch.bfloat16, device="cuda")
-    ids = torch.empty((100, w.K), dtype=torch.int32, device="cuda")
-    offs = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
-    perm = torch.empty(100 * w.K, dtype=torch.int32, device="cuda")
+    T = 200
+    x = make_tokens(w, T, stream=33)
+    out = torch.empty((T, w.d), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+    offs = torch.empty((2, w.E + 1), dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * w.K, dtype=torch.int32, device="cuda")
     o = M.fwd_opts(topk_ids=ids, path=M.MOE_PATH_PREFILL, sort_offsets=offs, sort_perm=perm)
-    M.moe_layer_forward_ex(to_device(x), gl.handle, out, 100, o)
+    M.moe_layer_forward_ex(to_device(x), gl.handle, out, T, o)
     torch.cuda.synchronize()
-    c, off_ref, perm_ref, _ = O.sort(ids.cpu().numpy(), w.E)
-    assert np.array_equal(offs.cpu().numpy(), off_ref)
-    assert np.array_equal(perm.cpu().numpy(), perm_ref)
+    ids_h, offs_h, perm_h = ids.cpu().numpy(), offs.cpu().numpy(), perm.cpu().numpy()
+    for c, (t0, t1) in enumerate(((0, 128), (128, T))):
+        _, off_ref, perm_ref, _ = O.sort(ids_h[t0:t1], w.E)
+        assert np.array_equal(offs_h[c], off_ref), c
+        assert np.array_equal(perm_h[t0 * w.K:t1 * w.K], perm_ref), c
+
+
+def test_reuse_previous_after_multichunk_prefill(prefill_layer):
+    """A 256-token prefill call, then calls that reuse its expert sets (prefill
+    and decode paths): every chunk's sets come back, with coefficients from
+    the new logits, and outputs match the oracle forced to those sets."""
+    w, gl, OL = prefill_layer
+    T = 256
+    x1 = make_tokens(w, T, stream=37)
+    _, ids1, _ = gl.forward(x1, path=M.MOE_PATH_PREFILL)
+    x2 = make_tokens(w, T, stream=38)
+    y2, ids2, wt2 = gl.forward(x2, path=M.MOE_PATH_PREFILL, reuse=True)
+    assert np.array_equal(ids2, ids1)
+    sample = np.r_[0:4, 124:132, 252:256]
+    check_layer(gl, OL, x2[sample], y2[sample], ids2[sample], wt2[sample], forced=ids1[sample])
+    y3, ids3, wt3 = gl.forward(x2, path=M.MOE_PATH_DECODE, reuse=True)
+    assert np.array_equal(ids3, ids1)
+    check_layer(gl, OL, x2[sample], y3[sample], ids3[sample], wt3[sample], forced=ids1[sample])
+    assert M.moe_layer_check_errors(gl.handle) == 0
+
+
+def test_prefill_router_integer_inputs_bit_exact(prefill_layer):
+    """Integer-valued tokens make every matrix-core router sum an exact
+    integer in fp32, so each logit is the fp32 rounding of the oracle's and
+    the chosen sets must equal the oracle's with no tie band."""
+    w, gl, OL = prefill_layer
+    rng = np.random.default_rng(12)
+    for rep in range(2):
+        x = f32_to_bf16_bits(rng.integers(-2, 3, size=(128, w.d)).astype(np.float32))
+        _, ids, wt = gl.forward(x, path=M.MOE_PATH_PREFILL)
+        _, ids_ref, w_ref, _ = _oracle_selection(OL, x, w.K)
+        assert np.array_equal(ids, ids_ref), rep
+        assert np.allclose(wt, w_ref, rtol=2e-5, atol=1e-7)
 
 
 PSHAPES = [  # (d, E, K, f, fs, T)

@@ -393,3 +393,58 @@ def test_sort_bit_exact(T):
     assert np.array_equal(perm.cpu().numpy()[:T * wl.K], p)
     assert np.array_equal(inv.cpu().numpy()[:T * wl.K], iv)
     gl.close()
+
+
+def test_decode_stack30_trajectory_teacher_forced():
+    """The 30-layer decode stack (d_model 2816, 128 experts, top-8, all
+    weights resident) driven for 16 steps of its recurrence, next input =
+    output + N(0, 0.1): every step of the production call equals its layers
+    run one by one, and nine sampled (step, layer) pairs, first and last
+    layer included, match the oracle on the GPU's own input."""
+    from gen.workloads import make_noise
+    from tests.helpers import check_stack_layer
+    torch = torch_mod()
+    w = WORKLOADS[2]
+    steps = 16
+    pairs = {(0, 0), (1, 29), (3, 7), (5, 14), (8, 21), (10, 3), (13, 26), (15, 11), (15, 29)}
+    keep = {l for _, l in pairs}
+    gls, ols = [], {}
+    for l in range(w.layers):
+        arrays = make_layer(w, layer=l)
+        gls.append(GpuLayer(w, arrays, 1))
+        if l in keep:
+            ols[l] = O.OracleLayer.from_workload(w, arrays)
+        del arrays
+    stack = M.moe_stack_create([g.handle for g in gls], 1e-6)
+    singles = [M.moe_stack_create([g.handle], 1e-6) for g in gls]
+    noise = torch.from_numpy(make_noise(w, steps)).cuda()
+    h = to_device(make_tokens(w, 1, stream=5))
+    hs = h.clone()
+    ids = torch.empty((1, 1, w.K), dtype=torch.int32, device="cuda")
+    checked = 0
+    for t in range(steps):
+        M.moe_stack_forward(h, stack, 1)
+        for l in range(w.layers):
+            if (t, l) in pairs:
+                torch.cuda.synchronize()
+                h_in = to_host(hs)[0]
+                M.moe_stack_forward(hs, singles[l], 1, ids_out=ids)
+                torch.cuda.synchronize()
+                rel = check_stack_layer(ols[l], w.K, h_in, to_host(hs)[0], ids.cpu().numpy())
+                print(f"step {t} layer {l}: rel err {rel:.3e}")
+                checked += 1
+            else:
+                M.moe_stack_forward(hs, singles[l], 1)
+        torch.cuda.synchronize()
+        assert torch.equal(h, hs), f"step {t}: the stack call differs from its layers"
+        h.copy_((h.float() + noise[t]).to(torch.bfloat16))
+        hs.copy_(h)
+    assert checked == len(pairs)
+    assert bool(torch.isfinite(h.float()).all())
+    for g in gls:
+        assert M.moe_layer_check_errors(g.handle) == 0
+    for s in singles:
+        M.moe_stack_destroy(s)
+    M.moe_stack_destroy(stack)
+    for g in gls:
+        g.close()
