@@ -416,7 +416,7 @@ __device__ float router_row(const LayerArgs& a, int t, int e, const XStage& S) {
       }
     }
   }
-  acc = xor_sum(acc, 1, 32);  // every lane holds the same sum
+  acc = wave_sum_f32(acc);  // every lane holds the same sum (DPP, fixed order)
   return fmaf(s, acc, b);
 }
 

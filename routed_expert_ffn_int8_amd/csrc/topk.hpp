@@ -20,12 +20,6 @@ __device__ __forceinline__ uint32_t order_key(float l) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
@@ -51,6 +45,23 @@ __device__ __forceinline__ uint32_t kth_prefix(const uint32_t (&key)[NE], int K)
     }
   }
   return prefix;
+}
+
+// Coefficients of a chosen set held in LDS (`scratch`: ids ascending in
+// [0, K), their logits in [K, 2K)), by one wavefront: lane k < K takes the
+// k-th chosen expert; the maximum and the denominator are whole-wavefront
+// reductions in a fixed order (DPP), so every lane holds the same bits and
+// every kernel that fills scratch alike gets the same coefficients.
+__device__ __forceinline__ void topk_finish(int K, const uint32_t* scratch, int* id_out, float* w_out) {
+  const int lane = threadIdx.x & 63;
+  const int my_id = lane < K ? (int)scratch[lane] : 0;
+  const float my_l = lane < K ? __uint_as_float(scratch[K + lane]) : -INFINITY;
+  const uint32_t km = wave_max_u32(lane < K ? order_key(my_l) : 0u);  // the largest chosen key, as a float:
+  const float mx = __uint_as_float((km & 0x80000000u) ? (km & 0x7FFFFFFFu) : ~km);
+  const float v = lane < K ? expf(my_l - mx) : 0.f;
+  const float den = wave_sum_f32(v);
+  *id_out = my_id;
+  *w_out = v / den;
 }
 
 // Softmax top-K of token t by one wavefront (lane = threadIdx.x & 63).
@@ -88,6 +99,53 @@ __device__ void topk_wave(const LayerArgs& a, int t, const float* lt, int* id_ou
       scratch[rank] = (uint32_t)my_id;
       scratch[K + rank] = __float_as_uint(my_l);
     }
+  } else if (K <= 16) {
+    // K rounds of: the wavefront maximum of the remaining keys (DPP), the
+    // lowest expert index holding it (ballots), which leaves the pool.  Then
+    // the chosen entries are compacted in ascending index order.
+    uint32_t key[NE];
+    float lv[NE];
+    bool sel[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = lane + 64 * i;
+      const bool ok = e < E;
+      lv[i] = ok ? lt[e] : -INFINITY;
+      key[i] = ok ? order_key(lv[i]) : 0u;
+      sel[i] = false;
+    }
+    for (int k = 0; k < K; ++k) {
+      uint32_t lm = key[0];
+#pragma unroll
+      for (int i = 1; i < NE; ++i) lm = max(lm, key[i]);
+      const uint32_t m = wave_max_u32(lm);
+      int slot = -1, at = 0;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const uint64_t b = __ballot(key[i] == m);
+        if (slot < 0 && b != 0) {
+          slot = i;
+          at = (int)__builtin_ctzll(b);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NE; ++i)
+        if (i == slot && lane == at) {
+          key[i] = 0u;
+          sel[i] = true;
+        }
+    }
+    int pos_base = 0;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const uint64_t sm = __ballot(sel[i]);
+      if (sel[i]) {
+        const int pos = pos_base + lanes_below(sm);
+        scratch[pos] = (uint32_t)(lane + 64 * i);
+        scratch[K + pos] = __float_as_uint(lv[i]);
+      }
+      pos_base += __popcll(sm);
+    }
   } else {
     uint32_t key[NE];
     float lv[NE];
@@ -123,18 +181,8 @@ __device__ void topk_wave(const LayerArgs& a, int t, const float* lt, int* id_ou
       }
     }
   }
-  __threadfence_block();
-  if (lane < K) {
-    my_id = (int)scratch[lane];
-    my_l = __uint_as_float(scratch[K + lane]);
-  } else {
-    my_l = -INFINITY;
-  }
-  const float lmax = wave_max_f32(my_l);
-  const float v = (lane < K) ? expf(my_l - lmax) : 0.f;
-  const float den = xor_sum(v, 1, 32);
-  *id_out = my_id;
-  *w_out = v / den;
+  __builtin_amdgcn_wave_barrier();  // a wavefront's LDS accesses complete in order
+  topk_finish(K, scratch, id_out, w_out);
 }
 
 // The k-th chosen expert of token t (ascending order), uniform across the
