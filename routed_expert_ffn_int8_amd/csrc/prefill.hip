@@ -313,20 +313,30 @@ __device__ void stage_rows(int width, const uint16_t* const* rows, v4u* lds, flo
   __syncthreads();
 }
 
-__device__ __forceinline__ bf16x8 b_operand(uint32_t w) {
+// The nibble mask held in a vector register: the compiler cannot fold it
+// into an immediate (vector ALU instructions with three operands take none
+// on gfx9), so each pair is one v_and_or_b32 (mask in a VGPR, exponent in an
+// SGPR) instead of an and plus an or: 7 instructions per packed word, not 11.
+__device__ __forceinline__ uint32_t nibble_mask_v() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m));
+  return m;
+}
+
+// MFMA B operand of one packed word: four bf16 pairs 128 + q (see nib_pairs).
+__device__ __forceinline__ bf16x8 b_operand(uint32_t w, uint32_t mask) {
+  constexpr uint32_t M = (kExpBf16 << 8) * 0x00010001u;
   v4u v;
-  uint32_t np[4];
-  nib_pairs<kExpBf16>(w, np);
-  v[0] = np[0];
-  v[1] = np[1];
-  v[2] = np[2];
-  v[3] = np[3];
+  v[0] = (w & mask) | M;
+  v[1] = ((w >> 4) & mask) | M;
+  v[2] = ((w >> 8) & mask) | M;
+  v[3] = ((w >> 12) & mask) | M;
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ void group_epilogue(f32x4& acc, const f32x4& t, uint32_t sb, const float* xs4, float on) {
-  const float s = on * f16_to_f32((uint16_t)(sb & 0xFFFFu));
-  const float bb = on * f16_to_f32((uint16_t)(sb >> 16)) - 128.f * s;
+__device__ __forceinline__ void group_epilogue(f32x4& acc, const f32x4& t, uint32_t sb, const float* xs4) {
+  const float s = f16_to_f32((uint16_t)(sb & 0xFFFFu));
+  const float bb = f16_to_f32((uint16_t)(sb >> 16)) - 128.f * s;
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, t[i], fmaf(bb, xs4[i], acc[i]));
 }
@@ -430,25 +440,28 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
   for (int t = 0; t < kGuTiles; ++t) accg[t] = accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const v4u* arow = xs_lds + n * (W + 1);  // A operand: tile row m = lane & 15
-  // Branch-free body (clamped group index, zero factor past the end) so the
-  // compiler can keep kPre groups of loads in flight across iterations.
+  const uint32_t nmask = nibble_mask_v();
+  // Branch-free loads and products (clamped group index; the epilogue of a
+  // group past the end is skipped) so the compiler can keep kPre groups of
+  // loads in flight across iterations.
   for (int g0 = 0; g0 < G; g0 += kPre) {
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
       const int g = g0 + i;
       const int gc = min(g, G - 1);
-      const float on = g < G ? 1.f : 0.f;
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 2 * kb]);
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 2 * kb + 1]);
       const float* xs4 = gsum + gc * kTile + 4 * kb;
 #pragma unroll
       for (int t = 0; t < kGuTiles; ++t) {
-        f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg[i][t].x), zero, 0, 0, 0);
-        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg[i][t].y), tg, 0, 0, 0);
-        f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu[i][t].x), zero, 0, 0, 0);
-        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu[i][t].y), tu, 0, 0, 0);
-        group_epilogue(accg[t], tg, sg[i][t], xs4, on);
-        group_epilogue(accu[t], tu, su[i][t], xs4, on);
+        f32x4 tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wg[i][t].x, nmask), zero, 0, 0, 0);
+        tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wg[i][t].y, nmask), tg, 0, 0, 0);
+        f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu[i][t].x, nmask), zero, 0, 0, 0);
+        tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu[i][t].y, nmask), tu, 0, 0, 0);
+        if (g < G) {  // uniform: groups past the end (clamped loads) are dropped
+          group_epilogue(accg[t], tg, sg[i][t], xs4);
+          group_epilogue(accu[t], tu, su[i][t], xs4);
+        }
       }
       // refill this slot with group g + kPre, as one batch after this
       // group's products: slots then complete in order, so the next
@@ -545,20 +558,20 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   for (int t = 0; t < kDnTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const v4u* arow = as_lds + n * (W + 1);
+  const uint32_t nmask = nibble_mask_v();
   for (int g0 = 0; g0 < G; g0 += kDnPre) {
 #pragma unroll
     for (int i = 0; i < kDnPre; ++i) {
       const int g = g0 + i;
       const int gc = min(g, G - 1);
-      const float on = g < G ? 1.f : 0.f;
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 2 * kb]);
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, arow[gc * 8 + 2 * kb + 1]);
       const float* xs4 = gsum + gc * kTile + 4 * kb;
 #pragma unroll
       for (int t = 0; t < kDnTiles; ++t) {
-        f32x4 m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w[i][t].x), zero, 0, 0, 0);
-        m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w[i][t].y), m, 0, 0, 0);
-        group_epilogue(acc[t], m, sb[i][t], xs4, on);
+        f32x4 m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w[i][t].x, nmask), zero, 0, 0, 0);
+        m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w[i][t].y, nmask), m, 0, 0, 0);
+        if (g < G) group_epilogue(acc[t], m, sb[i][t], xs4);  // uniform: groups past the end are dropped
       }
       fetch(i, (uint32_t)min(g + kDnPre, G - 1));
     }
