@@ -173,6 +173,21 @@ typedef struct {
 moe_status moe_layer_forward_ex(const void* x, moe_layer* layer, void* out, int32_t n_tokens,
                                 const moe_fwd_opts* opts, void* stream);
 
+/* For callers that cannot allocate device memory during a call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * out[t] = MoE(x[t]) as moe_layer_forward with MOE_PATH_DECODE on a resident
+ * layer (same kernels, same results bit for bit), its per-call workspace
+ * (logits, routing, activations) taken from a device array of the library,
+ * 8 MiB per GPU, held until the process ends.  The call allocates nothing and
+ * calls no allocating routine; the caller passes x and out as for
+ * moe_layer_forward.  n_tokens is limited by the array: about 16 KB per token
+ * for the bf16 d_model 2816 / 128-expert / K 8 layer; larger calls fail with
+ * MOE_ERR_INVALID.  Every such call on one GPU shares the array, so calls
+ * that overlap on one GPU (different streams, not ordered) race and give
+ * undefined results.  Streamed layers: MOE_ERR_INVALID.  The layer's error
+ * flags (moe_layer_check_errors) report as for its other calls. */
+moe_status moe_layer_forward_noalloc(const void* x, moe_layer* layer, void* out, int32_t n_tokens, void* stream);
+
 /* Router + softmax top-K only: ids DEVICE int32 [T][K] (ascending per token),
  * w DEVICE fp32 [T][K]. */
 moe_status moe_layer_route(const void* x, moe_layer* layer, int32_t* ids, float* w, int32_t n_tokens,

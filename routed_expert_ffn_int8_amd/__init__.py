@@ -63,6 +63,7 @@ _SIGS = {
     "moe_layer_destroy": [_P],
     "moe_layer_forward": [_P, _P, _P, C.c_int32, _P],
     "moe_layer_forward_ex": [_P, _P, _P, C.c_int32, C.POINTER(moe_fwd_opts), _P],
+    "moe_layer_forward_noalloc": [_P, _P, _P, C.c_int32, _P],
     "moe_layer_route": [_P, _P, _P, _P, C.c_int32, _P],
     "moe_layer_sort": [_P, _P, C.c_int32, _P, _P, _P, _P, _P],
     "moe_layer_bytes": [_P, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)],
@@ -188,6 +189,10 @@ def moe_layer_forward(x, layer: int, out, n_tokens: int, stream=None):
 def moe_layer_forward_ex(x, layer: int, out, n_tokens: int, opts: moe_fwd_opts | None = None, stream=None):
     _check(load().moe_layer_forward_ex(_addr(x), layer, _addr(out), n_tokens,
                                        None if opts is None else C.byref(opts), _stream(stream)))
+
+
+def moe_layer_forward_noalloc(x, layer: int, out, n_tokens: int, stream=None):
+    _check(load().moe_layer_forward_noalloc(_addr(x), layer, _addr(out), n_tokens, _stream(stream)))
 
 
 def fwd_opts(topk_ids=None, topk_w=None, forced_ids=None, reuse_previous=0, path=MOE_PATH_AUTO,

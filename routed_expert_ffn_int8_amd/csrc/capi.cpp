@@ -955,6 +955,48 @@ moe_status moe_layer_forward(const void* x, moe_layer* L, void* out, int32_t n_t
   return moe_layer_forward_ex(x, L, out, n_tokens, nullptr, stream);
 }
 
+// Bytes of the allocation-free forward's workspace for T tokens: logits,
+// ids, coefficients, chosen blob addresses and the activation vectors.
+static size_t noalloc_bytes(const moe_layer* L, size_t T) {
+  const size_t K = L->K, F = (size_t)L->fs + K * L->f;
+  return align256(T * L->E * 4) + 2 * align256(T * K * 4) + align256(T * K * 8) +
+         align256(T * F * (L->act == MOE_ACT_BF16 ? 2 : 4));
+}
+
+moe_status moe_layer_forward_noalloc(const void* x, moe_layer* L, void* out, int32_t n_tokens, void* stream) {
+  if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
+  if (n_tokens == 0) return MOE_OK;
+  if (n_tokens < 0 || n_tokens > L->max_tokens)
+    return fail(MOE_ERR_INVALID, "n_tokens=%d not in 0..%d", n_tokens, L->max_tokens);
+  if (!x || !out) return fail(MOE_ERR_INVALID, "x/out is NULL");
+  if (x == out) return fail(MOE_ERR_INVALID, "x and out may not alias");
+  if (L->residency != MOE_RESIDENT) return fail(MOE_ERR_INVALID, "the allocation-free forward serves resident layers");
+  const size_t need = noalloc_bytes(L, (size_t)n_tokens);
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_ERR_INVALID, "%d tokens need %zu bytes of workspace; the allocation-free forward has %zu", n_tokens,
+                need, kNoAllocScratchBytes);
+  HIP_OK(hipSetDevice(L->dev));
+  void* base = nullptr;
+  HIP_OK(noalloc_scratch(&base));
+  LayerArgs a = base_args(L, x, out, n_tokens);
+  const size_t T = (size_t)n_tokens, K = L->K;
+  char* p = static_cast<char*>(base);
+  a.logits = reinterpret_cast<float*>(p);
+  p += align256(T * L->E * 4);
+  a.ids = reinterpret_cast<int32_t*>(p);
+  p += align256(T * K * 4);
+  a.wts = reinterpret_cast<float*>(p);
+  p += align256(T * K * 4);
+  a.sel_addr = reinterpret_cast<uint64_t*>(p);
+  p += align256(T * K * 8);
+  a.abuf = p;
+  a.counter = nullptr;  // the three-kernel path uses neither the fused kernel's counters ...
+  a.arep = nullptr;     // ... nor its copies
+  a.topk_in_gate_up = 1;
+  HIP_OK(launch_decode(a, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 moe_status moe_layer_route(const void* x, moe_layer* L, int32_t* ids, float* w, int32_t n_tokens, void* stream) {
   if (!L) return fail(MOE_ERR_INVALID, "layer is NULL");
   if (n_tokens == 0) return MOE_OK;

@@ -29,6 +29,7 @@
 // with fp16 (1024 + q) against fp16-rounded activations.  fp32 activations
 // use an exact byte->float convert and fp32 FMAs.
 #include <algorithm>
+#include <mutex>
 
 #include "device.hpp"
 #include "kernels.hpp"
@@ -1222,6 +1223,30 @@ size_t decode_lds_bytes_down(int F, int NI, int K, int act) { return down_lds_by
 bool decode_fused_ok(const LayerArgs& a) {
   return a.T == 1 && a.act == 1 && a.E <= 1024 && a.d <= 4096 && fused_lds_bytes(a) + 6 * 1024 <= 64 * 1024 &&
          a.fs / 64 <= 64 && a.K * (a.f / 64) <= 128;
+}
+
+// Workspace of the allocation-free forward (moe_layer_forward_noalloc): a
+// file-scope device array, one per GPU, held until the process ends.  Its
+// address is taken once per device (host code never uses the array's name as
+// an address) and handed to the kernels like any other workspace pointer.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s) {

@@ -96,6 +96,11 @@ enum : int32_t { kErrBadForcedId = 1, kErrMissingExpert = 2, kErrSyncTimeout = 4
 constexpr float kF16HandoffMax = 65504.f;
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s);
+// The allocation-free forward's workspace: a device array of this many bytes
+// per GPU; *ptr receives its address on the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void** ptr);
 // Dequantise one matrix of an expert blob from the device layout into fp32
 // out[rows][cols] = fma(scale, q, bias) (test hook).
 hipError_t launch_dequant(const uint8_t* blob, uint32_t q_off, uint32_t sb_off, int rows, int cols, float* out,
