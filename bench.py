@@ -567,6 +567,13 @@ def run_stream(args, M, torch, np):
         "h2d_bytes_per_token": tot["h2d_bytes"] / steps,
         "h2d_gbps_during_fills": round(tot["h2d_bytes"] / max(1, tot["h2d_ns"]), 2),
         "misses_per_token": tot["misses"] / steps,
+        # one-token calls compute their hits in kernels queued before the cache
+        # step (the device expert table marks them), the misses after the fill
+        "slots_computed_ahead_frac": round(tot["ahead_slots"] / (steps * w.layers * w.K), 4),
+        "fill_ms_per_token": round(tot["h2d_ns"] / steps / 1e6, 4),
+        # step time above the resident layers on the same kernels: the host
+        # hand-off of every layer plus the fill time not overlapped
+        "exposed_ms_per_token": round(1e3 / out["streamed"] - 1e3 / out["resident_split"], 4),
         "streamed_equals_resident_same_path": bool(torch.equal(finals["resident_split"], finals["streamed"])),
         "lru_shared_pool": {
             "policy": "one LRU cache over (layer, expert), budget = 40 x 16 expert slots",

@@ -27,8 +27,8 @@
  *    objects may be used concurrently on distinct streams.
  *  - Calls on one object must run in order on the GPU (one stream, or streams
  *    ordered with events): every call reuses the object's device workspace
- *    (routing, activations, the fused kernel's counters, the verdict word of
- *    a streamed call).
+ *    (routing, activations, the fused kernel's counters, a streamed layer's
+ *    expert table and slots).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -138,12 +138,14 @@ moe_status moe_layer_destroy(moe_layer* layer);
  * n_tokens: 0..max_tokens (0 is a no-op).
  * Resident layers: only enqueues work on `stream`.  Streamed layers: blocks
  * the calling thread until the routing of this call is known on the host,
- * then enqueues the cache fills and compute.  With one token the top-K kernel
- * writes the routing into pinned host memory and the thread spins on it (up
- * to about 2 s, then it waits for the stream); the expert kernels are then
- * already enqueued and run as soon as the host reports that every chosen
- * expert was cached, or are skipped and enqueued again behind the fills.
- * More tokens: one small device->host copy and a stream synchronisation. */
+ * then enqueues the cache fills and the compute that needs them.  With one
+ * token (top_k <= 32) the router, routed gate/up and down kernels are all
+ * enqueued first: the gate/up launch runs the top-K, writes the routing into
+ * pinned host memory (the thread spins on it, up to about 2 s, then waits for
+ * the stream) and computes the experts that are cached; the down kernel runs
+ * when all were.  A miss then costs a fill kernel, a gate/up launch for the
+ * missed experts and the down kernel again.  More tokens: one small
+ * device->host copy and a stream synchronisation. */
 moe_status moe_layer_forward(const void* x, moe_layer* layer, void* out, int32_t n_tokens, void* stream);
 
 /* Optional controls of one forward call.  Every field may be 0/NULL. */
@@ -210,8 +212,7 @@ moe_status moe_layer_bytes(const moe_layer* layer, uint64_t* device_bytes, uint6
  *   bit 0  a forced expert id was outside 0..E-1 (it was replaced by 0);
  *   bit 1  a chosen expert was not resident (its output read as zero);
  *   bit 2  a workgroup gave up waiting for another one's results: a bounded
- *          wait of the fused kernel, or of expert kernels launched ahead of a
- *          streamed call's cache step, ran out (seconds; for example when
+ *          wait of the fused kernel ran out (seconds; for example when
  *          another process holds most of the GPU);
  *   bit 3  an intermediate activation |silu(gate.x) * up.x| reached 65504,
  *          the largest fp16 value: bf16 layers on the DECODE and FUSED paths
@@ -219,8 +220,7 @@ moe_status moe_layer_bytes(const moe_layer* layer, uint64_t* device_bytes, uint6
  *          outside their range (the PREFILL path keeps them in bf16).
  * Any set bit means the output of some call since the last check is not
  * valid.  The forward calls return MOE_OK without waiting for the GPU, so
- * MOE_OK from a FUSED call, or from a streamed call whose expert kernels
- * were launched ahead, does not prove that its output is valid: check the
+ * MOE_OK from a call does not prove that its output is valid: check the
  * flags after the calls whose outputs matter. */
 moe_status moe_layer_check_errors(moe_layer* layer, int32_t* flags);
 
@@ -262,14 +262,17 @@ moe_status moe_layer_profile_read(moe_layer* layer, int64_t* launches, double* t
  * one to the entry's count; a miss takes the lowest empty slot, else evicts
  * the entry with the least (count, last-used tick, slot) among entries not
  * chosen by the current call; a new entry starts at count 1; counts are
- * never aged.  Fills are hipMemcpyAsync from pinned host memory on a side
- * stream, ordered before the expert kernels by events. */
+ * never aged.  Fills are copy kernels on the call's stream that read the
+ * pinned host store over the host link (about 50 GB/s; DMA copies measured
+ * 43 GB/s on one stream and far less on two) and write the slots and the
+ * layer's device expert table. */
 
 /* Allocates n_slots HBM slots (n_slots >= top_k * max_tokens is not required;
  * n_slots >= the number of distinct experts a single call can choose is:
- * calls needing more return MOE_ERR_STATE).  side_stream may be NULL, in which
- * case the library creates one.  Errors: MOE_ERR_STATE if the layer is not
- * MOE_STREAMED or already has a cache. */
+ * calls needing more return MOE_ERR_STATE).  side_stream carries the
+ * fetch-ahead copies (moe_cache_prefetch, moe_stack_set_prefetch); it may be
+ * NULL, in which case the library creates one.  Errors: MOE_ERR_STATE if the
+ * layer is not MOE_STREAMED or already has a cache. */
 moe_status moe_cache_attach(moe_layer* layer, int32_t n_slots, void* side_stream);
 
 typedef struct {
@@ -278,9 +281,12 @@ typedef struct {
   uint64_t misses;
   uint64_t evictions;  /* entries replaced (by a miss or a prefetch) */
   uint64_t h2d_bytes;  /* (misses + prefetches) * expert bytes */
-  uint64_t h2d_ns;     /* wall time of the fills, host clock, summed */
+  uint64_t h2d_ns;     /* span of each call's fills, first copy start to last copy end (GPU event
+                          clock), summed */
   uint64_t prefetches;    /* experts placed ahead of use (moe_cache_prefetch) */
   uint64_t prefetch_used; /* of those, the ones a call then hit */
+  uint64_t ahead_slots;   /* one-token calls: routed slots computed by the kernels queued before the
+                             call's cache step (its hits, which the device expert table marks) */
 } moe_cache_stats;
 
 moe_status moe_cache_stats_get(const moe_layer* layer, moe_cache_stats* out);
@@ -313,12 +319,11 @@ moe_status moe_cache_prefetch(moe_layer* layer, const int32_t* experts, int32_t 
  * size).  Policy: a call's hits are touched first; each miss takes the
  * lowest empty slot, else evicts the entry (of any layer) with the oldest
  * last use, lower slot first on ties, never an entry chosen by the same
- * call; misses are placed in ascending expert order.  Fills are
- * hipMemcpyAsync from the layer's pinned store on the pool's side stream,
- * ordered before the expert kernels by events, as for per-layer caches.
- * Layers sharing a pool must be called from one stream (or calls ordered),
- * since a call may refill a slot another layer used last.  side_stream may
- * be NULL (the pool creates one). */
+ * call; misses are placed in ascending expert order.  Fills are copy
+ * kernels on the call's stream, as for per-layer caches.  Layers sharing a
+ * pool must be called from one stream (or calls ordered), since a call may
+ * refill a slot another layer used last.  The pool does no fetch-ahead:
+ * side_stream is accepted for symmetry with moe_cache_attach and not used. */
 moe_status moe_cache_pool_create(uint64_t budget_bytes, uint64_t expert_bytes, void* side_stream,
                                  moe_cache_pool** out);
 /* The layers that use it keep running only after another cache is

@@ -51,7 +51,7 @@ class moe_fwd_opts(C.Structure):
 
 class moe_cache_stats(C.Structure):
     _fields_ = [(n, C.c_uint64) for n in ("accesses", "hits", "misses", "evictions", "h2d_bytes", "h2d_ns",
-                                          "prefetches", "prefetch_used")]
+                                          "prefetches", "prefetch_used", "ahead_slots")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}

@@ -122,6 +122,7 @@ struct moe_layer {
   int fused_ok = -1;  // whether the single-launch decode kernel serves this layer here (-1: not yet known)
   // streamed experts
   uint8_t* h_store = nullptr;  // pinned, E blobs
+  const uint8_t* d_store = nullptr;  // its device view
   uint8_t* d_slots = nullptr;
   int n_slots = 0;
   std::unique_ptr<LfuPolicy> lfu;
@@ -129,8 +130,6 @@ struct moe_layer {
   int pool_id = -1;                // this layer's key in it
   hipStream_t side = nullptr;
   bool own_side = false;
-  hipStream_t side2 = nullptr;   // a second fill stream (own LFU cache): a call's fills alternate
-  hipEvent_t ev_fill2 = nullptr;  // between the two, so that two copy engines share them
   hipEvent_t ev_fill = nullptr, ev_fill_start = nullptr;
   bool fill_pending = false;
   hipEvent_t ev_ahead = nullptr;  // after the last prefetch's copies
@@ -142,13 +141,11 @@ struct moe_layer {
   void* d_host_ids = nullptr;  // its device view
   uint32_t host_seq = 0;       // sequence number of the last one-token routing written by the GPU
   int64_t host_wait_us = 2000000;  // how long the host spins for that routing before it waits for the stream
-  uint32_t* d_go = nullptr;    // device copy of the verdict word of a call launched ahead
   int32_t* h_pf = nullptr;     // prefill through the cache: pinned counts [E], then group tile lists
   int32_t* d_pf_tiles = nullptr;  // the group tile lists on the device
   size_t pf_ints = 0;          // capacity of both lists, in ints
   uint64_t* h_pf_addr = nullptr;  // pinned snapshots of the expert table, one per group of a chunk
   size_t pf_groups = 0;           // their count
-  hipEvent_t ev_pf = nullptr;  // a prefill group's GEMMs are done (its slots may be refilled)
   std::vector<char> fail_expert;
   moe_cache_stats stats{};
   uint64_t device_bytes = 0;
@@ -192,8 +189,6 @@ struct moe_cache_pool {
   uint64_t expert_bytes = 0;
   int n_slots = 0;
   uint8_t* d_slots = nullptr;
-  hipStream_t side = nullptr;
-  bool own_side = false;
   std::unique_ptr<LruPool> policy;
   std::vector<moe_layer*> members;  // by key; null once a layer has left
   moe_cache_stats stats{};
@@ -293,14 +288,10 @@ void free_layer(moe_layer* L) {
   if (L->h_pf) (void)hipHostFree(L->h_pf);
   if (L->h_pf_addr) (void)hipHostFree(L->h_pf_addr);
   (void)hipFree(L->d_pf_tiles);
-  if (L->ev_pf) (void)hipEventDestroy(L->ev_pf);
-  (void)hipFree(L->d_go);
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
   if (L->ev_fill_start) (void)hipEventDestroy(L->ev_fill_start);
   if (L->ev_ahead) (void)hipEventDestroy(L->ev_ahead);
   if (L->own_side && L->side) (void)hipStreamDestroy(L->side);
-  if (L->side2) (void)hipStreamDestroy(L->side2);
-  if (L->ev_fill2) (void)hipEventDestroy(L->ev_fill2);
   delete L;
 }
 
@@ -336,6 +327,9 @@ moe_status create_impl(const moe_layer_desc* D, moe_layer* L) {
     if (hipHostMalloc(reinterpret_cast<void**>(&L->h_store), E * stride, hipHostMallocDefault) != hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned host store of %zu bytes failed", E * stride);
     pack_parallel(D, L->rl, L->h_store);
+    void* dv = nullptr;  // the fill kernel reads the store through its device view
+    HIP_OK(hipHostGetDevicePointer(&dv, L->h_store, 0));
+    L->d_store = static_cast<const uint8_t*>(dv);
     // pinned mirror of the device expert table [E]
     if (hipHostMalloc(reinterpret_cast<void**>(&L->h_addr), E * 8, hipHostMallocDefault) != hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned expert table failed");
@@ -461,18 +455,24 @@ moe_status prefetch_impl(moe_layer* L, const int32_t* experts, int n, hipEvent_t
   return MOE_OK;
 }
 
+// Add the last call's fill time to the layer's counters; its events must be
+// complete.
+void account_fills(moe_layer* L) {
+  if (!L->fill_pending) return;
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, L->ev_fill_start, L->ev_fill) == hipSuccess) L->stats.h2d_ns += (uint64_t)(ms * 1e6);
+  L->fill_pending = false;
+}
+
 // Byte offset of the sequence word behind the routing copy in h_ids.
 size_t host_flag_offset(const moe_layer* L) { return ((size_t)L->max_tokens * L->K * 4 + 63) / 64 * 64; }
 
-// The verdict word of a call whose routed and down kernels were launched
-// before the cache step (its own 64-byte line after the sequence word):
-// 2*seq to run them, 2*seq+1 to skip them.
-uint32_t* go_word(const moe_layer* L) {
-  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(L->h_ids) + host_flag_offset(L) + 64);
-}
-void set_go(const moe_layer* L, uint32_t seq, bool run) {
-  __atomic_store_n(go_word(L), 2u * seq + (run ? 0u : 1u), __ATOMIC_RELEASE);
-}
+// A one-token call of a streamed layer computes its hits in kernels queued
+// before the cache step (the device table marks them); its misses are
+// computed after the fill kernel, on the same stream.
+struct SlotPlan {
+  uint32_t late = 0;  // slots of the missed experts
+};
 
 // Spin until the GPU has written `seq` behind the routing in h_ids (at most
 // the layer's host_wait_us, 2 s unless a test shortened it); true when it has.
@@ -507,25 +507,17 @@ std::vector<int32_t> predict_next(const moe_layer* L, int depth) {
 // router has run on `stream`.  Blocks on the routing copy: once it is back,
 // everything queued earlier on `stream` is done, so no slot about to be
 // refilled is still being read.  (A one-token call instead spins until the
-// top-K kernel has published the routing: stream order then also puts every
-// earlier command of the stream behind it.)
+// routed gate/up's top-K workgroup has published the routing: stream order
+// puts every earlier command of the stream behind it, and the call's own
+// kernels read only the slots of chosen experts, which the step never
+// refills.)
 moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = nullptr, int depth = 0,
-                     uint32_t seq = 0, int* verdict = nullptr) {
+                     uint32_t seq = 0, SlotPlan* plan = nullptr) {
   moe_cache_pool* P = L->pool;
   if (!L->lfu && !P) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
   const size_t n = (size_t)T * L->K;
-  bool verdict_given = false;
   if (seq) {  // one token: the top-K kernel writes the ids and then seq into host memory
     if (!wait_host_flag(L, seq)) {  // not within the time limit: the stream's own status decides
-      // Expert kernels launched ahead on `stream` wait for this call's
-      // verdict, so the synchronisation below would wait for them until their
-      // own bounded waits ran out.  They are told to skip first; the call then
-      // runs them again behind its fills, as after a miss.
-      if (verdict) {
-        set_go(L, seq, false);
-        *verdict = 0;
-        verdict_given = true;
-      }
       HIP_OK(hipStreamSynchronize(stream));
       if (!wait_host_flag(L, seq)) return fail(MOE_ERR_STATE, "the routing of the call did not reach the host");
     }
@@ -533,11 +525,7 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
     HIP_OK(hipMemcpyAsync(L->h_ids, L->d_ids, n * 4, hipMemcpyDeviceToHost, stream));
     HIP_OK(hipStreamSynchronize(stream));
   }
-  if (L->fill_pending) {  // account the previous call's fills (complete by now)
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, L->ev_fill_start, L->ev_fill) == hipSuccess) L->stats.h2d_ns += (uint64_t)(ms * 1e6);
-    L->fill_pending = false;
-  }
+  account_fills(L);  // the previous call's (complete by now)
   if (L->ahead_pending) {  // this call may use what was fetched ahead
     HIP_OK(hipStreamWaitEvent(stream, L->ev_ahead, 0));
     L->ahead_pending = false;
@@ -558,41 +546,51 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
     P->policy->step(L->pool_id, chosen.data(), m, slot.data(), miss.data(), ev_layer.data(), ev_expert.data());
   else
     L->lfu->step(chosen.data(), m, slot.data(), miss.data(), ev_expert.data());
-  if (verdict && !verdict_given) {  // kernels launched ahead: they run now when every chosen expert was a hit
-    bool any_miss = false;
-    for (int i = 0; i < m; ++i) any_miss |= miss[i] != 0;
-    set_go(L, seq, !any_miss);
-    *verdict = any_miss ? 0 : 1;
+  // One token: slot k holds expert h_ids[k] (chosen[] is those ids sorted,
+  // without repeats).  The hits were computed by the kernels queued ahead.
+  std::vector<uint32_t> slots_of(m, 0u);
+  if (plan) {
+    uint32_t hits = 0;
+    for (int k = 0; k < L->K; ++k) {
+      const int i = (int)(std::lower_bound(chosen.begin(), chosen.end(), L->h_ids[k]) - chosen.begin());
+      slots_of[i] |= 1u << k;
+      if (!miss[i]) hits |= 1u << k;
+    }
+    L->stats.ahead_slots += (uint64_t)__builtin_popcount(hits);
+    if (P) P->stats.ahead_slots += (uint64_t)__builtin_popcount(hits);
   }
   const size_t stride = L->rl.stride;
   uint8_t* base = P ? P->d_slots : L->d_slots;
-  hipStream_t side = P ? P->side : L->side;
-  hipStream_t side2 = P ? nullptr : L->side2;
-  bool any = false, any2 = false;
-  int nfill = 0;
+  // The misses are filled by copy kernels on `stream` (kMaxFills blobs per
+  // launch), which also write the layer's table entries: the expert kernels
+  // that follow on the stream see both.
+  FillArgs fa{};
+  fa.bytes = stride;
+  fa.table = L->d_expert_addr;
+  bool any = false;
   uint64_t h2d = 0;
   for (int i = 0; i < m; ++i) {
     if (!miss[i]) continue;
-    if (!any) HIP_OK(hipEventRecord(L->ev_fill_start, side));
+    if (!any) HIP_OK(hipEventRecord(L->ev_fill_start, stream));
     any = true;
     uint8_t* dst = base + (size_t)slot[i] * stride;
-    const bool second = side2 && (nfill++ & 1);
-    if (second && !any2) {  // starts no earlier than the first stream's fills
-      HIP_OK(hipEventRecord(L->ev_fill2, side));
-      HIP_OK(hipStreamWaitEvent(side2, L->ev_fill2, 0));
+    moe_layer* owner = nullptr;  // the layer whose entry the fill evicts (another one's, for a pool)
+    if (ev_expert[i] >= 0) owner = P ? (ev_layer[i] >= 0 ? P->members[ev_layer[i]] : nullptr) : L;
+    if (fa.n == kMaxFills) {
+      HIP_OK(launch_fill(fa, stream));
+      fa.n = 0;
     }
-    any2 |= second;
-    HIP_OK(hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice,
-                          second ? side2 : side));
-    if (ev_expert[i] >= 0) {  // the slot's previous entry (of this layer, or of another for a pool)
-      moe_layer* owner = P ? (ev_layer[i] >= 0 ? P->members[ev_layer[i]] : nullptr) : L;
-      if (owner) {  // that layer re-uploads its table on its next call
-        owner->h_addr[ev_expert[i]] = 0;
-        owner->addr_dirty = true;
-      }
+    fa.src[fa.n] = L->d_store + (size_t)chosen[i] * stride;
+    fa.dst[fa.n] = dst;
+    fa.expert[fa.n] = chosen[i];
+    fa.evicted[fa.n] = owner == L ? ev_expert[i] : -1;
+    ++fa.n;
+    if (plan) plan->late |= slots_of[i];
+    if (owner) {  // the kernel clears this layer's entry; another layer re-uploads its table on its next call
+      owner->h_addr[ev_expert[i]] = 0;
+      if (owner != L) owner->addr_dirty = true;
     }
     L->h_addr[chosen[i]] = reinterpret_cast<uint64_t>(dst);
-    L->addr_dirty = true;
     h2d += stride;
   }
   if (P) {  // this layer's share of the pool's counts
@@ -621,12 +619,8 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
   if (L->hist.empty()) L->hist.assign(L->E, 0);
   for (int32_t e : chosen) ++L->hist[e];
   if (any) {
-    if (any2) {  // the second stream's fills, then the first's event covers both
-      HIP_OK(hipEventRecord(L->ev_fill2, side2));
-      HIP_OK(hipStreamWaitEvent(side, L->ev_fill2, 0));
-    }
-    HIP_OK(hipEventRecord(L->ev_fill, side));
-    HIP_OK(hipStreamWaitEvent(stream, L->ev_fill, 0));
+    HIP_OK(launch_fill(fa, stream));
+    HIP_OK(hipEventRecord(L->ev_fill, stream));
     L->fill_pending = true;
   }
   if (next && depth > 0 && next->lfu) {  // fetch ahead for the next layer, behind this layer's fills
@@ -635,10 +629,11 @@ moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = 
     if (st != MOE_OK) return st;
   }
   // The routed kernel reads each chosen expert's address from the device
-  // table, so the table goes up only when a fill, a fetch-ahead or another
-  // layer's eviction changed it (the stream was synchronised above, so no
-  // earlier upload of h_addr is still pending).
-  if (L->addr_dirty) {
+  // table; the fill kernels wrote this call's entries, so the table goes up
+  // only when a fetch-ahead or another layer's eviction changed it (the
+  // stream was synchronised above, so no earlier upload of h_addr is still
+  // pending).
+  if (L->addr_dirty && !plan) {
     HIP_OK(hipMemcpyAsync(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice, stream));
     L->addr_dirty = false;
   }
@@ -707,41 +702,57 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
   if (L->residency == MOE_STREAMED) {
     LayerArgs a1 = a;
     a1.stages = kStageRouter | kStageShared;
-    uint32_t seq = 0;
-    if (T == 1 && L->d_host_ids) {
-      seq = ++L->host_seq;
-      if (seq >= (1u << 30)) seq = L->host_seq = 1;  // 0 means "no flag"; the verdict word holds 2*seq+1
-      a1.host_ids = static_cast<int32_t*>(L->d_host_ids);
-      a1.host_flag = reinterpret_cast<uint32_t*>(static_cast<char*>(L->d_host_ids) + host_flag_offset(L));
-      a1.host_seq = seq;
-    }
-    HIP_OK(launch_decode(a1, s));
     LayerArgs a2 = a;
     a2.stages = kStageRouted | kStageDown;
     a2.sel_from_table = 1;
-    // One token and an up-to-date device table: the routed and down kernels
-    // go out now and wait on the GPU for the host's verdict, so their launch
-    // overlaps the routing hand-off and the cache step.  A call with a miss
-    // skips them and runs them again behind its fills.
-    const bool ahead = seq != 0 && !L->addr_dirty;
-    if (ahead) {
-      if (L->ahead_pending) {  // fetched-ahead copies land before these kernels read their slots
+    // One token: three launches are queued at once, before the cache step:
+    // the router; the routed gate/up, whose first workgroup runs the top-K and
+    // hands the routing to the host through host memory, with the shared
+    // expert's gate/up in the same launch; the down kernel.  The device table
+    // holds exactly the cache's contents (it is brought up to date first), so
+    // those kernels compute the hits without waiting for the host.  The host
+    // launches each miss behind its own fill and the down kernel again after
+    // the last; with no miss it launches nothing more.
+    const bool one = T == 1 && L->d_host_ids && L->K <= 32;
+    uint32_t seq = 0;
+    if (one) {
+      seq = ++L->host_seq;
+      if (seq >= (1u << 30)) seq = L->host_seq = 1;  // 0 means "no flag"
+      a1.stages = kStageRouter;
+      a1.topk_in_gate_up = 1;  // no top-K kernel after the router
+      if (L->addr_dirty) {  // a fetch-ahead or another layer's eviction changed it since the last upload
+        HIP_OK(hipMemcpyAsync(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice, s));
+        L->addr_dirty = false;
+      }
+    }
+    HIP_OK(launch_decode(a1, s));
+    if (one) {
+      if (L->ahead_pending) {  // fetched-ahead copies land before the expert kernels read their slots
         HIP_OK(hipStreamWaitEvent(s, L->ev_ahead, 0));
         L->ahead_pending = false;
       }
       LayerArgs a3 = a2;
-      a3.go_host = reinterpret_cast<const uint32_t*>(static_cast<char*>(L->d_host_ids) + host_flag_offset(L) + 64);
-      a3.go_dev = L->d_go;
+      a3.hits_only = 1;
+      a3.shared_in_routed = 1;
+      a3.topk_in_gate_up = 1;
+      a3.host_ids = static_cast<int32_t*>(L->d_host_ids);
+      a3.host_flag = reinterpret_cast<uint32_t*>(static_cast<char*>(L->d_host_ids) + host_flag_offset(L));
       a3.host_seq = seq;
       HIP_OK(launch_decode(a3, s));
     }
-    int verdict = -1;
-    moe_status st = stream_in(L, T, s, next, depth, seq, ahead ? &verdict : nullptr);
-    if (st != MOE_OK) {
-      if (ahead && verdict < 0) set_go(L, seq, false);
-      return st;
+    SlotPlan plan;
+    moe_status st = stream_in(L, T, s, next, depth, seq, one ? &plan : nullptr);
+    if (st != MOE_OK) return st;
+    if (!one) {
+      HIP_OK(launch_decode(a2, s));
+    } else if (plan.late) {  // behind the fill kernel on the stream
+      a2.stages = kStageRouted;
+      a2.run_mask = plan.late;
+      HIP_OK(launch_decode(a2, s));
+      a2.stages = kStageDown;
+      a2.run_mask = 0;
+      HIP_OK(launch_decode(a2, s));
     }
-    if (verdict != 1) HIP_OK(launch_decode(a2, s));
   } else {
     a.topk_in_gate_up = 1;
     HIP_OK(launch_decode(a, s));
@@ -829,28 +840,29 @@ struct StreamPrefill final : PrefillStreamer {
     std::vector<int32_t> slot(m), miss(m), ev_expert(m, -1);
     if (m > 0) L->lfu->step(chosen.data(), m, slot.data(), miss.data(), ev_expert.data());
     const size_t stride = L->rl.stride;
-    bool any = false, any2 = false;
-    int nfill = 0;
+    // Fill kernels on the chunk's stream (after the previous group's GEMMs,
+    // whose slots they may reuse); they also write the table entries.
+    FillArgs fa{};
+    fa.bytes = stride;
+    fa.table = L->d_expert_addr;
     hipError_t e = hipSuccess;
     for (int i = 0; i < m; ++i) {
       if (!miss[i]) continue;
-      if (!any && gi > 0 && (e = hipStreamWaitEvent(L->side, L->ev_pf, 0)) != hipSuccess) return e;
-      any = true;
-      const bool second = nfill++ & 1;
-      if (second && !any2) {  // the second stream starts behind the first one's wait
-        if ((e = hipEventRecord(L->ev_fill2, L->side)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(L->side2, L->ev_fill2, 0)) != hipSuccess) return e;
+      if (fa.n == kMaxFills) {
+        if ((e = launch_fill(fa, s)) != hipSuccess) return e;
+        fa.n = 0;
       }
-      any2 |= second;
       uint8_t* dst = L->d_slots + (size_t)slot[i] * stride;
-      e = hipMemcpyAsync(dst, L->h_store + (size_t)chosen[i] * stride, stride, hipMemcpyHostToDevice,
-                         second ? L->side2 : L->side);
-      if (e != hipSuccess) return e;
+      fa.src[fa.n] = L->d_store + (size_t)chosen[i] * stride;
+      fa.dst[fa.n] = dst;
+      fa.expert[fa.n] = chosen[i];
+      fa.evicted[fa.n] = ev_expert[i];
+      ++fa.n;
       if (ev_expert[i] >= 0) L->h_addr[ev_expert[i]] = 0;
       L->h_addr[chosen[i]] = reinterpret_cast<uint64_t>(dst);
-      L->addr_dirty = true;
       L->stats.h2d_bytes += stride;
     }
+    if ((e = launch_fill(fa, s)) != hipSuccess) return e;
     L->stats.accesses = L->lfu->accesses;
     L->stats.hits = L->lfu->hits;
     L->stats.misses = L->lfu->misses;
@@ -858,15 +870,7 @@ struct StreamPrefill final : PrefillStreamer {
     L->stats.prefetch_used = L->lfu->prefetch_used;
     if (L->hist.empty()) L->hist.assign(L->E, 0);
     for (int32_t x : chosen) ++L->hist[x];
-    if (any) {
-      if (any2) {
-        if ((e = hipEventRecord(L->ev_fill2, L->side2)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(L->side, L->ev_fill2, 0)) != hipSuccess) return e;
-      }
-      if ((e = hipEventRecord(L->ev_fill, L->side)) != hipSuccess) return e;
-      if ((e = hipStreamWaitEvent(s, L->ev_fill, 0)) != hipSuccess) return e;
-    }
-    if (L->addr_dirty) {
+    if (L->addr_dirty) {  // a fetch-ahead changed it before this chunk
       // from a snapshot of its own: the host takes the next group's step
       // (and changes h_addr) before this copy runs
       if ((size_t)gi >= L->pf_groups) return hipErrorInvalidValue;  // cannot happen: sized for every group
@@ -880,7 +884,7 @@ struct StreamPrefill final : PrefillStreamer {
     return hipSuccess;
   }
 
-  hipError_t done(int, hipStream_t s) override { return hipEventRecord(L->ev_pf, s); }
+  hipError_t done(int, hipStream_t) override { return hipSuccess; }
 };
 
 moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_opts* o, hipStream_t s) {
@@ -905,7 +909,6 @@ moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_o
     if (hipHostMalloc(reinterpret_cast<void**>(&L->h_pf_addr), L->pf_groups * L->E * 8, hipHostMallocDefault) !=
         hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned table snapshots failed");
-    HIP_OK(hipEventCreateWithFlags(&L->ev_pf, hipEventDisableTiming));
   }
   StreamPrefill sp(L);
   p.streamer = &sp;
@@ -1130,16 +1133,12 @@ namespace {
 // Routing copy and fill events of a streamed layer that gets a cache.
 moe_status cache_common(moe_layer* L) {
   if (!L->h_ids) {  // coherent, so the top-K kernel can write a one-token routing straight into it
-    const size_t bytes = host_flag_offset(L) + 128;  // + the sequence word, + the verdict word
+    const size_t bytes = host_flag_offset(L) + 64;  // + the sequence word
     if (hipHostMalloc(reinterpret_cast<void**>(&L->h_ids), bytes, hipHostMallocCoherent | hipHostMallocMapped) !=
         hipSuccess)
       return fail(MOE_ERR_NOMEM, "pinned routing buffer failed");
     std::memset(L->h_ids, 0, bytes);
     HIP_OK(hipHostGetDevicePointer(&L->d_host_ids, L->h_ids, 0));
-  }
-  if (!L->d_go) {
-    if (dalloc(&L->d_go, 256) != hipSuccess) return fail(MOE_ERR_NOMEM, "verdict word alloc failed");
-    HIP_OK(hipMemset(L->d_go, 0, 256));
   }
   if (!L->ev_fill) HIP_OK(hipEventCreate(&L->ev_fill));
   if (!L->ev_fill_start) HIP_OK(hipEventCreate(&L->ev_fill_start));
@@ -1171,8 +1170,6 @@ moe_status moe_cache_attach(moe_layer* L, int32_t n_slots, void* side_stream) {
     HIP_OK(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
     L->own_side = true;
   }
-  if (!L->side2) HIP_OK(hipStreamCreateWithFlags(&L->side2, hipStreamNonBlocking));
-  if (!L->ev_fill2) HIP_OK(hipEventCreateWithFlags(&L->ev_fill2, hipEventDisableTiming));
   L->n_slots = n_slots;
   L->lfu.reset(new LfuPolicy(n_slots));
   L->device_bytes += bytes;
@@ -1193,14 +1190,7 @@ moe_status moe_cache_pool_create(uint64_t budget_bytes, uint64_t expert_bytes, v
   P->n_slots = (int)(budget_bytes / expert_bytes);
   if (dalloc(&P->d_slots, (size_t)P->n_slots * expert_bytes) != hipSuccess)
     return fail(MOE_ERR_NOMEM, "slot pool of %llu bytes failed", (unsigned long long)budget_bytes);
-  if (side_stream) {
-    P->side = static_cast<hipStream_t>(side_stream);
-  } else if (hipStreamCreateWithFlags(&P->side, hipStreamNonBlocking) != hipSuccess) {
-    (void)hipFree(P->d_slots);
-    return fail(MOE_ERR_HIP, "side stream creation failed");
-  } else {
-    P->own_side = true;
-  }
+  (void)side_stream;  // fills run on the calls' streams; the pool fetches nothing ahead
   P->policy.reset(new LruPool(P->n_slots));
   *out = P.release();
   return MOE_OK;
@@ -1217,7 +1207,6 @@ moe_status moe_cache_pool_destroy(moe_cache_pool* P) {
       (void)clear_addresses(L);
     }
   (void)hipFree(P->d_slots);
-  if (P->own_side && P->side) (void)hipStreamDestroy(P->side);
   delete P;
   return MOE_OK;
 }
@@ -1258,8 +1247,6 @@ moe_status moe_cache_detach(moe_layer* L) {
     if (L->own_side && L->side) (void)hipStreamDestroy(L->side);
     L->side = nullptr;
     L->own_side = false;
-    if (L->side2) (void)hipStreamDestroy(L->side2);
-    L->side2 = nullptr;
   }
   L->fill_pending = false;
   L->ahead_pending = false;
@@ -1308,9 +1295,7 @@ moe_status moe_cache_stats_get(const moe_layer* L, moe_cache_stats* out) {
   moe_layer* M = const_cast<moe_layer*>(L);
   if (M->fill_pending) {
     HIP_OK(hipEventSynchronize(M->ev_fill));
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, M->ev_fill_start, M->ev_fill) == hipSuccess) M->stats.h2d_ns += (uint64_t)(ms * 1e6);
-    M->fill_pending = false;
+    account_fills(M);
   }
   *out = L->stats;
   return MOE_OK;

@@ -421,12 +421,18 @@ __device__ float router_row(const LayerArgs& a, int t, int e, const XStage& S) {
   return fmaf(s, acc, b);
 }
 
+// Workgroups of the router part of a route_shared launch (none when the
+// launch runs the shared gate/up alone).
+__host__ __device__ inline int route_blocks(const LayerArgs& a) {
+  return (a.stages == 0 || (a.stages & kStageRouter)) ? (a.E + kWaves - 1) / kWaves : 0;
+}
+
 template <int ACT, int MAXI>
 __global__ __launch_bounds__(kThreads) void route_shared_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const XStage S = carve_x(smem, a.d);
   const int t = blockIdx.y;
-  const int NR = (a.E + kWaves - 1) / kWaves;  // one router row per wavefront
+  const int NR = route_blocks(a);  // one router row per wavefront
   if ((int)blockIdx.x >= NR) {
     XRegs xr;
     x_issue<ACT>(a, t, xr);
@@ -449,45 +455,20 @@ __global__ __launch_bounds__(64) void topk_kernel(LayerArgs a) {
   float w;
   topk_wave<NE>(a, blockIdx.x, s_logits, &id, &w, scratch);
   publish_routing(a, blockIdx.x, threadIdx.x, id, w);
-  if (a.host_ids) {  // one token (one workgroup): its ids into host memory, then the sequence number
-    if (threadIdx.x < a.K)
-      __hip_atomic_store(a.host_ids + threadIdx.x, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(a.host_flag, a.host_seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
 }
 
 // ---------------------------------------------------------------- kernel B
-// Kernels launched before the host has run the cache step of the call wait
-// for its verdict: block 0 polls the host's word (over the host link, one
-// lane, one load in flight) and relays it into device memory, where the
-// other blocks poll it.  Bounded: a wait that runs out sets the error flag and
-// skips.  Returns true to run the call, false to skip it.
-constexpr uint32_t kGoSpinLimit = 1u << 21;  // relay polls (about 1.5 us each); the others poll 2x as often
-__device__ bool wait_go(const LayerArgs& a) {
-  __shared__ uint32_t s_go;
-  const uint32_t run = 2u * a.host_seq;
-  if (threadIdx.x == 0) {
-    const bool relay = blockIdx.x == 0 && blockIdx.y == 0;
-    uint32_t v = 0;
-    for (uint32_t it = 0;; ++it) {
-      v = relay ? __hip_atomic_load(a.go_host, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
-                : __hip_atomic_load(a.go_dev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((v >> 1) == a.host_seq) break;
-      if (it == (relay ? kGoSpinLimit : 2 * kGoSpinLimit)) {
-        atomicOr(a.err, kErrSyncTimeout);
-        v = run + 1;
-        break;
-      }
-      if (!relay) __builtin_amdgcn_s_sleep(1);  // the relay's own load is a host-link round trip
-    }
-    if (relay) __hip_atomic_store(a.go_dev, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_go = v;
-  }
-  __syncthreads();
-  return s_go == run;
-}
-
+// Routed gate/up, workgroups in this order:
+//   - with the top-K done here (topk_in_gate_up): one workgroup that runs it
+//     for the token and publishes ids, weights and chosen addresses for the
+//     down kernel (and, for a one-token streamed call, the ids and then the
+//     sequence number into host memory), first so it is dispatched first;
+//   - the shared expert's fs/8 (shared_in_routed), which need no routing;
+//   - f/8 workgroups of 8 rows per chosen slot (all K slots, or the slots of
+//     run_mask).
+// Each slot's expert blob comes from the top-K run by the workgroup itself
+// (then from expert_base, or from the device expert table), from the table
+// through the published ids (sel_from_table), or from sel_addr.
 template <int ACT, int MAXI, int NE>
 __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -495,32 +476,65 @@ __global__ __launch_bounds__(kThreads) void routed_gu_kernel(LayerArgs a) {
   __shared__ float s_logits[1024];
   const XStage S = carve_x(smem, a.d);
   const int t = blockIdx.y;
-  const int RB = a.f >> 3;
-  const int k = blockIdx.x / RB, rb = blockIdx.x - k * RB;
-  XRegs xr;
-  x_issue<ACT>(a, t, xr);
-  const uint8_t* blob;
-  if (a.topk_in_gate_up) {  // resident experts: every wavefront finds its expert itself
-    stage_logits<kThreads>(a, t, s_logits);
-    if (k == a.K) {  // one extra workgroup publishes ids and weights for the combine kernel
+  int b = blockIdx.x;
+  if (a.topk_in_gate_up) {
+    if (b == 0) {
+      stage_logits<kThreads>(a, t, s_logits);
       if (threadIdx.x < 64) {
         int id;
         float w;
         topk_wave<NE>(a, t, s_logits, &id, &w, scratch);
         publish_routing(a, t, threadIdx.x, id, w);
+        if (a.host_ids && threadIdx.x < a.K)
+          __hip_atomic_store(a.host_ids + threadIdx.x, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+      if (a.host_ids) {  // the sequence number after every id
+        __syncthreads();
+        if (threadIdx.x == 0)
+          __hip_atomic_store(a.host_flag, a.host_seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
       }
       return;
     }
+    --b;
+  }
+  const int NS = a.shared_in_routed ? a.fs >> 3 : 0;
+  if (b < NS) {  // the shared expert's gate/up: no routing needed
+    XRegs xr;
+    x_issue<ACT>(a, t, xr);
+    gate_up_block<ACT, MAXI>(a, t, a.shared_blob, a.so, b, 0, S, xr);
+    return;
+  }
+  b -= NS;
+  const int RB = a.f >> 3;
+  const int j = b / RB, rb = b - j * RB;
+  int k = j;
+  if (a.run_mask) {  // one token, some slots only: k = the j-th set bit
+    uint32_t m = a.run_mask;
+    for (int i = 0; i < j; ++i) m &= m - 1u;
+    k = __builtin_ctz(m);
+  }
+  XRegs xr;
+  x_issue<ACT>(a, t, xr);
+  const uint8_t* blob;
+  if (a.topk_in_gate_up) {  // every workgroup finds its expert itself
+    stage_logits<kThreads>(a, t, s_logits);
     if (threadIdx.x < 64) {
       const int id = topk_kth<NE>(a, t, s_logits, k);
       if (threadIdx.x == 0) scratch[0] = (uint32_t)id;
     }
     __syncthreads();
-    blob = a.expert_base + (size_t)scratch[0] * a.expert_stride;
+    const uint32_t id = scratch[0];
+    if (a.sel_from_table) {  // streamed experts: a zero address marks one that is not cached
+      const uint64_t addr = a.expert_addr[id];
+      if (a.hits_only && addr == 0) return;  // the host launches it again behind its fill
+      blob = reinterpret_cast<const uint8_t*>(addr);
+    } else {
+      blob = a.expert_base + (size_t)id * a.expert_stride;
+    }
   } else if (a.sel_from_table) {  // streamed experts: the table was brought up to date after the routing
-    if (a.go_host && !wait_go(a)) return;  // skipped: the host runs the call again after its fills
     const size_t o = (size_t)t * a.K + k;
     const uint64_t addr = a.expert_addr[a.ids[o]];
+    if (a.hits_only && addr == 0) return;  // not cached: the host launches it again behind its fill
     if (rb == 0 && threadIdx.x == 0) a.sel_addr[o] = addr;  // for the down kernel, which runs after this one
     blob = reinterpret_cast<const uint8_t*>(addr);
   } else {
@@ -692,8 +706,11 @@ template <int ACT, int MAXI>
 __global__ __launch_bounds__(kThreads) void down_combine_kernel(LayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int t = blockIdx.y;
-  // launched before the host's cache step: the routed kernel before this one relayed the verdict
-  if (a.go_dev && __hip_atomic_load(a.go_dev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 2u * a.host_seq) return;
+  if (a.hits_only) {  // queued before the cache step: runs when every chosen expert was cached
+    const int lane = threadIdx.x & 63;  // (every wavefront reads the same words: one decision per workgroup)
+    const bool miss = lane < a.K && a.expert_addr[a.ids[(size_t)t * a.K + lane]] == 0;
+    if (__ballot(miss)) return;
+  }
   down_block<ACT, MAXI>(a, t, blockIdx.x, a.sel_addr + (size_t)t * a.K, a.wts + (size_t)t * a.K, smem);
 }
 
@@ -1087,16 +1104,20 @@ template <int ACT, int MAXI, int NE>
 hipError_t launch_ab(const LayerArgs& a, int stages, hipStream_t s) {
   const size_t lds = x_stage_bytes(a.d);
   if (stages & (kStageRouter | kStageShared)) {
-    const int NR = (a.E + kWaves - 1) / kWaves;
+    const int NR = route_blocks(a);
     const int NS = (stages & kStageShared) ? a.fs / 8 : 0;
-    launch_timed(a.prof, kKRouteShared, route_shared_kernel<ACT, MAXI>, dim3(NR + NS, a.T), dim3(kThreads), lds, s,
-                 a);
-    if (!a.topk_in_gate_up) launch_timed(a.prof, kKTopK, topk_kernel<NE>, dim3(a.T), dim3(64), 0, s, a);
+    if (NR + NS > 0)
+      launch_timed(a.prof, kKRouteShared, route_shared_kernel<ACT, MAXI>, dim3(NR + NS, a.T), dim3(kThreads), lds, s,
+                   a);
+    if ((stages & kStageRouter) && !a.topk_in_gate_up)
+      launch_timed(a.prof, kKTopK, topk_kernel<NE>, dim3(a.T), dim3(64), 0, s, a);
   }
   if (stages & kStageRouted) {
     const int extra = a.topk_in_gate_up ? 1 : 0;  // the publishing workgroup
-    launch_timed(a.prof, kKRoutedGateUp, routed_gu_kernel<ACT, MAXI, NE>, dim3(a.K * (a.f / 8) + extra, a.T),
-                 dim3(kThreads), lds, s, a);
+    const int slots = a.run_mask ? __builtin_popcount(a.run_mask) : a.K;
+    const int NS = a.shared_in_routed ? a.fs / 8 : 0;
+    launch_timed(a.prof, kKRoutedGateUp, routed_gu_kernel<ACT, MAXI, NE>,
+                 dim3(NS + slots * (a.f / 8) + extra, a.T), dim3(kThreads), lds, s, a);
   }
   return hipGetLastError();
 }
@@ -1202,7 +1223,37 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* blob, uint3
   out[i] = fmaf(f16_to_f32((uint16_t)(sb & 0xFFFFu)), (float)nib, f16_to_f32((uint16_t)(sb >> 16)));
 }
 
+// Fills: kFillBlocks workgroups per blob stream it with 16-byte loads, four
+// in flight per lane (about 50 GB/s from pinned host memory for one blob).
+constexpr int kFillBlocks = 128;
+__global__ __launch_bounds__(256) void fill_kernel(FillArgs f) {
+  const int i = blockIdx.x / kFillBlocks, part = blockIdx.x - i * kFillBlocks;
+  const v4u* src = reinterpret_cast<const v4u*>(f.src[i]);
+  v4u* dst = reinterpret_cast<v4u*>(f.dst[i]);
+  const size_t n16 = f.bytes / 16, stride = (size_t)kFillBlocks * 256;
+  size_t j = (size_t)part * 256 + threadIdx.x;
+  for (; j + 3 * stride < n16; j += 4 * stride) {
+    const v4u w0 = src[j], w1 = src[j + stride], w2 = src[j + 2 * stride], w3 = src[j + 3 * stride];
+    dst[j] = w0;
+    dst[j + stride] = w1;
+    dst[j + 2 * stride] = w2;
+    dst[j + 3 * stride] = w3;
+  }
+  for (; j < n16; j += stride) dst[j] = src[j];
+  if (blockIdx.x == 0 && (int)threadIdx.x < f.n) {
+    f.table[f.expert[threadIdx.x]] = reinterpret_cast<uint64_t>(f.dst[threadIdx.x]);
+    if (f.evicted[threadIdx.x] >= 0) f.table[f.evicted[threadIdx.x]] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fill(const FillArgs& f, hipStream_t s) {
+  if (f.n <= 0) return hipSuccess;
+  if (f.n > kMaxFills || f.bytes % 16 != 0) return hipErrorInvalidValue;
+  fill_kernel<<<dim3((unsigned)(f.n * kFillBlocks)), dim3(256), 0, s>>>(f);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant(const uint8_t* blob, uint32_t q_off, uint32_t sb_off, int rows, int cols, float* out,
                           hipStream_t s) {

@@ -71,15 +71,23 @@ struct LayerArgs {
   void* out;              // [T][d]
   const void* resid;      // [T][d] or null
   // which parts to run (0 = all): 1 router + top-K, 2 shared gate/up,
-  // 4 routed gate/up, 8 down + combine
+  // 4 routed gate/up, 8 down + combine; the router and the shared gate/up
+  // share a launch when both are asked for
   int stages;
   int topk_in_gate_up;  // 1: every routed gate/up workgroup runs the top-K itself
-  int32_t* host_ids;    // T == 1, streamed layers: the top-K kernel also writes the chosen ids here
-  uint32_t* host_flag;  // (host memory, device view), then host_seq into *host_flag
+  int32_t* host_ids;    // T == 1, streamed layers: the routed gate/up's top-K workgroup also writes the
+  uint32_t* host_flag;  // chosen ids here (host memory, device view), then host_seq into *host_flag
   uint32_t host_seq;
-  const uint32_t* go_host;  // routed/down kernels launched before the host's cache step: the host writes
-  uint32_t* go_dev;         // 2*host_seq (run) or 2*host_seq+1 (skip) into *go_host; routed gate/up
-                            // block 0 relays it into *go_dev, read by its other blocks and the down kernel
+  // One token: routed gate/up and down kernels queued before the host's cache
+  // step.  The device expert table then holds exactly what the cache holds, so
+  // a nonzero address marks a hit: gate/up computes those slots only, and the
+  // down kernel runs only when every chosen expert was a hit.  The host
+  // launches the misses behind their fills, then the down kernel again.
+  int hits_only;
+  uint32_t run_mask;    // one token: the routed gate/up launch computes only the slots set here (0 = all);
+                        // its grid holds popcount(run_mask) * f/8 workgroups
+  int shared_in_routed;  // 1: the routed gate/up launch also runs the shared expert's gate/up, in its
+                         // first fs/8 workgroups (which wait for nothing)
   int sel_from_table;   // 1: routed gate/up takes each chosen expert's address from expert_addr[ids]
                         // (current after the call's fills) and writes it to sel_addr for the down kernel
   int fused;            // 1: one launch per layer (batch 1, bf16, resident experts)
@@ -96,6 +104,22 @@ enum : int32_t { kErrBadForcedId = 1, kErrMissingExpert = 2, kErrSyncTimeout = 4
 constexpr float kF16HandoffMax = 65504.f;
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t s);
+
+// Cache fills by a kernel on the call's stream: each blob is read from pinned
+// host memory over the host link and written to its slot; then the layer's
+// device expert table gets the filled experts' addresses, and zeros for the
+// experts the fills evicted.  Kernel arguments only, no workspace.
+constexpr int kMaxFills = 32;
+struct FillArgs {
+  int n;           // blobs (<= kMaxFills)
+  uint64_t bytes;  // per blob, a multiple of 16
+  const uint8_t* src[kMaxFills];  // device view of pinned host memory
+  uint8_t* dst[kMaxFills];        // cache slots
+  uint64_t* table;                // [E] device expert table
+  int32_t expert[kMaxFills];      // table[expert[i]] = dst[i]
+  int32_t evicted[kMaxFills];     // table[evicted[i]] = 0 (when >= 0)
+};
+hipError_t launch_fill(const FillArgs& f, hipStream_t s);
 // The allocation-free forward's workspace: a device array of this many bytes
 // per GPU; *ptr receives its address on the current device.
 constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;

@@ -102,10 +102,10 @@ FALLBACK_W = Workload(72, "fallback", d=512, E=64, K=8, f=128, fs=128, act="bf16
 
 def test_streamed_call_without_host_spin_matches_resident():
     """A streamed one-token call whose host spin for the routing runs out at
-    once falls back to waiting for the stream.  Its expert kernels were
-    launched ahead and wait for the verdict: they are told to skip before the
-    wait and run again behind the fills, so every call still equals the
-    resident layer bit for bit, flags stay clear and the counters replay."""
+    once falls back to waiting for the stream (which then also holds its hits,
+    computed by the kernels queued before the cache step); its misses still
+    run after their fill, so every call equals the resident layer bit for
+    bit, flags stay clear and the counters replay."""
     w = FALLBACK_W
     arrays = make_layer(w)
     res = GpuLayer(w, arrays, 1)

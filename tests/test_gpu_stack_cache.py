@@ -112,6 +112,57 @@ def test_streamed_layer_bit_identical_and_counters_replay(w):
     assert stats["h2d_bytes"] == replay.misses * stride
     experts, counts = M.moe_cache_contents(st.handle, w.slots)
     assert list(experts) == replay.expert and list(counts) == replay.count
+    # every hit of a one-token call was computed by the kernels queued before
+    # the cache step
+    assert stats["ahead_slots"] == replay.hits
+    assert M.moe_layer_check_errors(st.handle) == 0
+    res.close()
+    st.close()
+
+
+def test_streamed_hits_at_once_misses_after_their_fill():
+    """Forced routings whose calls mix hits and misses in every proportion
+    (0 to K misses, repeated ids in a call): the hits of a one-token call are
+    computed by kernels queued before its cache step, its misses after the
+    fill kernel, then the down kernel.  Outputs stay bit-identical to the
+    resident layer, the cache follows the replay, and the slots computed ahead
+    are exactly the slots whose experts were hits."""
+    w = CACHE_W
+    arrays = make_layer(w)
+    res = GpuLayer(w, arrays, 1)
+    st = GpuLayer(w, arrays, 1, residency=M.MOE_STREAMED)
+    M.moe_cache_attach(st.handle, w.slots)
+    x = make_tokens(w, 48, stream=37)
+    rng = np.random.default_rng(41)
+    replay = LfuReplay(w.slots)
+    want_ahead = 0
+    plans = [list(range(8)), [0, 1, 2, 3, 4, 5, 8, 9], [0, 1, 2, 3, 4, 5, 6, 10], [1, 1, 2, 3, 11, 11, 12, 4],
+             list(range(20, 28))]
+    for t in range(48):
+        cached = [e for e in replay.expert if e >= 0]
+        if t < len(plans):
+            ids = plans[t]
+        else:  # n_miss of the K slots from experts not cached, the rest from the cache
+            n_miss = int(rng.integers(0, w.K + 1)) if len(cached) >= w.K else w.K
+            absent = [e for e in range(w.E) if e not in cached]
+            ids = list(rng.choice(absent, n_miss, replace=False)) + list(rng.choice(cached, w.K - n_miss,
+                                                                                    replace=False))
+            rng.shuffle(ids)
+        forced = np.array([ids], np.int32)
+        y_r, ids_r, w_r = res.forward(x[t:t + 1], path=M.MOE_PATH_DECODE, forced=forced)
+        y_s, ids_s, w_s = st.forward(x[t:t + 1], path=M.MOE_PATH_DECODE, forced=forced)
+        assert np.array_equal(y_r, y_s), f"call {t} (routing {ids}) differs from resident"
+        assert np.array_equal(ids_r, ids_s) and np.array_equal(w_r, w_s)
+        want_ahead += sum(1 for e in ids if e in cached)
+        replay.step(sorted(set(int(e) for e in ids)))
+    stats = M.moe_cache_stats_get(st.handle)
+    assert (stats["accesses"], stats["hits"], stats["misses"], stats["evictions"]) == \
+        (replay.accesses, replay.hits, replay.misses, replay.evictions)
+    assert replay.evictions > 0 and replay.hits > 0
+    assert stats["ahead_slots"] == want_ahead
+    assert stats["h2d_ns"] > 0
+    experts, counts = M.moe_cache_contents(st.handle, w.slots)
+    assert list(experts) == replay.expert and list(counts) == replay.count
     assert M.moe_layer_check_errors(st.handle) == 0
     res.close()
     st.close()
@@ -365,8 +416,8 @@ def test_streamed_fault_injection_leaves_state_unchanged():
     res = GpuLayer(w, arrays, 1)
     y_r, _, _ = res.forward(x[2:3], path=M.MOE_PATH_DECODE)
     assert np.array_equal(y_r, y_s)
-    # the failed call's routed and down kernels, launched before the cache
-    # step, were told to skip: none of their bounded waits ran out
+    # the failed call's kernels queued before the cache step found no chosen
+    # expert in the table: they computed nothing and raised no flag
     assert M.moe_layer_check_errors(st.handle) == 0
     res.close()
     st.close()
