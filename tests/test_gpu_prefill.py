@@ -124,6 +124,8 @@ PSHAPES = [  # (d, E, K, f, fs, T)
     (1024, 300, 8, 256, 128, 130),
     (2816, 128, 8, 704, 2112, 24),
     (256, 1, 1, 64, 64, 16),
+    (512, 4, 2, 128, 64, 128),     # every routed expert has about 64 rows (four 16-row tiles)
+    (1024, 8, 8, 128, 128, 200),   # K = E: every expert takes every row (128, then 72)
 ]
 
 
@@ -151,3 +153,60 @@ def test_prefill_and_decode_paths_agree(prefill_layer):
     assert np.max(np.abs(wp - wd)) < 1e-5
     a, b = O.tokens_to_f64(yp), O.tokens_to_f64(yd)
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 5e-3
+
+
+def _mixed_forced(w, T, seed):
+    """Forced sets: the first half of the tokens choose experts 0..K-1 (so
+    those experts have at least T/2 rows: several 16-row tiles each), the
+    rest random distinct sets (a few rows per expert)."""
+    rng = np.random.default_rng(seed)
+    ids = np.empty((T, w.K), np.int32)
+    for t in range(T):
+        ids[t] = np.arange(w.K) if t < T // 2 else np.sort(rng.choice(w.E, w.K, replace=False))
+    return ids
+
+
+def test_prefill_busy_and_sparse_experts_in_one_chunk(prefill_layer):
+    """Experts with many rows (several 16-row tiles, a ragged last one)
+    beside experts with a few rows and the shared expert, in one 128-token
+    chunk and in a 300-token call, against the oracle forced to the same
+    sets."""
+    w, gl, OL = prefill_layer
+    for T, seed in ((128, 51), (300, 52)):
+        x = make_tokens(w, T, stream=seed)
+        forced = _mixed_forced(w, T, seed)
+        y, ids, wt = gl.forward(x, path=M.MOE_PATH_PREFILL, forced=forced)
+        worst = check_layer(gl, OL, x, y, ids, wt, forced=forced)
+        print(f"mixed forced T={T}: worst rel L2 {worst:.3e}")
+
+
+def test_prefill_dense_routing_matches_oracle(prefill_layer):
+    """The dense-routing case of the prefill benchmark (every token on
+    experts 0..K-1: eight full 16-row tiles per chosen expert)."""
+    w, gl, OL = prefill_layer
+    x = make_tokens(w, 128, stream=53)
+    forced = np.tile(np.arange(w.K, dtype=np.int32), (128, 1))
+    y, ids, wt = gl.forward(x, path=M.MOE_PATH_PREFILL, forced=forced)
+    worst = check_layer(gl, OL, x, y, ids, wt, forced=forced)
+    print(f"dense routing: worst rel L2 {worst:.3e}")
+
+
+def test_streamed_prefill_busy_experts_equals_resident():
+    """A streamed layer's prefill with busy experts (many tiles each, inside
+    the cache groups) stays bit-identical to the resident layer."""
+    w = Workload(89, "pf-stream-wide", d=512, E=64, K=8, f=128, fs=128, act="bf16", zipf=1.0, T=1, slots=16)
+    arrays = make_layer(w)
+    res = GpuLayer(w, arrays, 256)
+    st = GpuLayer(w, arrays, 256, residency=M.MOE_STREAMED)
+    M.moe_cache_attach(st.handle, w.slots)
+    for T, seed in ((128, 54), (256, 55)):
+        x = make_tokens(w, T, stream=seed)
+        forced = _mixed_forced(w, T, seed)
+        y_r, ids_r, w_r = res.forward(x, path=M.MOE_PATH_PREFILL, forced=forced)
+        y_s, ids_s, w_s = st.forward(x, path=M.MOE_PATH_PREFILL, forced=forced)
+        assert np.array_equal(y_r, y_s), f"T={T}: streamed prefill differs from resident"
+        assert np.array_equal(w_r, w_s)
+    check_layer(res, O.OracleLayer.from_workload(w, arrays), x, y_r, ids_r, w_r, forced=forced)
+    assert M.moe_layer_check_errors(st.handle) == 0
+    res.close()
+    st.close()
