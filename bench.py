@@ -367,6 +367,13 @@ def run_prefill(args, M, torch, np, chunks=None, summary=False):
             "ms_per_chunk": round(ddt * 1e3, 4), "tflops": round(flops / ddt / 1e12, 2),
             "mfma_util": round(flops / ddt / 1e12 / PEAK_BF16_TFLOPS, 4),
             "kernels": {k: dk[k] for k in ("prefill_gate_up", "prefill_down") if k in dk}}
+        # The shared expert at T = 128 is one 128-row dense GEMM; in the dense
+        # case every launched expert has that shape (9 x 128 rows, d_ff 512),
+        # so the launches' utilisation is the shared expert's.
+        res["shared_expert_T128"] = {
+            "from": "dense-routing launches: 9 experts of 128 rows, the shared expert one of them",
+            **{k + "_mfma_util": round(dk[k]["tflops"] / PEAK_BF16_TFLOPS, 4)
+               for k in ("prefill_gate_up", "prefill_down") if k in dk and "tflops" in dk[k]}}
         for T in (512, 2048):  # longer prompts as sequential 128-token chunks inside one call
             if T > C * nch:
                 continue
@@ -499,10 +506,17 @@ def run_stream(args, M, torch, np):
         for L in layers:
             M.moe_layer_set_default_path(L, path)
         stack = M.moe_stack_create(layers, 1e-6)
-        if layers is res_layers:  # untimed warm-up (the streamed runs start from empty caches on purpose)
+        if layers is res_layers:  # untimed warm-up (the streamed runs start from empty caches on purpose),
+            # long enough for the GPU's clocks to leave the idle state of layer creation: the first
+            # timed run was otherwise up to 3x slow on the fused kernel
             hw = h0.clone()
-            for t in range(8):
-                M.moe_stack_forward(hw, stack, 1, reuse_mask=coins[t])
+            t_end, t = time.perf_counter() + 0.5, 0
+            while t < 8 or time.perf_counter() < t_end:
+                M.moe_stack_forward(hw, stack, 1, reuse_mask=coins[t % steps])
+                t += 1
+                if t % 16 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
         h = h0.clone()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
