@@ -268,22 +268,30 @@ __device__ __forceinline__ TileInfo tile_info(const PrefillArgs& p, int tile) {
 // (v[8j+m], v[8j+m+4]) per 16-byte word, rows padded by 16 bytes against bank
 // conflicts, and per-group sums gsum[g][m].  rows[m] is the source row (or
 // nullptr for an empty row), natural order when PERMUTE, already paired
-// otherwise.  Every thread issues all of its loads before touching LDS.
-// STG = 16-byte words per thread (16 rows x width columns / 512 threads).
-template <bool PERMUTE, int STG>
-__device__ void stage_rows(int width, const uint16_t* const* rows, v4u* lds, float* gsum) {
-  const int W = width >> 3, stride = W + 1;  // words per row (+1 pad word)
+// otherwise.  STG = 16-byte words per thread (16 rows x width columns / 512
+// threads).  In two steps, so that a kernel can request its first weights
+// between them: stage_rows_load issues every load of the thread (branch-free,
+// all in flight at once); stage_rows_commit writes LDS and ends with a
+// barrier.  A wavefront's loads complete in order, so the commit waits for
+// the row loads only and weights requested after them stay in flight.
+template <int STG>
+__device__ __forceinline__ void stage_rows_load(int width, const uint16_t* const* rows, v4u (&buf)[STG]) {
+  const int W = width >> 3;
   const int total = kTile * W;
-  v4u buf[STG];
-  const uint16_t* any_row = rows[0] ? rows[0] : rows[kTile - 1];  // a valid row (row 0 is never empty)
+  const uint16_t* any_row = rows[0] ? rows[0] : rows[kTile - 1];
 #pragma unroll
-  for (int it = 0; it < STG; ++it) {  // branch-free so every load is in flight at once
+  for (int it = 0; it < STG; ++it) {
     const int idx = min((int)threadIdx.x + kPThreads * it, total - 1);
     const int m = idx / W, j = idx - m * W;
     const uint16_t* src = rows[m] ? rows[m] : any_row;
     const v4u w = ldg<v4u>(src + (size_t)j * 8);
     buf[it] = rows[m] ? w : v4u{0u, 0u, 0u, 0u};
   }
+}
+template <bool PERMUTE, int STG>
+__device__ __forceinline__ void stage_rows_commit(int width, v4u (&buf)[STG], v4u* lds, float* gsum) {
+  const int W = width >> 3, stride = W + 1;
+  const int total = kTile * W;
 #pragma unroll
   for (int it = 0; it < STG; ++it) {
     const int idx = threadIdx.x + kPThreads * it;
@@ -413,11 +421,13 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
     rows[m] = tok < 0 ? nullptr : static_cast<const uint16_t*>(p.xact) + (size_t)tok * d;
   }
   __syncthreads();
-  // The token rows are staged before any weight is requested: a wavefront's
-  // loads complete in order, so staging behind a first batch of weight loads
-  // would wait for them, and the grid's first batch is tens of megabytes.
-  stage_rows<true, STG>(d, rows, xs_lds, gsum);
-  if (n0 >= fdim) return;  // no barrier follows
+  // The token rows are requested first and the first kPre groups of weights
+  // right behind them; then the rows are committed to LDS, which waits for
+  // the row loads only (a wavefront's loads complete in order), so the
+  // weights stream while the tile is staged.  Measured: 57.9 against 59.7 us
+  // per 128-token chunk.
+  v4u sbuf[STG];
+  stage_rows_load<STG>(d, rows, sbuf);
   v2u wg[kPre][kGuTiles], wu[kPre][kGuTiles];
   uint32_t sg[kPre][kGuTiles], su[kPre][kGuTiles];
   auto fetch = [&](int i, uint32_t g) {
@@ -435,6 +445,9 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
     fetch(i, (uint32_t)min(i, G - 1));
   }
   __builtin_amdgcn_sched_barrier(0);
+  stage_rows_commit<true, STG>(d, sbuf, xs_lds, gsum);
+  __builtin_amdgcn_sched_barrier(0);
+  if (n0 >= fdim) return;  // no barrier follows
   f32x4 accg[kGuTiles], accu[kGuTiles];
 #pragma unroll
   for (int t = 0; t < kGuTiles; ++t) accg[t] = accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -536,8 +549,8 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
     rows[m] = (m >= ti.m_valid) ? nullptr : src + (size_t)(ti.base + ti.tt * kTile + m) * fdim;
   }
   __syncthreads();
-  stage_rows<false, STG>(fdim, rows, as_lds, gsum);  // before any weight request, as in gate/up
-  if (n0 >= a.d) return;  // no barrier follows
+  v4u sbuf[STG];
+  stage_rows_load<STG>(fdim, rows, sbuf);  // then the first weights, then the commit (as in gate/up)
   v2u w[kDnPre][kDnTiles];
   uint32_t sb[kDnPre][kDnTiles];
   // slot i's loads go out as one batch, slots in order (scheduling
@@ -553,6 +566,9 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   };
 #pragma unroll
   for (int i = 0; i < kDnPre; ++i) fetch(i, (uint32_t)min(i, G - 1));
+  stage_rows_commit<false, STG>(fdim, sbuf, as_lds, gsum);
+  __builtin_amdgcn_sched_barrier(0);
+  if (n0 >= a.d) return;  // no barrier follows
   f32x4 acc[kDnTiles];
 #pragma unroll
   for (int t = 0; t < kDnTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
