@@ -836,8 +836,8 @@ __device__ __forceinline__ void stage_logits_dev(const LayerArgs& a, const uint6
 // passed their last wait (8 parts, replica 0; part i % 8 for down workgroup
 // i).  A down workgroup passes it only after every other workgroup of the
 // launch has started and read the count (shared and routed workgroups arrive
-// on the counters it waits for; every routed workgroup has read every router
-// workgroup's tagged logits), and the count
+// on the counters it waits for; it has itself read every router workgroup's
+// logits, which carry the tag the router read), and the count
 // cannot reach the next multiple of nd before every down workgroup, the
 // reader included, has passed.  So every workgroup of launch n reads a total
 // in [(n-1) nd, n nd) and takes tag = total / nd + 1 = n, with no reset
@@ -1083,7 +1083,11 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
     XRegs xr;
     x_issue<1>(a, 0, xr);
     __builtin_amdgcn_s_setprio(2);
-    stage_logits_dev<NE>(a, my_rep, tag, s_logits);  // re-reads entries until they carry this launch's tag
+    // re-reads entries until they carry this launch's tag.  Forced sets (a
+    // reused routing) name the experts without the logits: the weights then
+    // stream from the start; only the down workgroups, which compute the
+    // coefficients, wait for the logits.
+    if (!a.forced) stage_logits_dev<NE>(a, my_rep, tag, s_logits);
     if (threadIdx.x < 64) {  // one wavefront finds the expert
       const int id = topk_kth<NE>(a, 0, s_logits, k);
       if (threadIdx.x == 0) scratch[0] = (uint32_t)id;
