@@ -140,6 +140,7 @@ struct moe_layer {
   int32_t* h_ids = nullptr;    // pinned, coherent routing copy [max_tokens*K], then a sequence word
   void* d_host_ids = nullptr;  // its device view
   uint32_t host_seq = 0;       // sequence number of the last one-token routing written by the GPU
+  bool h_ids_last = false;     // h_ids holds the routing of this layer's last call (a one-token streamed call)
   int64_t host_wait_us = 2000000;  // how long the host spins for that routing before it waits for the stream
   int32_t* h_pf = nullptr;     // prefill through the cache: pinned counts [E], then group tile lists
   int32_t* d_pf_tiles = nullptr;  // the group tile lists on the device
@@ -512,11 +513,17 @@ std::vector<int32_t> predict_next(const moe_layer* L, int depth) {
 // kernels read only the slots of chosen experts, which the step never
 // refills.)
 moe_status stream_in(moe_layer* L, int T, hipStream_t stream, moe_layer* next = nullptr, int depth = 0,
-                     uint32_t seq = 0, SlotPlan* plan = nullptr) {
+                     uint32_t seq = 0, SlotPlan* plan = nullptr, bool ids_known = false) {
   moe_cache_pool* P = L->pool;
   if (!L->lfu && !P) return fail(MOE_ERR_STATE, "streamed layer has no cache: call moe_cache_attach first");
   const size_t n = (size_t)T * L->K;
-  if (seq) {  // one token: the top-K kernel writes the ids and then seq into host memory
+  if (ids_known) {
+    // a one-token call that reuses the previous call's sets: h_ids already
+    // holds them (that call waited for them), so the cache step needs
+    // nothing from this call's kernels and the host goes on at once; only a
+    // fill of the previous call is waited for, to account its time
+    if (L->fill_pending) HIP_OK(hipEventSynchronize(L->ev_fill));
+  } else if (seq) {  // one token: the top-K kernel writes the ids and then seq into host memory
     if (!wait_host_flag(L, seq)) {  // not within the time limit: the stream's own status decides
       HIP_OK(hipStreamSynchronize(stream));
       if (!wait_host_flag(L, seq)) return fail(MOE_ERR_STATE, "the routing of the call did not reach the host");
@@ -646,6 +653,8 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
   if (T == 0) return MOE_OK;
   if (T < 0 || T > L->max_tokens) return fail(MOE_ERR_INVALID, "n_tokens=%d not in 0..%d", T, L->max_tokens);
   HIP_OK(hipSetDevice(L->dev));
+  const bool h_ids_last = L->h_ids_last;  // set again below when this call leaves its routing in h_ids
+  L->h_ids_last = false;
   if (o) {
     a.ids_out = o->topk_ids;
     a.w_out = o->topk_w;
@@ -715,6 +724,7 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
     // the last; with no miss it launches nothing more.
     const bool one = T == 1 && L->d_host_ids && L->K <= 32;
     uint32_t seq = 0;
+    bool uploaded = false;  // the device table goes up from h_addr in this call
     if (one) {
       seq = ++L->host_seq;
       if (seq >= (1u << 30)) seq = L->host_seq = 1;  // 0 means "no flag"
@@ -723,6 +733,7 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
       if (L->addr_dirty) {  // a fetch-ahead or another layer's eviction changed it since the last upload
         HIP_OK(hipMemcpyAsync(L->d_expert_addr, L->h_addr, (size_t)L->E * 8, hipMemcpyHostToDevice, s));
         L->addr_dirty = false;
+        uploaded = true;
       }
     }
     HIP_OK(launch_decode(a1, s));
@@ -741,8 +752,14 @@ moe_status forward_impl(moe_layer* L, LayerArgs a, const moe_fwd_opts* o, hipStr
       HIP_OK(launch_decode(a3, s));
     }
     SlotPlan plan;
-    moe_status st = stream_in(L, T, s, next, depth, seq, one ? &plan : nullptr);
+    // The host may skip the wait for the routing only when it needs nothing
+    // from this call's kernels: the sets are reused and known, and no upload
+    // of h_addr is in flight (the copy reads host memory when it runs, and
+    // the cache step is about to change it).
+    const bool known = one && o && o->reuse_previous && h_ids_last && !uploaded;
+    moe_status st = stream_in(L, T, s, next, depth, seq, one ? &plan : nullptr, known);
     if (st != MOE_OK) return st;
+    L->h_ids_last = one;
     if (!one) {
       HIP_OK(launch_decode(a2, s));
     } else if (plan.late) {  // behind the fill kernel on the stream
@@ -1011,6 +1028,7 @@ moe_status moe_layer_route(const void* x, moe_layer* L, int32_t* ids, float* w, 
   a.stages = kStageRouter;
   a.ids_out = ids;
   a.w_out = w;
+  L->h_ids_last = false;  // the layer's stored sets become these
   HIP_OK(launch_decode(a, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }

@@ -146,6 +146,22 @@ def test_fused_forced_and_reused(decode_layer):
     assert M.moe_layer_check_errors(gl.handle) == 0
 
 
+def test_fused_forced_set_in_any_order(decode_layer):
+    """A forced set names its experts in any order: the routed gate/up
+    workgroups take the k-th smallest id without waiting for the logits, and
+    the result is bit-identical to the same set given in ascending order."""
+    w, gl, OL = decode_layer
+    x = make_tokens(w, 1, stream=27)
+    ordered = np.array([[3, 7, 11, 50, 51, 90, 100, 126]], np.int32)
+    shuffled = np.array([[126, 3, 90, 7, 51, 11, 100, 50]], np.int32)
+    a = gl.forward(x, path=M.MOE_PATH_FUSED, forced=ordered)
+    b = gl.forward(x, path=M.MOE_PATH_FUSED, forced=shuffled)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    check_layer(gl, OL, x, *b, forced=ordered)
+    assert M.moe_layer_check_errors(gl.handle) == 0
+
+
 def test_fused_bad_forced_id_is_flagged(decode_layer):
     w, gl, OL = decode_layer
     x = make_tokens(w, 1, stream=25)

@@ -120,6 +120,43 @@ def test_streamed_layer_bit_identical_and_counters_replay(w):
     st.close()
 
 
+def test_streamed_reuse_follows_the_stored_sets():
+    """A one-token call of a streamed layer that reuses the previous sets does
+    its cache step from the host's copy of the routing, without waiting for
+    its kernels.  The stored sets are the last routing of the layer, also a
+    route-only call's (moe_layer_route): after one, a reusing call must take
+    that call's sets, like the resident layer, and run bit-identical to it."""
+    torch = torch_mod()
+    w = CACHE_W
+    arrays = make_layer(w, seed=9)
+    res = GpuLayer(w, arrays, 1)
+    st = GpuLayer(w, arrays, 1, residency=M.MOE_STREAMED)
+    M.moe_cache_attach(st.handle, w.slots)
+    x = make_tokens(w, 6, stream=41)
+    calls = [("fwd", False), ("fwd", True), ("fwd", True), ("route", None), ("fwd", True), ("fwd", False),
+             ("fwd", True)]
+    routed = None
+    for i, (kind, reuse) in enumerate(calls):
+        xi = x[i % 6:i % 6 + 1]
+        if kind == "route":
+            xd = to_device(xi)
+            for g in (res, st):
+                ids = torch.empty((1, w.K), dtype=torch.int32, device="cuda")
+                wts = torch.empty((1, w.K), dtype=torch.float32, device="cuda")
+                M.moe_layer_route(xd, g.handle, ids, wts, 1)
+            torch.cuda.synchronize()
+            routed = ids.cpu().numpy()
+            continue
+        y_r, ids_r, w_r = res.forward(xi, path=M.MOE_PATH_DECODE, reuse=reuse)
+        y_s, ids_s, w_s = st.forward(xi, path=M.MOE_PATH_DECODE, reuse=reuse)
+        assert np.array_equal(y_r, y_s) and np.array_equal(ids_r, ids_s), f"call {i}"
+        if i == 4:
+            assert np.array_equal(ids_s, routed), "a reusing call after a route-only call takes its sets"
+    assert M.moe_layer_check_errors(st.handle) == 0
+    res.close()
+    st.close()
+
+
 def test_streamed_hits_at_once_misses_after_their_fill():
     """Forced routings whose calls mix hits and misses in every proportion
     (0 to K misses, repeated ids in a call): the hits of a one-token call are
