@@ -145,7 +145,10 @@ moe_status moe_layer_destroy(moe_layer* layer);
  * the stream) and computes the experts that are cached; the down kernel runs
  * when all were.  A miss then costs a fill kernel, a gate/up launch for the
  * missed experts and the down kernel again.  More tokens: one small
- * device->host copy and a stream synchronisation. */
+ * device->host copy and a stream synchronisation.  A one-token call with
+ * reuse_previous right after another one-token call of the layer already
+ * has its sets on the host and does not wait, unless the layer's device
+ * expert table has to be uploaded in that call. */
 moe_status moe_layer_forward(const void* x, moe_layer* layer, void* out, int32_t n_tokens, void* stream);
 
 /* Optional controls of one forward call.  Every field may be 0/NULL. */
@@ -157,8 +160,10 @@ typedef struct {
                                  coefficients are renormalised from this call's
                                  logits over the given set */
   int32_t reuse_previous;     /* nonzero: use the expert sets of this layer's
-                                 previous forward call (same n_tokens), with
-                                 coefficients from this call's logits */
+                                 previous forward call (same n_tokens; a
+                                 moe_layer_route call in between replaces
+                                 them), with coefficients from this call's
+                                 logits */
   int32_t path;               /* MOE_PATH_* (see above) */
   int32_t residual;           /* nonzero: out = act(x_in + y) where x_in is the
                                  `residual_src` tensor (stack glue) */
