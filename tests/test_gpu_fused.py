@@ -98,6 +98,37 @@ def test_fused_shapes(shape):
     gl.close()
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_fused_forced_sets_on_random_shapes(seed):
+    """Seeded random shapes within the fused kernel's limits, each with a
+    forced set of distinct experts given in shuffled order (the routed
+    gate/up workgroups then skip the logits): the oracle on the same set, and
+    the three-kernel path on it."""
+    rng = np.random.default_rng(1000 + seed)
+    while True:
+        d = 64 * int(rng.integers(1, 65))
+        E = int(rng.integers(1, 301))
+        K = int(rng.integers(1, min(E, 16) + 1))
+        f = 64 * int(rng.integers(1, 13))
+        fs = 64 * int(rng.integers(0, 9))
+        if K * (f // 64) <= 128:
+            break
+    print(f"shape d={d} E={E} K={K} f={f} fs={fs}", flush=True)
+    w = Workload(124 + seed, "forced-shape", d=d, E=E, K=K, f=f, fs=fs, act="bf16", zipf=1.0, T=2)
+    arrays = make_layer(w)
+    gl = GpuLayer(w, arrays, 1)
+    OL = O.OracleLayer.from_workload(w, arrays)
+    x = make_tokens(w, 2, stream=6)
+    for t in range(2):
+        chosen = np.sort(rng.choice(E, size=K, replace=False)).astype(np.int32)
+        shuffled = rng.permutation(chosen).astype(np.int32)[None, :]
+        got = gl.forward(x[t:t + 1], path=M.MOE_PATH_FUSED, forced=shuffled)
+        check_layer(gl, OL, x[t:t + 1], *got, forced=chosen[None, :])
+        _agree(got, gl.forward(x[t:t + 1], path=M.MOE_PATH_DECODE, forced=chosen[None, :]))
+    assert M.moe_layer_check_errors(gl.handle) == 0
+    gl.close()
+
+
 def test_fused_many_launches_and_graph_replays(decode_layer):
     """Back-to-back launches, then a captured graph of 8 calls replayed 4
     times with eager work in between; every replay equals the eager result."""
