@@ -37,11 +37,14 @@ __device__ __forceinline__ T ldg(const void* p) {
 }
 
 constexpr int kTile = 16;      // tokens per MFMA tile
-#ifndef MOE_PF_WAVES
-#define MOE_PF_WAVES 8
+#ifndef MOE_GU_WAVES
+#define MOE_GU_WAVES 16
 #endif
-constexpr int kPWaves = MOE_PF_WAVES;  // wavefronts per prefill GEMM workgroup
-constexpr int kPThreads = 64 * kPWaves;
+#ifndef MOE_DN_WAVES
+#define MOE_DN_WAVES 8
+#endif
+constexpr int kGuThreads = 64 * MOE_GU_WAVES;  // threads of a gate/up GEMM workgroup
+constexpr int kDnThreads = 64 * MOE_DN_WAVES;  // threads of a down GEMM workgroup
 
 // ------------------------------------------------------------ sort + tiles
 // Exclusive prefix sum of one int per thread over the workgroup (up to 1024
@@ -268,33 +271,33 @@ __device__ __forceinline__ TileInfo tile_info(const PrefillArgs& p, int tile) {
 // (v[8j+m], v[8j+m+4]) per 16-byte word, rows padded by 16 bytes against bank
 // conflicts, and per-group sums gsum[g][m].  rows[m] is the source row (or
 // nullptr for an empty row), natural order when PERMUTE, already paired
-// otherwise.  STG = 16-byte words per thread (16 rows x width columns / 512
+// otherwise.  STG = 16-byte words per thread (16 rows x width columns / NTH
 // threads).  In two steps, so that a kernel can request its first weights
 // between them: stage_rows_load issues every load of the thread (branch-free,
 // all in flight at once); stage_rows_commit writes LDS and ends with a
 // barrier.  A wavefront's loads complete in order, so the commit waits for
 // the row loads only and weights requested after them stay in flight.
-template <int STG>
+template <int NTH, int STG>
 __device__ __forceinline__ void stage_rows_load(int width, const uint16_t* const* rows, v4u (&buf)[STG]) {
   const int W = width >> 3;
   const int total = kTile * W;
   const uint16_t* any_row = rows[0] ? rows[0] : rows[kTile - 1];
 #pragma unroll
   for (int it = 0; it < STG; ++it) {
-    const int idx = min((int)threadIdx.x + kPThreads * it, total - 1);
+    const int idx = min((int)threadIdx.x + NTH * it, total - 1);
     const int m = idx / W, j = idx - m * W;
     const uint16_t* src = rows[m] ? rows[m] : any_row;
     const v4u w = ldg<v4u>(src + (size_t)j * 8);
     buf[it] = rows[m] ? w : v4u{0u, 0u, 0u, 0u};
   }
 }
-template <bool PERMUTE, int STG>
+template <int NTH, bool PERMUTE, int STG>
 __device__ __forceinline__ void stage_rows_commit(int width, v4u (&buf)[STG], v4u* lds, float* gsum) {
   const int W = width >> 3, stride = W + 1;
   const int total = kTile * W;
 #pragma unroll
   for (int it = 0; it < STG; ++it) {
-    const int idx = threadIdx.x + kPThreads * it;
+    const int idx = threadIdx.x + NTH * it;
     if (idx < total) {  // uniform across each aligned group of 8 lanes
       const int m = idx / W, j = idx - m * W;
       const v4u w = buf[it];
@@ -342,6 +345,11 @@ __device__ __forceinline__ bf16x8 b_operand(uint32_t w, uint32_t mask) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Word v of lane (lane & 15) + 16 j of the wavefront (j uniform).
+__device__ __forceinline__ uint32_t from_quarter(uint32_t v, int j) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 15) + 16 * j) << 2), (int)v);
+}
+
 __device__ __forceinline__ void group_epilogue(f32x4& acc, const f32x4& t, uint32_t sb, const float* xs4) {
   const float s = f16_to_f32((uint16_t)(sb & 0xFFFFu));
   const float bb = f16_to_f32((uint16_t)(sb >> 16)) - 128.f * s;
@@ -367,22 +375,26 @@ __device__ __forceinline__ v2u bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 }
 
 // ------------------------------------------------------------ gate/up GEMM
-// One workgroup: one (expert, 16-token tile) x 256 rows of gate and up, two
-// 16-row tiles per wavefront sharing each A operand read, so that the chunk's
-// (expert, tile) pairs fit the GPU in one round of workgroups.  Lane
-// (n = lane & 15, kb = lane >> 4) of wavefront w owns weight row n0 + 16 t + n
-// of tile t; for MFMA j of a group it feeds word 2 kb + j of the row (B
-// operand) and of the tile rows (A operand, from LDS), so both operands share
-// one order of the 64 k values, and a lane's two words of a group are
-// adjacent in the packed layout: one 8-byte load.
+// One workgroup: one (expert, 16-token tile) x 256 rows of gate and up, one
+// 16-row tile per wavefront (16 wavefronts), so a 512-row expert stages each
+// token tile in two workgroups (with 8 wavefronts, four: 56.7-57.0 against
+// 58.0 us per 128-token chunk).  Lane (n = lane & 15, kb = lane >> 4) of
+// wavefront w owns weight row n0 + 16 t + n of tile t; for MFMA j of a group
+// it feeds word 2 kb + j of the row (B operand) and of the tile rows (A
+// operand, from LDS), so both operands share one order of the 64 k values,
+// and a lane's two words of a group are adjacent in the packed layout: one
+// 8-byte load.  The scale/bias words go out four groups at a time: lane
+// quarter kb loads group g0 + kb of its row, and each group's word is taken
+// from its quarter through ds_bpermute (a quarter of the load instructions
+// for them).
 #ifndef MOE_GU_TILES
 #define MOE_GU_TILES 1
 #endif
 constexpr int kGuTiles = MOE_GU_TILES;
-constexpr int kGuRowsPerWG = 16 * kGuTiles * kPWaves;
+constexpr int kGuRowsPerWG = 16 * kGuTiles * MOE_GU_WAVES;
 
 template <int STG>
-__global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(kGuThreads) void pf_gate_up_kernel(PrefillArgs p) {
   extern __shared__ __align__(16) char smem[];
   const LayerArgs& a = p.L;
   const int nch = (max(a.f, a.fs) + kGuRowsPerWG - 1) / kGuRowsPerWG;
@@ -427,25 +439,33 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
   // weights stream while the tile is staged.  Measured: 57.9 against 59.7 us
   // per 128-token chunk.
   v4u sbuf[STG];
-  stage_rows_load<STG>(d, rows, sbuf);
+  stage_rows_load<kGuThreads, STG>(d, rows, sbuf);
   v2u wg[kPre][kGuTiles], wu[kPre][kGuTiles];
-  uint32_t sg[kPre][kGuTiles], su[kPre][kGuTiles];
+  uint32_t sgc[kGuTiles], suc[kGuTiles], sgn[kGuTiles], sun[kGuTiles];
   auto fetch = [&](int i, uint32_t g) {
 #pragma unroll
     for (int t = 0; t < kGuTiles; ++t) {
       wg[i][t] = bload2(rs, vgq[t], g * 256);
       wu[i][t] = bload2(rs, vuq[t], g * 256);
-      sg[i][t] = bload(rs, vgs[t], g * 32);
-      su[i][t] = bload(rs, vus[t], g * 32);
     }
   };
+  auto fetch_sb = [&](int g0) {  // lane quarter kb: scale/bias of group g0 + kb
+    const uint32_t go = (uint32_t)min(g0 + kb, G - 1) * 32;
+#pragma unroll
+    for (int t = 0; t < kGuTiles; ++t) {
+      sgn[t] = bload(rs, vgs[t] + go, 0);
+      sun[t] = bload(rs, vus[t] + go, 0);
+    }
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_sb(0);
 #pragma unroll
   for (int i = 0; i < kPre; ++i) {  // in slot order (see the refill below)
     __builtin_amdgcn_sched_barrier(0);
     fetch(i, (uint32_t)min(i, G - 1));
   }
   __builtin_amdgcn_sched_barrier(0);
-  stage_rows_commit<true, STG>(d, sbuf, xs_lds, gsum);
+  stage_rows_commit<kGuThreads, true, STG>(d, sbuf, xs_lds, gsum);
   __builtin_amdgcn_sched_barrier(0);
   if (n0 >= fdim) return;  // no barrier follows
   f32x4 accg[kGuTiles], accu[kGuTiles];
@@ -458,6 +478,11 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
   // group past the end is skipped) so the compiler can keep kPre groups of
   // loads in flight across iterations.
   for (int g0 = 0; g0 < G; g0 += kPre) {
+#pragma unroll
+    for (int t = 0; t < kGuTiles; ++t) {
+      sgc[t] = sgn[t];
+      suc[t] = sun[t];
+    }
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
       const int g = g0 + i;
@@ -472,14 +497,15 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
         f32x4 tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(wu[i][t].x, nmask), zero, 0, 0, 0);
         tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(wu[i][t].y, nmask), tu, 0, 0, 0);
         if (g < G) {  // uniform: groups past the end (clamped loads) are dropped
-          group_epilogue(accg[t], tg, sg[i][t], xs4);
-          group_epilogue(accu[t], tu, su[i][t], xs4);
+          group_epilogue(accg[t], tg, from_quarter(sgc[t], i), xs4);
+          group_epilogue(accu[t], tu, from_quarter(suc[t], i), xs4);
         }
       }
       // refill this slot with group g + kPre, as one batch after this
       // group's products: slots then complete in order, so the next
       // group's wait leaves the other slots' loads in flight
       __builtin_amdgcn_sched_barrier(0);
+      if (i == 0) fetch_sb(g0 + kPre);
       fetch(i, (uint32_t)min(g + kPre, G - 1));
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -514,11 +540,11 @@ __global__ __launch_bounds__(kPThreads) void pf_gate_up_kernel(PrefillArgs p) {
 #define MOE_DN_PRE 4
 #endif
 constexpr int kDnTiles = MOE_DN_TILES;                   // 16-row tiles per wavefront
-constexpr int kDnRowsPerWG = 16 * kDnTiles * kPWaves;
+constexpr int kDnRowsPerWG = 16 * kDnTiles * MOE_DN_WAVES;
 constexpr int kDnPre = MOE_DN_PRE;                       // groups in flight per lane
 
 template <int STG>
-__global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(kDnThreads) void pf_down_kernel(PrefillArgs p) {
   extern __shared__ __align__(16) char smem[];
   const LayerArgs& a = p.L;
   const int nch = (a.d + kDnRowsPerWG - 1) / kDnRowsPerWG;
@@ -550,7 +576,7 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   }
   __syncthreads();
   v4u sbuf[STG];
-  stage_rows_load<STG>(fdim, rows, sbuf);  // then the first weights, then the commit (as in gate/up)
+  stage_rows_load<kDnThreads, STG>(fdim, rows, sbuf);  // then the first weights, then the commit (as in gate/up)
   v2u w[kDnPre][kDnTiles];
   uint32_t sb[kDnPre][kDnTiles];
   // slot i's loads go out as one batch, slots in order (scheduling
@@ -566,7 +592,7 @@ __global__ __launch_bounds__(kPThreads) void pf_down_kernel(PrefillArgs p) {
   };
 #pragma unroll
   for (int i = 0; i < kDnPre; ++i) fetch(i, (uint32_t)min(i, G - 1));
-  stage_rows_commit<false, STG>(fdim, sbuf, as_lds, gsum);
+  stage_rows_commit<kDnThreads, false, STG>(fdim, sbuf, as_lds, gsum);
   __builtin_amdgcn_sched_barrier(0);
   if (n0 >= a.d) return;  // no barrier follows
   f32x4 acc[kDnTiles];
@@ -682,8 +708,8 @@ void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, 
 }
 
 // Staging words per thread for 16 rows of `width` bf16 values, rounded up to a power of two.
-static int stage_words(int width) {
-  const int need = (kTile * (width / 8) + kPThreads - 1) / kPThreads;
+static int stage_words(int width, int threads) {
+  const int need = (kTile * (width / 8) + threads - 1) / threads;
   int s = 1;
   while (s < need) s <<= 1;
   return s;
@@ -760,8 +786,8 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
       if (p0.streamer && (e = p0.streamer->group(grp, s, &p.tiles)) != hipSuccess) return e;
       const int nch_gu = (((a.f > a.fs) ? a.f : a.fs) + kGuRowsPerWG - 1) / kGuRowsPerWG;
       const size_t lds_gu = prefill_lds_gate_up(a.d);
-      const dim3 g_gu((unsigned)(mt * nch_gu)), blk(kPThreads);
-      switch (stage_words(a.d)) {
+      const dim3 g_gu((unsigned)(mt * nch_gu)), blk(kGuThreads);
+      switch (stage_words(a.d, kGuThreads)) {
         case 1: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<1>, g_gu, blk, lds_gu, s, p); break;
         case 2: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<2>, g_gu, blk, lds_gu, s, p); break;
         case 4: launch_timed(a.prof, kKPrefillGateUp, pf_gate_up_kernel<4>, g_gu, blk, lds_gu, s, p); break;
@@ -772,12 +798,13 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
       const int nch_dn = (a.d + kDnRowsPerWG - 1) / kDnRowsPerWG;
       const size_t lds_dn = (size_t)kTile * (fmax / 8 + 1) * 16 + (size_t)(fmax / 64) * kTile * 4;
       const dim3 g_dn((unsigned)(mt * nch_dn));
-      switch (stage_words(fmax)) {
-        case 1: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<1>, g_dn, blk, lds_dn, s, p); break;
-        case 2: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<2>, g_dn, blk, lds_dn, s, p); break;
-        case 4: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<4>, g_dn, blk, lds_dn, s, p); break;
-        case 8: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<8>, g_dn, blk, lds_dn, s, p); break;
-        default: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<16>, g_dn, blk, lds_dn, s, p); break;
+      const dim3 blk_dn(kDnThreads);
+      switch (stage_words(fmax, kDnThreads)) {
+        case 1: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<1>, g_dn, blk_dn, lds_dn, s, p); break;
+        case 2: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<2>, g_dn, blk_dn, lds_dn, s, p); break;
+        case 4: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<4>, g_dn, blk_dn, lds_dn, s, p); break;
+        case 8: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<8>, g_dn, blk_dn, lds_dn, s, p); break;
+        default: launch_timed(a.prof, kKPrefillDown, pf_down_kernel<16>, g_dn, blk_dn, lds_dn, s, p); break;
       }
       if (p0.streamer && (e = p0.streamer->done(grp, s)) != hipSuccess) return e;
     }
