@@ -578,18 +578,23 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(PrefillArgs p) {
   v4u sbuf[STG];
   stage_rows_load<kDnThreads, STG>(fdim, rows, sbuf);  // then the first weights, then the commit (as in gate/up)
   v2u w[kDnPre][kDnTiles];
-  uint32_t sb[kDnPre][kDnTiles];
+  uint32_t sbc[kDnTiles], sbn[kDnTiles];
   // slot i's loads go out as one batch, slots in order (scheduling
-  // barriers), so each group waits only for its own slot
+  // barriers), so each group waits only for its own slot; the scale/bias
+  // words of four groups go out with slot 0 (as in gate/up)
   auto fetch = [&](int i, uint32_t g) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < kDnTiles; ++t) {
-      w[i][t] = bload2(rs, vq[t], g * 256);
-      sb[i][t] = bload(rs, vs[t], g * 32);
-    }
+    for (int t = 0; t < kDnTiles; ++t) w[i][t] = bload2(rs, vq[t], g * 256);
     __builtin_amdgcn_sched_barrier(0);
   };
+  auto fetch_sb = [&](int g0) {
+    const uint32_t go = (uint32_t)min(g0 + kb, G - 1) * 32;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kDnTiles; ++t) sbn[t] = bload(rs, vs[t] + go, 0);
+  };
+  fetch_sb(0);
 #pragma unroll
   for (int i = 0; i < kDnPre; ++i) fetch(i, (uint32_t)min(i, G - 1));
   stage_rows_commit<kDnThreads, false, STG>(fdim, sbuf, as_lds, gsum);
@@ -603,6 +608,8 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(PrefillArgs p) {
   const uint32_t nmask = nibble_mask_v();
   for (int g0 = 0; g0 < G; g0 += kDnPre) {
 #pragma unroll
+    for (int t = 0; t < kDnTiles; ++t) sbc[t] = sbn[t];
+#pragma unroll
     for (int i = 0; i < kDnPre; ++i) {
       const int g = g0 + i;
       const int gc = min(g, G - 1);
@@ -613,8 +620,9 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(PrefillArgs p) {
       for (int t = 0; t < kDnTiles; ++t) {
         f32x4 m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b_operand(w[i][t].x, nmask), zero, 0, 0, 0);
         m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b_operand(w[i][t].y, nmask), m, 0, 0, 0);
-        if (g < G) group_epilogue(acc[t], m, sb[i][t], xs4);  // uniform: groups past the end are dropped
+        if (g < G) group_epilogue(acc[t], m, from_quarter(sbc[t], i), xs4);  // uniform: past-the-end groups dropped
       }
+      if (i == 0) fetch_sb(g0 + kDnPre);
       fetch(i, (uint32_t)min(g + kDnPre, G - 1));
     }
   }
