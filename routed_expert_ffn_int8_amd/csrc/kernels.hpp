@@ -141,7 +141,7 @@ struct PrefillArgs {
   int32_t* perm;     // [T*K]
   int32_t* inv;      // [T*K]
   int32_t* tiles;    // work list for the grouped GEMMs
-  uint32_t* route_cnt;  // [ceil(T/16)] router arrival counters (zero between calls)
+  uint32_t* route_cnt;  // [ceil(T/16) + 1] arrival counters: per token tile, then per chunk (zero between calls)
   void* xact;        // [T][d] bf16 layer input (after rmsnorm in stack mode)
   uint16_t* A;       // [T*K][f] bf16 routed activations, in perm order
   uint16_t* As;      // [T][fs] bf16 shared activations

@@ -84,11 +84,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
 // entries: ceil(n_e/16) per chosen expert in expert order, then ceil(T/16) for
 // the shared expert (expert id E).  Needs E * ceil(T/32) words of LDS;
 // repeated ids in one token's set are counted once.  E <= 1024.
-__global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ ids, int T, int K, int E,
-                                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                                                   int32_t* tiles, int with_shared) {
-  extern __shared__ uint32_t sh[];  // off[E+1], mask[E][NW]
-  __shared__ int scan_sh[16];
+// DEV: the ids were stored by other workgroups of the running kernel and are
+// read with device-scope loads.  sh: (E + 1 + E * ceil(T/32)) words of LDS,
+// scan_sh: 16 ints.
+template <bool DEV>
+__device__ __forceinline__ int load_id(const int32_t* p) {
+  if (DEV) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool DEV>
+__device__ void sort_body(const int32_t* __restrict__ ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int32_t* tiles, int with_shared, uint32_t* sh, int* scan_sh) {
   const int NW = (T + 31) >> 5;
   int32_t* off = reinterpret_cast<int32_t*>(sh);
   uint32_t* mask = sh + E + 1;
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
   for (int i = tid; i < E * NW; i += blockDim.x) mask[i] = 0u;
   __syncthreads();
   for (int i = tid; i < n; i += blockDim.x) {
-    const int e = ids[i], t = i / K;
+    const int e = load_id<DEV>(ids + i), t = i / K;
     if (e >= 0 && e < E) atomicOr(&mask[e * NW + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
   }
   __syncthreads();
   for (int i = tid; i < n; i += blockDim.x) {
-    const int e = ids[i], t = i / K;
+    const int e = load_id<DEV>(ids + i), t = i / K;
     if (e < 0 || e >= E) continue;
     const uint32_t* m = mask + e * NW;
     int rank = __popc(m[t >> 5] & ((1u << (t & 31)) - 1u));
@@ -140,6 +146,14 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
     perm[pos] = i;
     inv[i] = pos;
   }
+}
+
+__global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ ids, int T, int K, int E,
+                                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                                   int32_t* tiles, int with_shared) {
+  extern __shared__ uint32_t sh[];  // off[E+1], mask[E][NW]
+  __shared__ int scan_sh[16];
+  sort_body<false>(ids, T, K, E, counts, offsets, perm, inv, tiles, with_shared, sh, scan_sh);
 }
 
 // ------------------------------------------------------------ router + top-K
@@ -164,10 +178,11 @@ size_t route_lds_bytes(int E) { return (size_t)kTile * E * 4; }
 
 template <int NE>
 __global__ __launch_bounds__(64 * kRouteWaves) void pf_route_kernel(PrefillArgs p) {
-  extern __shared__ __align__(16) char smem[];  // [16][E] logits of the tile (last workgroup)
+  extern __shared__ __align__(16) char smem[];  // [16][E] logits of the tile, then the sort's words (last workgroup)
   __shared__ float part[kRouteWaves][64][4];
   __shared__ uint32_t scratch[kRouteWaves][2 * 64];
   __shared__ uint32_t last_sh;
+  __shared__ int sort_sh[16];
   const LayerArgs& a = p.L;
   const int d = a.d, E = a.E, T = a.T;
   const int t0 = blockIdx.x * kTile;
@@ -225,20 +240,37 @@ __global__ __launch_bounds__(64 * kRouteWaves) void pf_route_kernel(PrefillArgs 
   __syncthreads();
   if (!last_sh) return;
   const int t = t0 + wave;
-  if (t >= T) return;
-  float* s_log = reinterpret_cast<float*>(smem) + (size_t)wave * E;
-  const float* lt = a.logits + (size_t)t * E;
-  float v[NE];
+  if (t < T) {
+    float* s_log = reinterpret_cast<float*>(smem) + (size_t)wave * E;
+    const float* lt = a.logits + (size_t)t * E;
+    float v[NE];
 #pragma unroll
-  for (int i = 0; i < NE; ++i) v[i] = __hip_atomic_load(lt + min(lane + 64 * i, E - 1), __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < NE; ++i) v[i] = __hip_atomic_load(lt + min(lane + 64 * i, E - 1), __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-  for (int i = 0; i < NE; ++i)
-    if (lane + 64 * i < E) s_log[lane + 64 * i] = v[i];
-  int id;
-  float w;
-  topk_wave<NE>(a, t, s_log, &id, &w, scratch[wave]);
-  publish_routing(a, t, lane, id, w);
+    for (int i = 0; i < NE; ++i)
+      if (lane + 64 * i < E) s_log[lane + 64 * i] = v[i];
+    int id;
+    float w;
+    topk_wave<NE>(a, t, s_log, &id, &w, scratch[wave]);
+    publish_routing(a, t, lane, id, w);  // ids with device-scope stores
+  }
+  // The workgroup that completes the chunk's last token tile (a second
+  // arrival counter, reset by that workgroup) groups the chunk's tokens by
+  // expert, reading the other tiles' ids with device-scope loads: one launch
+  // fewer per chunk.
+  __builtin_amdgcn_s_waitcnt(0);  // this tile's ids are stored before the arrival
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* all = p.route_cnt + gridDim.x;
+    const uint32_t old = atomicAdd(all, 1u);
+    last_sh = old == gridDim.x - 1 ? 1u : 0u;
+    if (last_sh) __hip_atomic_store(all, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last_sh) return;
+  sort_body<true>(a.ids, T, a.K, E, p.counts, p.offsets, p.perm, p.inv, p.tiles, a.fs > 0 ? 1 : 0,
+                  reinterpret_cast<uint32_t*>(smem), sort_sh);
 }
 
 // ------------------------------------------------------------ tile staging
@@ -641,19 +673,35 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(PrefillArgs p) {
 
 // ------------------------------------------------------------ combine
 // y_t = shared_t + sum_k w_{t,k} * Y[inv[t*K + k]] (k ascending), + residual.
+// One thread per 4 consecutive columns (d is a multiple of 64): 16-byte loads
+// of the fp32 rows, 8-byte bf16 residual loads and output stores.
+constexpr int kCombineCols = 4 * 256;  // columns per workgroup
 __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillArgs p) {
   const LayerArgs& a = p.L;
   const int t = blockIdx.y;
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.x * kCombineCols + threadIdx.x * 4;
   if (c >= a.d) return;
-  float y = a.fs > 0 ? p.Ys[(size_t)t * a.d + c] : 0.f;
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+  if (a.fs > 0) y = *reinterpret_cast<const f32x4*>(p.Ys + (size_t)t * a.d + c);
   for (int k = 0; k < a.K; ++k) {
     const int pos = p.inv[t * a.K + k];
-    y = fmaf(a.wts[t * a.K + k], p.Y[(size_t)pos * a.d + c], y);
+    const float w = a.wts[t * a.K + k];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p.Y + (size_t)pos * a.d + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = fmaf(w, v[j], y[j]);
   }
   const size_t o = (size_t)t * a.d + c;
-  if (a.resid) y += bf16_to_f32(static_cast<const uint16_t*>(a.resid)[o]);
-  static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(y);
+  if (a.resid) {
+    const v2u r = *reinterpret_cast<const v2u*>(static_cast<const uint16_t*>(a.resid) + o);
+    y[0] += bf16_to_f32((uint16_t)(r.x & 0xFFFFu));
+    y[1] += bf16_to_f32((uint16_t)(r.x >> 16));
+    y[2] += bf16_to_f32((uint16_t)(r.y & 0xFFFFu));
+    y[3] += bf16_to_f32((uint16_t)(r.y >> 16));
+  }
+  v2u out;
+  out.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+  out.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+  *reinterpret_cast<v2u*>(static_cast<uint16_t*>(a.out) + o) = out;
 }
 
 }  // namespace
@@ -687,7 +735,7 @@ size_t prefill_workspace_bytes(int T, int d, int E, int K, int f, int fs) {
   const int C = T < kChunkTokens ? T : kChunkTokens;
   size_t b = 0;
   b += align_up((size_t)E * 4) + align_up((size_t)(E + 1) * 4);  // counts, offsets
-  b += align_up((size_t)((C + kTile - 1) / kTile) * 4);            // router arrival counters
+  b += align_up((size_t)((C + kTile - 1) / kTile + 1) * 4);        // router arrival counters (tiles, chunk)
   b += 2 * align_up((size_t)C * K * 4);                            // perm, inv
   b += align_up((1 + 2 * max_tiles(C, K, E)) * 4);                 // tiles
   b += align_up((size_t)C * K * f * 2) + align_up((size_t)C * (fs > 0 ? fs : 64) * 2);  // A, As
@@ -705,7 +753,7 @@ void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, 
   };
   p.counts = reinterpret_cast<int32_t*>(take((size_t)E * 4));
   p.offsets = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
-  p.route_cnt = reinterpret_cast<uint32_t*>(take((size_t)((C + kTile - 1) / kTile) * 4));
+  p.route_cnt = reinterpret_cast<uint32_t*>(take((size_t)((C + kTile - 1) / kTile + 1) * 4));
   p.perm = reinterpret_cast<int32_t*>(take((size_t)C * K * 4));
   p.inv = reinterpret_cast<int32_t*>(take((size_t)C * K * 4));
   p.tiles = reinterpret_cast<int32_t*>(take((1 + 2 * max_tiles(C, K, E)) * 4));
@@ -768,11 +816,11 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
     if (a0.ids_out) a.ids_out = a0.ids_out + (size_t)c0 * a.K;
     if (a0.w_out) a.w_out = a0.w_out + (size_t)c0 * a.K;
     p.xact = const_cast<void*>(a.x);
-    // 1. router + top-K
+    // 1. router + top-K, then grouping + tiles (in the router launch)
     {
       const dim3 g_rt((unsigned)((C + kTile - 1) / kTile), (unsigned)((a.E + 15) / 16));
       const dim3 b_rt(64 * kRouteWaves);
-      const size_t l_rt = route_lds_bytes(a.E);
+      const size_t l_rt = std::max(route_lds_bytes(a.E), sort_lds_bytes(C, a.E));
       if (a.E <= 64)
         launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<1>, g_rt, b_rt, l_rt, s, p);
       else if (a.E <= 128)
@@ -783,9 +831,6 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
         launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<16>, g_rt, b_rt, l_rt, s, p);
     }
     hipError_t e;
-    // 2. grouping + tiles
-    launch_timed(a.prof, kKSort, sort_kernel, dim3(1), dim3(1024), sort_lds_bytes(C, a.E), s, (const int32_t*)a.ids,
-                 C, a.K, a.E, p.counts, p.offsets, p.perm, p.inv, p.tiles, a.fs > 0 ? 1 : 0);
     // 3. gate/up, 4. down (per group of cached experts when they are streamed), 5. combine
     const size_t mt = max_tiles(C, a.K, a.E);
     int n_groups = 1;
@@ -816,7 +861,8 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
       }
       if (p0.streamer && (e = p0.streamer->done(grp, s)) != hipSuccess) return e;
     }
-    launch_timed(a.prof, kKPrefillCombine, pf_combine_kernel, dim3((a.d + 255) / 256, C), dim3(256), 0, s, p);
+    launch_timed(a.prof, kKPrefillCombine, pf_combine_kernel, dim3((a.d + kCombineCols - 1) / kCombineCols, C),
+                 dim3(256), 0, s, p);
     if (p0.sort_offsets_out)  // one row of E + 1 offsets per chunk
       if ((e = hipMemcpyAsync(p0.sort_offsets_out + (size_t)(c0 / kChunkTokens) * (a.E + 1), p.offsets,
                               (a.E + 1) * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)

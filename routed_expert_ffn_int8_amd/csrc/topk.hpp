@@ -240,7 +240,8 @@ __device__ int topk_kth(const LayerArgs& a, int t, const float* lt, int k) {
 __device__ __forceinline__ void publish_routing(const LayerArgs& a, int t, int lane, int id, float w) {
   if (lane < a.K) {
     const size_t o = (size_t)t * a.K + lane;
-    if (a.ids != a.forced) a.ids[o] = id;  // reusing the stored sets: they stay as they are
+    if (a.ids != a.forced)  // reusing the stored sets: they stay as they are
+      __hip_atomic_store(a.ids + o, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // read by the prefill sort
     a.wts[o] = w;
     a.sel_addr[o] = a.expert_addr[id];
     if (a.ids_out) a.ids_out[o] = id;
