@@ -291,9 +291,10 @@ __device__ __forceinline__ char* abuf_of(const LayerArgs& a, int t, int act) {
 // staged before the weights are requested (its loads went out long before):
 // staging it after them would make the first product wait for every weight,
 // as the wait for the token loads cannot be told apart from theirs.
+// `staged`: the caller has staged the token already.
 template <int ACT, int MAXI, int ROWS = 8, bool REPS = false>
 __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, const BlobOffsets& o, int rb,
-                              int apos, const XStage& S, const XRegs& xr, uint32_t tag = 0) {
+                              int apos, const XStage& S, const XRegs& xr, uint32_t tag = 0, bool staged = false) {
   constexpr int JJ = kThreads / ROWS;
   const int tid = threadIdx.x, r = tid % ROWS, jj = tid / ROWS;
   const int G = a.d >> 6;
@@ -304,7 +305,7 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
   const uint8_t* gsb = blob + o.gsb + ((size_t)rb8 * G * 8 + r8) * 4;  // + g * 32
   const uint8_t* usb = blob + o.usb + ((size_t)rb8 * G * 8 + r8) * 4;
   float accg = 0.f, accu = 0.f;
-  if (REPS) x_commit<ACT>(a, t, xr, S);
+  if (REPS && !staged) x_commit<ACT>(a, t, xr, S);
   for (int base = 0; base < G; base += JJ * MAXI) {
     v4u qg0[MAXI], qg1[MAXI], qu0[MAXI], qu1[MAXI];
     uint32_t sg[MAXI], su[MAXI];
@@ -319,7 +320,7 @@ __device__ void gate_up_block(const LayerArgs& a, int t, const uint8_t* blob, co
       sg[i] = ldg<uint32_t>(gsb + g * 32);
       su[i] = ldg<uint32_t>(usb + g * 32);
     }
-    if (!REPS && base == 0) x_commit<ACT>(a, t, xr, S);
+    if (!REPS && !staged && base == 0) x_commit<ACT>(a, t, xr, S);
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
       const int g = base + jj + JJ * i;
@@ -1082,6 +1083,12 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
     const uint32_t tag = launch_tag(area, ND);
     XRegs xr;
     x_issue<1>(a, 0, xr);
+    // A residual-stream input is normalised (a block reduction) as it is
+    // staged: that is done while the router runs, off the critical path
+    // (30-layer stack 20.3 against 21.1 us per layer).  A plain token is
+    // staged after the top-K, as before: staged early it cost the layer
+    // 0.6 us, at either wave priority.
+    if (a.rms) x_commit<1>(a, 0, xr, S);
     __builtin_amdgcn_s_setprio(2);
     // re-reads entries until they carry this launch's tag.  Forced sets (a
     // reused routing) name the experts without the logits: the weights then
@@ -1096,7 +1103,7 @@ __global__ __launch_bounds__(kThreads, 4) void fused_layer_kernel(LayerArgs a) {
     __builtin_amdgcn_s_setprio(0);
     const int id = (int)scratch[0];
     gate_up_block<1, MAXI, kFusedGuRows, true>(a, 0, a.expert_base + (size_t)id * a.expert_stride, a.ro, rb,
-                                               a.fs + k * a.f, S, xr, tag);
+                                               a.fs + k * a.f, S, xr, tag, a.rms != 0);
     arrive(area, kCntRouted, g);
   } else {
     down_fused<SS, SR, NE>(a, b - NR - NS - NG, ND, (uint32_t)NS, (uint32_t)NG, my_rep, smem,
