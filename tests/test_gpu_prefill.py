@@ -126,6 +126,8 @@ PSHAPES = [  # (d, E, K, f, fs, T)
     (256, 1, 1, 64, 64, 16),
     (512, 4, 2, 128, 64, 128),     # every routed expert has about 64 rows (four 16-row tiles)
     (1024, 8, 8, 128, 128, 200),   # K = E: every expert takes every row (128, then 72)
+    (192, 8, 2, 64, 64, 40),       # 3 groups per gate/up row, 1 per down row: the scale batches of 4 clamp
+    (320, 16, 4, 192, 0, 17),      # 5 and 3 groups per row, no shared expert, ragged last tile
 ]
 
 
