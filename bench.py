@@ -667,7 +667,7 @@ def main():
                     help="run one 256 MiB device copy first (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(no collectives, no sharding); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     rank = int(os.environ.get("RANK", "0"))
