@@ -907,7 +907,7 @@ struct StreamPrefill final : PrefillStreamer {
 moe_status launch_prefill_path(moe_layer* L, const LayerArgs& a, const moe_fwd_opts* o, hipStream_t s) {
   PrefillArgs p{};
   p.L = a;
-  prefill_carve(p, L->d_prefill, a.T, L->d, L->E, L->K, L->f, L->fs);
+  prefill_carve(p, L->d_prefill, L->max_tokens, L->d, L->E, L->K, L->f, L->fs);  // the layout of every call
   p.sort_offsets_out = o ? o->sort_offsets : nullptr;
   p.sort_perm_out = o ? o->sort_perm : nullptr;
   if (L->residency != MOE_STREAMED) {

@@ -136,12 +136,12 @@ size_t decode_sync_bytes(int E);
 
 struct PrefillArgs {
   LayerArgs L;
-  int32_t* counts;   // [E]
+  int32_t* counts;   // [E] of a chunk; the router launch gets chunk 0's and writes [chunks][E]
   int32_t* offsets;  // [E+1]
   int32_t* perm;     // [T*K]
   int32_t* inv;      // [T*K]
   int32_t* tiles;    // work list for the grouped GEMMs
-  uint32_t* route_cnt;  // [ceil(T/16) + 1] arrival counters: per token tile, then per chunk (zero between calls)
+  uint32_t* route_cnt;  // arrival counters: per token tile of the call, then per chunk (zero between calls)
   void* xact;        // [T][d] bf16 layer input (after rmsnorm in stack mode)
   uint16_t* A;       // [T*K][f] bf16 routed activations, in perm order
   uint16_t* As;      // [T][fs] bf16 shared activations

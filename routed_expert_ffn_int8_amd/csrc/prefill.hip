@@ -156,6 +156,16 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
   sort_body<false>(ids, T, K, E, counts, offsets, perm, inv, tiles, with_shared, sh, scan_sh);
 }
 
+constexpr int kChunkTokens = 128;  // prefill chunk (Rockchip-NPU plan §8.4)
+constexpr int kChunkTiles = kChunkTokens / 16;  // token tiles per chunk
+
+// Entries of a chunk's (expert, tile) list: at most T*K/16 + E tiles of
+// routed experts and ceil(T/16) of the shared expert.
+__host__ __device__ inline size_t max_tiles(int T, int K, int E) {
+  return (size_t)T * K / 16 + E + (T + 15) / 16 + 1;
+}
+__host__ __device__ inline size_t tile_list_ints(int K, int E) { return 1 + 2 * max_tiles(kChunkTokens, K, E); }
+
 // ------------------------------------------------------------ router + top-K
 // Workgroup (16-token tile, 16 experts) of 16 wavefronts: they split d in
 // sixteen and each runs v_mfma_f32_16x16x32_bf16 over its share, A = the
@@ -255,22 +265,27 @@ __global__ __launch_bounds__(64 * kRouteWaves) void pf_route_kernel(PrefillArgs 
     topk_wave<NE>(a, t, s_log, &id, &w, scratch[wave]);
     publish_routing(a, t, lane, id, w);  // ids with device-scope stores
   }
-  // The workgroup that completes the chunk's last token tile (a second
-  // arrival counter, reset by that workgroup) groups the chunk's tokens by
-  // expert, reading the other tiles' ids with device-scope loads: one launch
-  // fewer per chunk.
+  // The workgroup that completes a chunk's last token tile (a per-chunk
+  // arrival counter after the tiles', reset by that workgroup) groups the
+  // chunk's tokens by expert into the chunk's buffers, reading the other
+  // tiles' ids with device-scope loads.  The launch covers every chunk of
+  // the call, so no chunk pays a launch of its own for routing or grouping.
   __builtin_amdgcn_s_waitcnt(0);  // this tile's ids are stored before the arrival
   __syncthreads();
+  const int c = blockIdx.x / kChunkTiles;
   if (threadIdx.x == 0) {
-    uint32_t* all = p.route_cnt + gridDim.x;
-    const uint32_t old = atomicAdd(all, 1u);
-    last_sh = old == gridDim.x - 1 ? 1u : 0u;
-    if (last_sh) __hip_atomic_store(all, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t tiles_c = min((uint32_t)kChunkTiles, gridDim.x - (uint32_t)c * kChunkTiles);
+    uint32_t* cnt = p.route_cnt + gridDim.x + c;
+    const uint32_t old = atomicAdd(cnt, 1u);
+    last_sh = old == tiles_c - 1 ? 1u : 0u;
+    if (last_sh) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!last_sh) return;
-  sort_body<true>(a.ids, T, a.K, E, p.counts, p.offsets, p.perm, p.inv, p.tiles, a.fs > 0 ? 1 : 0,
-                  reinterpret_cast<uint32_t*>(smem), sort_sh);
+  const int c0 = c * kChunkTokens, C = min(kChunkTokens, T - c0);
+  sort_body<true>(a.ids + (size_t)c0 * a.K, C, a.K, E, p.counts + (size_t)c * E, p.offsets + (size_t)c * (E + 1),
+                  p.perm + (size_t)c0 * a.K, p.inv + (size_t)c0 * a.K, p.tiles + (size_t)c * tile_list_ints(a.K, E),
+                  a.fs > 0 ? 1 : 0, reinterpret_cast<uint32_t*>(smem), sort_sh);
 }
 
 // ------------------------------------------------------------ tile staging
@@ -725,19 +740,21 @@ hipError_t launch_sort(const int32_t* ids, int T, int K, int E, int32_t* counts,
   return hipGetLastError();
 }
 
-constexpr int kChunkTokens = 128;  // prefill chunk (Rockchip-NPU plan §8.4)
-
-static size_t max_tiles(int T, int K, int E) { return (size_t)T * K / kTile + E + (T + kTile - 1) / kTile + 1; }
 
 static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Layout for calls of up to T tokens, the same for every call: the arrival
+// counters first (zero between calls: the workgroup that completes one resets
+// it), then each chunk's grouping (counts, offsets, tile list; perm and inv
+// [T][K], chunk-local indices), then one chunk's activations and outputs.
 size_t prefill_workspace_bytes(int T, int d, int E, int K, int f, int fs) {
   const int C = T < kChunkTokens ? T : kChunkTokens;
+  const size_t nc = (size_t)(T + kChunkTokens - 1) / kChunkTokens;
   size_t b = 0;
-  b += align_up((size_t)E * 4) + align_up((size_t)(E + 1) * 4);  // counts, offsets
-  b += align_up((size_t)((C + kTile - 1) / kTile + 1) * 4);        // router arrival counters (tiles, chunk)
-  b += 2 * align_up((size_t)C * K * 4);                            // perm, inv
-  b += align_up((1 + 2 * max_tiles(C, K, E)) * 4);                 // tiles
+  b += align_up(((size_t)(T + kTile - 1) / kTile + nc) * 4);                       // arrivals: tiles, chunks
+  b += align_up(nc * E * 4) + align_up(nc * (E + 1) * 4);                          // counts, offsets
+  b += 2 * align_up((size_t)T * K * 4);                                            // perm, inv
+  b += align_up(nc * tile_list_ints(K, E) * 4);                                    // tile lists
   b += align_up((size_t)C * K * f * 2) + align_up((size_t)C * (fs > 0 ? fs : 64) * 2);  // A, As
   b += align_up((size_t)C * K * d * 4) + align_up((size_t)C * d * 4);                  // Y, Ys
   return b;
@@ -745,18 +762,19 @@ size_t prefill_workspace_bytes(int T, int d, int E, int K, int f, int fs) {
 
 void prefill_carve(PrefillArgs& p, char* ws, int T, int d, int E, int K, int f, int fs) {
   const int C = T < kChunkTokens ? T : kChunkTokens;
+  const size_t nc = (size_t)(T + kChunkTokens - 1) / kChunkTokens;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* q = ws + off;
     off += align_up(bytes);
     return q;
   };
-  p.counts = reinterpret_cast<int32_t*>(take((size_t)E * 4));
-  p.offsets = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
-  p.route_cnt = reinterpret_cast<uint32_t*>(take((size_t)((C + kTile - 1) / kTile + 1) * 4));
-  p.perm = reinterpret_cast<int32_t*>(take((size_t)C * K * 4));
-  p.inv = reinterpret_cast<int32_t*>(take((size_t)C * K * 4));
-  p.tiles = reinterpret_cast<int32_t*>(take((1 + 2 * max_tiles(C, K, E)) * 4));
+  p.route_cnt = reinterpret_cast<uint32_t*>(take(((size_t)(T + kTile - 1) / kTile + nc) * 4));
+  p.counts = reinterpret_cast<int32_t*>(take(nc * E * 4));
+  p.offsets = reinterpret_cast<int32_t*>(take(nc * (E + 1) * 4));
+  p.perm = reinterpret_cast<int32_t*>(take((size_t)T * K * 4));
+  p.inv = reinterpret_cast<int32_t*>(take((size_t)T * K * 4));
+  p.tiles = reinterpret_cast<int32_t*>(take(nc * tile_list_ints(K, E) * 4));
   p.A = reinterpret_cast<uint16_t*>(take((size_t)C * K * f * 2));
   p.As = reinterpret_cast<uint16_t*>(take((size_t)C * (fs > 0 ? fs : 64) * 2));
   p.Y = reinterpret_cast<float*>(take((size_t)C * K * d * 4));
@@ -798,11 +816,35 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
+  // 1. router + top-K of every token of the call, and each chunk's grouping
+  //    and tile list, in one launch
+  {
+    PrefillArgs p = p0;
+    const LayerArgs& a = p.L;
+    p.xact = const_cast<void*>(a.x);
+    const dim3 g_rt((unsigned)((a.T + kTile - 1) / kTile), (unsigned)((a.E + 15) / 16));
+    const dim3 b_rt(64 * kRouteWaves);
+    const size_t l_rt = std::max(route_lds_bytes(a.E), sort_lds_bytes(kChunkTokens, a.E));
+    if (a.E <= 64)
+      launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<1>, g_rt, b_rt, l_rt, s, p);
+    else if (a.E <= 128)
+      launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<2>, g_rt, b_rt, l_rt, s, p);
+    else if (a.E <= 256)
+      launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<4>, g_rt, b_rt, l_rt, s, p);
+    else
+      launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<16>, g_rt, b_rt, l_rt, s, p);
+  }
   for (int c0 = 0; c0 < a0.T; c0 += kChunkTokens) {
     PrefillArgs p = p0;
     LayerArgs& a = p.L;
     const int C = (a0.T - c0 < kChunkTokens) ? a0.T - c0 : kChunkTokens;
+    const int ci = c0 / kChunkTokens;
     a.T = C;
+    p.counts = p0.counts + (size_t)ci * a.E;  // this chunk's grouping
+    p.offsets = p0.offsets + (size_t)ci * (a.E + 1);
+    p.perm = p0.perm + (size_t)c0 * a.K;
+    p.inv = p0.inv + (size_t)c0 * a.K;
+    p.tiles = p0.tiles + (size_t)ci * tile_list_ints(a.K, a.E);
     const size_t xo = (size_t)c0 * a.d * 2;
     a.x = static_cast<const char*>(a0.x) + xo;
     a.out = static_cast<char*>(a0.out) + xo;
@@ -816,22 +858,8 @@ hipError_t launch_prefill(const PrefillArgs& p0, hipStream_t s) {
     if (a0.ids_out) a.ids_out = a0.ids_out + (size_t)c0 * a.K;
     if (a0.w_out) a.w_out = a0.w_out + (size_t)c0 * a.K;
     p.xact = const_cast<void*>(a.x);
-    // 1. router + top-K, then grouping + tiles (in the router launch)
-    {
-      const dim3 g_rt((unsigned)((C + kTile - 1) / kTile), (unsigned)((a.E + 15) / 16));
-      const dim3 b_rt(64 * kRouteWaves);
-      const size_t l_rt = std::max(route_lds_bytes(a.E), sort_lds_bytes(C, a.E));
-      if (a.E <= 64)
-        launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<1>, g_rt, b_rt, l_rt, s, p);
-      else if (a.E <= 128)
-        launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<2>, g_rt, b_rt, l_rt, s, p);
-      else if (a.E <= 256)
-        launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<4>, g_rt, b_rt, l_rt, s, p);
-      else
-        launch_timed(a.prof, kKPrefillRoute, pf_route_kernel<16>, g_rt, b_rt, l_rt, s, p);
-    }
     hipError_t e;
-    // 3. gate/up, 4. down (per group of cached experts when they are streamed), 5. combine
+    // 2. gate/up, 3. down (per group of cached experts when they are streamed), 4. combine
     const size_t mt = max_tiles(C, a.K, a.E);
     int n_groups = 1;
     if (p0.streamer && (e = p0.streamer->plan(p, C, s, &n_groups)) != hipSuccess) return e;
