@@ -249,11 +249,11 @@ enum {
   MOE_KERNEL_ROUTE_SHARED = 0,   /* router GEMV + shared gate/up (decode) */
   MOE_KERNEL_ROUTED_GATE_UP = 1, /* top-K + chosen experts' gate/up + SiLU*mul (decode) */
   MOE_KERNEL_DOWN_COMBINE = 2,   /* down projections + weighted combine (decode) */
-  MOE_KERNEL_SORT = 3,           /* token->expert grouping (prefill) */
+  MOE_KERNEL_SORT = 3,           /* token->expert grouping (moe_layer_sort; prefill groups in its router launch) */
   MOE_KERNEL_PREFILL_GATE_UP = 4,
   MOE_KERNEL_PREFILL_DOWN = 5,
   MOE_KERNEL_PREFILL_COMBINE = 6,
-  MOE_KERNEL_PREFILL_ROUTE = 7,
+  MOE_KERNEL_PREFILL_ROUTE = 7,  /* router + top-K of every token of a prefill call, and each chunk's grouping */
   MOE_KERNEL_TOPK = 8,           /* stand-alone softmax top-K */
   MOE_KERNEL_FUSED_LAYER = 9,    /* whole layer for one token in one launch */
   MOE_N_KERNELS = 10
