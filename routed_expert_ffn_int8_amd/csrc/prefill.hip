@@ -174,7 +174,9 @@ __host__ __device__ inline size_t tile_list_ints(int K, int E) { return 1 + 2 * 
 // order in LDS and scaled: logit = scale_e * acc + bias_e.  Logits go to the
 // layer's logit array with device-scope stores.  The workgroup that completes
 // a token tile (an arrival counter, which that workgroup resets for the next
-// call) runs the softmax top-K of the tile's tokens, one wavefront per token.
+// call) runs the softmax top-K of the tile's tokens, one wavefront per token;
+// the one that completes a chunk's last tile then groups the chunk's tokens
+// by expert.  One launch covers every token of a prefill call.
 constexpr int kRouteWaves = 16;
 constexpr int kRoutePre = 4;  // k-blocks of router weights in flight per lane
 
