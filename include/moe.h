@@ -299,9 +299,12 @@ moe_status moe_cache_stats_get(const moe_layer* layer, moe_cache_stats* out);
 moe_status moe_cache_reset(moe_layer* layer, int32_t drop_contents);
 /* HOST outputs [n_slots]: expert held by each slot (-1 = empty), use count. */
 moe_status moe_cache_contents(const moe_layer* layer, int32_t* expert_of_slot, uint32_t* use_count);
-/* Test hook: make expert `expert` unreadable (1) or readable (0); a call that
- * needs to fill an unreadable expert returns MOE_ERR_IO before enqueuing any
- * expert compute and leaves the slot table unchanged. */
+/* Test hook: make expert `expert` unreadable (1) or readable (0).  A decode
+ * call that needs to fill an unreadable expert returns MOE_ERR_IO before
+ * enqueuing any expert compute and leaves the slot table unchanged.  A
+ * prefill call returns MOE_ERR_IO at the group that needs it: the groups and
+ * chunks before it have already stepped the cache and run, so the slot table
+ * holds their experts and the call's output is incomplete. */
 moe_status moe_cache_fail_expert(moe_layer* layer, int32_t expert, int32_t fail);
 
 /* Fetch ahead into a layer's own (LFU) cache, Rockchip-NPU plan §8
