@@ -196,7 +196,9 @@ moe_status moe_layer_forward_ex(const void* x, moe_layer* layer, void* out, int3
 moe_status moe_layer_forward_noalloc(const void* x, moe_layer* layer, void* out, int32_t n_tokens, void* stream);
 
 /* Router + softmax top-K only: ids DEVICE int32 [T][K] (ascending per token),
- * w DEVICE fp32 [T][K]. */
+ * w DEVICE fp32 [T][K].  The gating of BigMoeOnEdge, section "re-routing at
+ * every token and layer", and the Rockchip-NPU plan, section 2.1: a softmax
+ * over all experts, the K largest kept, their weights renormalised. */
 moe_status moe_layer_route(const void* x, moe_layer* layer, int32_t* ids, float* w, int32_t n_tokens,
                            void* stream);
 
@@ -209,11 +211,13 @@ moe_status moe_layer_sort(const int32_t* ids, moe_layer* layer, int32_t n_tokens
                           int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
 
 /* Bytes the layer keeps in device memory, and the per-expert byte size
- * (gate + up + down at 4.5 bits per weight, padded to 256 B). */
+ * (gate + up + down at 4.5 bits per weight, padded to 256 B).  A library
+ * utility: no passage of the pages defines it. */
 moe_status moe_layer_bytes(const moe_layer* layer, uint64_t* device_bytes, uint64_t* expert_bytes);
 
 /* Waits for the device, then returns and clears the layer's sticky kernel
- * error flags in *flags (HOST):
+ * error flags in *flags (HOST); a library utility, no passage of the pages
+ * defines it:
  *   bit 0  a forced expert id was outside 0..E-1 (it was replaced by 0);
  *   bit 1  a chosen expert was not resident (its output read as zero);
  *   bit 2  a workgroup gave up waiting for another one's results: a bounded
@@ -240,7 +244,8 @@ moe_status moe_layer_check_errors(moe_layer* layer, int32_t* flags);
  * values. */
 moe_status moe_layer_set_default_path(moe_layer* layer, int32_t path);
 
-/* Per-kernel timing.  enable != 0 brackets every kernel the layer launches
+/* Per-kernel timing (a library utility: no passage of the pages defines it).
+ * enable != 0 brackets every kernel the layer launches
  * with HIP events on the launch stream; 0 stops and discards the record.
  * moe_layer_profile_read waits for the device, then fills HOST arrays
  * launches[MOE_N_KERNELS] and total_ms[MOE_N_KERNELS] (index = MOE_KERNEL_*)
